@@ -1,0 +1,255 @@
+"""Plain fp64 CPU oracle of the MISA routed token indexer.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports, calls or links
+this module: only the tests, the graft smoke check and the benchmark's
+``cpu_baseline`` leg use it. It shares no code with the HIP library.
+
+It follows the MISA pages (arXiv 2605.07363; MISA abstract on the
+engineersofai.com breakdown and the chatpaper.ai page; gist.science
+"Technische Samenvatting": "Probleemstelling", "Methodologie: MISA",
+"Hiërarchische Variant (MISA†)"). The pages never print a formula; the readings
+taken where they are silent are listed beside each function and in the design
+notes. Every value is computed in float64 from the exact bf16 values the GPU
+receives; there is no blocking, fusion or reordering beyond the definitions.
+
+Notation (pages' notation where they have one):
+  H (= H_I)  indexer heads;  h  routed heads per query;  B  block size;
+  L / p      prefix length (p = visible prefix of one query);
+  M = ceil(p / B) blocks;    k  selected tokens;  k' candidates (MISA†).
+  q[t, g, :] query of head g for query t;  w[t, g] head weight;
+  k[n, s, :] the single indexer key of token s of sequence n (shared by heads).
+
+Status of each function's pin (see tests/test_oracle_*.py):
+  pool_keys, route, routed_scores, select_topk, score_topk, dsa_index_dense,
+  hier_rerank, misa_indexer, misa_hier_indexer: pinned (brute force, closed
+  forms, invariants). The router's aggregation rule is a reading of the pages;
+  agreement with the authors' own (unpublished) router is "parity unpinned".
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+__all__ = [
+    "pool_keys", "router_values", "route", "routed_scores", "select_topk", "score_topk",
+    "dsa_index_dense", "hier_rerank", "misa_indexer", "misa_hier_indexer", "mac_count",
+]
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+# ------------------------------------------------------------------ a1: pooling
+def pool_keys(k, B: int) -> np.ndarray:
+    """Mean-pooled keys of the complete blocks of each stored sequence.
+
+    MISA pages, "Methodologie: MISA" (block-pooled router): the prefix is cut
+    into blocks of B tokens and the indexer keys of each block are mean-pooled.
+    Block j covers tokens [jB, jB + B). Only complete blocks are stored here; a
+    query's partial last block depends on its own prefix and is pooled by the
+    router (``router_values``).
+
+    k: [nseq, L, d]  ->  Kbar: [nseq, L // B, d] float64
+    """
+    k = _f64(k)
+    nseq, L, d = k.shape
+    nb = L // B
+    out = np.zeros((nseq, nb, d))
+    for j in range(nb):
+        out[:, j, :] = k[:, j * B:(j + 1) * B, :].sum(axis=1) / B
+    return out
+
+
+# ------------------------------------------------------------------ a2: router
+def router_values(q_t, w_t, keys_seq, p: int, B: int):
+    """Per-head router importance of one query.
+
+    MISA pages, "Methodologie: MISA": the prefix of length p is split into
+    M = ceil(p / B) blocks; the router computes per-head affinities against the
+    mean-pooled keys and aggregates them into one importance per head.
+
+    Reading taken (the pages give no formula): the aggregate is the head's own
+    indexer term evaluated on the pooled keys,
+        r_g = w_g * sum_{j < M} max(q_g . Kbar_j, 0),
+    where Kbar_j is the mean of the keys of block j that the query can see (the
+    last block may be partial: mean over its visible tokens only).
+
+    Returns (r as float64 [H], r as exact Fractions [H]). The Fractions carry
+    the same quantity with the partial block's division done exactly, so that
+    ties between heads are decided on exact values.
+    """
+    q_t = _f64(q_t)
+    w_t = _f64(w_t)
+    keys = _f64(keys_seq)[:p]
+    H = q_t.shape[0]
+    M = -(-p // B)
+    # block j = tokens [jB, min(jB + B, p)); n_j of them are visible
+    n = np.array([min((j + 1) * B, p) - j * B for j in range(M)])
+    blk_sum = np.stack([keys[j * B:j * B + n[j]].sum(axis=0) for j in range(M)])   # [M, d]
+    a_sum = blk_sum @ q_t.T                       # [M, H]: q_g . (sum of block j's keys)
+    a = a_sum / n[:, None]                        # q_g . Kbar_j
+    r = w_t * np.maximum(a, 0.0).sum(axis=0)
+    r_exact = []
+    for g in range(H):
+        acc = Fraction(0)
+        for j in range(M):
+            v = Fraction(float(a_sum[j, g])) / int(n[j])
+            if v > 0:
+                acc += v
+        r_exact.append(Fraction(float(w_t[g])) * acc)
+    return r, r_exact
+
+
+def route(q, w, k, q_seq, q_len, B: int, h: int, queries=None):
+    """Routed head set of each query: the h heads of largest router importance.
+
+    MISA pages, MISA abstract and "Methodologie: MISA": the router keeps the
+    top-h heads per query. Ties go to the lower head id (reading: the pages are
+    silent; this mirrors the lower-token-index rule of the token top-k). The
+    set is returned in ascending head id.
+
+    Returns heads [nq, h] int32 and r [nq, H] float64 for the listed queries.
+    """
+    q = _f64(q)
+    w = _f64(w)
+    T, H, d = q.shape
+    qs = range(T) if queries is None else list(queries)
+    heads = np.zeros((len(qs), h), np.int32)
+    rr = np.zeros((len(qs), H))
+    for i, t in enumerate(qs):
+        r, r_exact = router_values(q[t], w[t], k[q_seq[t]], int(q_len[t]), B)
+        order = sorted(range(H), key=lambda g: (-r_exact[g], g))
+        heads[i] = np.sort(np.array(order[:h], np.int32))
+        rr[i] = r
+    return heads, rr
+
+
+# ------------------------------------------------------------------ a3: routed scoring
+def routed_scores(q_t, w_t, keys_seq, heads_t, p: int) -> np.ndarray:
+    """Index score of every visible token s < p with the given heads.
+
+    MISA pages, MISA abstract and "Methodologie: MISA" (sparse token scoring):
+    only the routed heads score every prefix token. The indexer score follows the
+    DSA indexer it replaces (a ReLU'd query-key product per head, weighted per
+    head and summed over heads):
+        S_s = sum_{g in R, ascending g} w_g * max(q_g . k_s, 0).
+    No 1/sqrt(d) factor: a positive global scale changes no selection.
+    """
+    q_t = _f64(q_t)
+    w_t = _f64(w_t)
+    keys = _f64(keys_seq)[:p]
+    S = np.zeros(p)
+    for g in sorted(int(x) for x in heads_t):
+        S = S + w_t[g] * np.maximum(keys @ q_t[g], 0.0)
+    return S
+
+
+# ------------------------------------------------------------------ a4: top-k
+def select_topk(S, k: int):
+    """The k best tokens of one score row.
+
+    Order tokens by (score descending, token index ascending) and keep the first
+    min(k, p); ties are broken by the lower token index. The selected set is
+    returned in ascending token index, padded with -1 (index) / 0.0 (score) to k.
+    """
+    S = _f64(S)
+    p = S.shape[0]
+    n = min(k, p)
+    order = np.lexsort((np.arange(p), -S))[:n]
+    sel = np.sort(order)
+    idx = np.full(k, -1, np.int64)
+    val = np.zeros(k)
+    idx[:n] = sel
+    val[:n] = S[sel]
+    return idx, val
+
+
+def score_topk(q, w, k, heads, q_seq, q_len, topk: int, queries=None):
+    """Routed scoring followed by the per-query top-k (MISA's selection).
+
+    heads: [nq, h] routed head ids of the listed queries (row i <-> query queries[i]).
+    Returns idx [nq, topk] int64 (ascending, -1 padded) and scores [nq, topk].
+    """
+    T = np.asarray(q).shape[0]
+    qs = range(T) if queries is None else list(queries)
+    idx = np.full((len(qs), topk), -1, np.int64)
+    val = np.zeros((len(qs), topk))
+    for i, t in enumerate(qs):
+        p = int(q_len[t])
+        S = routed_scores(q[t], w[t], k[q_seq[t]], heads[i], p)
+        idx[i], val[i] = select_topk(S, topk)
+    return idx, val
+
+
+# ------------------------------------------------------------------ a6: dense DSA
+def dsa_index_dense(q, w, k, q_seq, q_len, topk: int, queries=None):
+    """The dense DSA indexer: every one of the H heads scores every prefix token.
+
+    MISA pages, MISA abstract and "Probleemstelling": the DSA indexer scores
+    every prefix token with its full pool of H_I heads and keeps the top-k,
+    shared by all heads. Same score and selection rules as ``score_topk`` with
+    R = {0, ..., H-1}.
+    """
+    T, H, _ = np.asarray(q).shape
+    qs = range(T) if queries is None else list(queries)
+    all_heads = np.tile(np.arange(H, dtype=np.int32), (len(qs), 1))
+    return score_topk(q, w, k, all_heads, q_seq, q_len, topk, queries=qs)
+
+
+# ------------------------------------------------------------------ a5: MISA† re-rank
+def hier_rerank(q, w, k, cand, q_seq, q_len, topk: int, queries=None):
+    """Fine stage of MISA†: re-rank a candidate set with the full dense indexer.
+
+    MISA pages, "Hiërarchische Variant (MISA†)": the routed pass keeps an
+    enlarged candidate set of k' tokens; the original DSA indexer with all H_I
+    heads re-scores only those candidates and the final top-k is taken from them.
+    Ties go to the lower token index (not to the coarse rank). The returned
+    scores are dense scores.
+
+    cand: [nq, k'] ascending token ids, -1 padded (row i <-> query queries[i]).
+    """
+    q = _f64(q)
+    w = _f64(w)
+    T, H, _ = q.shape
+    qs = range(T) if queries is None else list(queries)
+    idx = np.full((len(qs), topk), -1, np.int64)
+    val = np.zeros((len(qs), topk))
+    for i, t in enumerate(qs):
+        p = int(q_len[t])
+        c = np.asarray(cand[i])
+        c = c[c >= 0]
+        keys = _f64(k[q_seq[t]])[c]
+        S = np.zeros(len(c))
+        for g in range(H):
+            S = S + w[t, g] * np.maximum(keys @ q[t, g], 0.0)
+        # rank candidates by (dense score desc, token id asc)
+        order = np.lexsort((c, -S))[:min(topk, len(c))]
+        sel = np.sort(order)                       # c ascending => slot order is token order
+        idx[i, :len(sel)] = c[sel]
+        val[i, :len(sel)] = S[sel]
+        assert np.all(c < p)
+    return idx, val
+
+
+# ------------------------------------------------------------------ whole indexers
+def misa_indexer(q, w, k, q_seq, q_len, B: int, h: int, topk: int, queries=None):
+    """MISA: route (top-h heads on pooled keys), routed scoring, top-k."""
+    heads, r = route(q, w, k, q_seq, q_len, B, h, queries=queries)
+    idx, val = score_topk(q, w, k, heads, q_seq, q_len, topk, queries=queries)
+    return heads, r, idx, val
+
+
+def misa_hier_indexer(q, w, k, q_seq, q_len, B: int, h: int, kc: int, topk: int, queries=None):
+    """MISA†: routed pass keeps k' candidates, the dense indexer re-ranks them to k."""
+    heads, r = route(q, w, k, q_seq, q_len, B, h, queries=queries)
+    cand, _ = score_topk(q, w, k, heads, q_seq, q_len, kc, queries=queries)
+    idx, val = hier_rerank(q, w, k, cand, q_seq, q_len, topk, queries=queries)
+    return heads, cand, idx, val
+
+
+def mac_count(q_len, H: int, h: int, d: int, B: int) -> int:
+    """Multiply-accumulates of MISA as the pages count them: O(h*L + H_I*M) per query
+    ("Methodologie: MISA"), i.e. d * (h * p + H * ceil(p / B)) summed over queries."""
+    return int(sum(d * (h * int(p) + H * (-(-int(p) // B))) for p in q_len))

@@ -1,0 +1,380 @@
+"""Pins of the CPU oracle against things other than itself: a hand-worked
+example, brute force on tiny inputs, closed forms, special cases that reduce to
+library routines, and the invariants the MISA pages state (routing h = H
+reproduces the dense indexer; the hierarchical variant with a full candidate set
+reproduces DSA). Each test is chosen so that a plausible mistake in the oracle
+(a dropped ReLU or weight, a wrong block boundary, a flipped tie rule, an
+off-by-one prefix) fails it.
+"""
+import itertools
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import misa_oracle as O
+from routed_token_indexer_amd.workloads import make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _parse_golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, rhs = (s.strip() for s in line.split("=", 1))
+            rows = [[float(x) for x in r.split()] for r in rhs.split(";")]
+            arr = np.array(rows if len(rows) > 1 else rows[0])
+            vals[key] = arr.item() if arr.size == 1 else arr
+    return vals
+
+
+# ------------------------------------------------------------------ hand-worked example
+@pytest.fixture(scope="module")
+def hand():
+    g = _parse_golden("hand_example.txt")
+    keys = g["keys"][None]               # [1, 5, 2]
+    q = np.stack([g["q"], g["q"]])       # queries A and B share q and w
+    w = np.stack([g["w"], g["w"]])
+    q_seq = np.array([0, 0], np.int32)
+    q_len = np.array([int(g["A.p"]), int(g["B.p"])], np.int32)
+    return g, keys, q, w, q_seq, q_len
+
+
+def test_hand_router_values(hand):
+    g, keys, q, w, q_seq, q_len = hand
+    B = int(g["B"])
+    for i, tag in enumerate("AB"):
+        r, r_exact = O.router_values(q[i], w[i], keys[0], int(q_len[i]), B)
+        np.testing.assert_array_equal(r, g[f"{tag}.r"])
+        assert [float(x) for x in r_exact] == list(g[f"{tag}.r"])
+
+
+def test_hand_route(hand):
+    g, keys, q, w, q_seq, q_len = hand
+    B = int(g["B"])
+    h1, _ = O.route(q, w, keys, q_seq, q_len, B, 1)
+    assert h1[0].tolist() == [int(x) for x in np.atleast_1d(g["A.heads_h1"])]
+    assert h1[1].tolist() == [int(x) for x in np.atleast_1d(g["B.heads_h1"])]   # exact tie -> lower id
+    h2, _ = O.route(q, w, keys, q_seq, q_len, B, 2)
+    assert h2[0].tolist() == g["A.heads_h2"].astype(int).tolist()
+
+
+def test_hand_scores_and_topk(hand):
+    g, keys, q, w, q_seq, q_len = hand
+    S = O.routed_scores(q[0], w[0], keys[0], [0], 5)
+    np.testing.assert_array_equal(S, g["A.routed_scores_h1"])
+    for kk in (2, 3):
+        idx, _ = O.select_topk(S, kk)
+        assert idx.tolist() == g[f"A.routed_top{kk}"].astype(int).tolist()
+    Sd = O.routed_scores(q[0], w[0], keys[0], [0, 1, 2], 5)
+    np.testing.assert_array_equal(Sd, g["A.dense_scores"])
+    di, _ = O.dsa_index_dense(q, w, keys, q_seq, q_len, 2, queries=[0])
+    assert di[0].tolist() == g["A.dense_top2"].astype(int).tolist()
+    bi, _ = O.score_topk(q, w, keys, np.array([[0]]), q_seq, q_len, 2, queries=[1])
+    assert bi[0].tolist() == g["B.routed_top2"].astype(int).tolist()
+
+
+def test_hand_hier(hand):
+    g, keys, q, w, q_seq, q_len = hand
+    B = int(g["B"])
+    _, cand, idx, val = O.misa_hier_indexer(q, w, keys, q_seq, q_len, B, 1, 3, 2, queries=[0])
+    assert cand[0].tolist() == [0, 2, 4]
+    assert idx[0].tolist() == g["A.hier_kc3_top2"].astype(int).tolist()
+    np.testing.assert_array_equal(val[0], g["A.hier_kc3_top2_scores"])
+    _, cand, idx, _ = O.misa_hier_indexer(q, w, keys, q_seq, q_len, B, 1, 2, 2, queries=[0])
+    assert idx[0].tolist() == g["A.hier_kc2_top2"].astype(int).tolist()
+
+
+def test_hand_pool(hand):
+    g, keys, *_ = hand
+    kb = O.pool_keys(keys, 2)
+    np.testing.assert_array_equal(kb[0], g["pooled_blocks_L5"])     # the partial block is not stored
+
+
+# ------------------------------------------------------------------ pooling
+def test_pool_mass_and_bruteforce():
+    x = make_inputs("c0")
+    k = x.k.astype(np.float64)
+    B = x.cfg.B
+    kb = O.pool_keys(k, B)
+    nb = k.shape[1] // B
+    # mass invariant: sum_j B * Kbar_j == sum of the keys of the complete blocks
+    np.testing.assert_allclose((kb * B).sum(axis=1), k[:, :nb * B].sum(axis=1), rtol=0, atol=1e-12)
+    # scalar brute force on a few entries
+    for j, c in [(0, 0), (3, 7), (nb - 1, 31)]:
+        s = 0.0
+        for t in range(j * B, j * B + B):
+            s += float(k[0, t, c])
+        assert kb[0, j, c] == pytest.approx(s / B, abs=1e-15)
+
+
+def test_pool_grid_exact():
+    x = make_inputs("c0", mode="grid")
+    kb = O.pool_keys(x.k, x.cfg.B)
+    # grid keys are multiples of 2^-4; B = 32 so the means are multiples of 2^-9, exact in fp64
+    assert np.all(np.round(kb * 2 ** 9) == kb * 2 ** 9)
+
+
+# ------------------------------------------------------------------ router
+def _exact_r(q_t, w_t, keys, p, B):
+    """Router importance in exact rational arithmetic, from integer loops."""
+    H, d = q_t.shape
+    out = []
+    for g in range(H):
+        acc = Fraction(0)
+        for j in range(0, p, B):
+            blk = range(j, min(j + B, p))
+            mean = [sum(Fraction(float(keys[s, c])) for s in blk) / len(blk) for c in range(d)]
+            a = sum(Fraction(float(q_t[g, c])) * mean[c] for c in range(d))
+            acc += max(a, Fraction(0))
+        out.append(Fraction(float(w_t[g])) * acc)
+    return out
+
+
+def test_router_exact_small():
+    x = make_inputs("c0", mode="grid")
+    for t in (0, 5, 15):
+        p = int(x.q_len[t])
+        _, r_exact = O.router_values(x.q[t], x.w[t], x.k[0], p, x.cfg.B)
+        assert r_exact == _exact_r(x.q[t], x.w[t], x.k[0], p, x.cfg.B)
+
+
+def test_router_subset_bruteforce_c0():
+    """The routed set maximises the summed importance over all C(H, h) subsets,
+    with the lexicographically smallest set among equal sums (lower ids win)."""
+    for mode in ("gauss", "grid"):
+        x = make_inputs("c0", mode=mode)
+        H, h = x.cfg.H, x.cfg.h
+        heads, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, h)
+        for t in range(x.cfg.T):
+            r = _exact_r(x.q[t], x.w[t], x.k[0], int(x.q_len[t]), x.cfg.B) if mode == "grid" else \
+                O.router_values(x.q[t], x.w[t], x.k[0], int(x.q_len[t]), x.cfg.B)[1]
+            best = max(itertools.combinations(range(H), h), key=lambda c: (sum(r[g] for g in c),
+                                                                           [-g for g in c]))
+            assert heads[t].tolist() == list(best), (mode, t)
+
+
+def test_router_grid_has_ties():
+    """Grid mode produces exact router ties, so the tie rule is exercised."""
+    x = make_inputs("c0", mode="grid")
+    ties = 0
+    for t in range(x.cfg.T):
+        _, r = O.router_values(x.q[t], x.w[t], x.k[0], int(x.q_len[t]), x.cfg.B)
+        ties += len(r) - len(set(r))
+    assert ties > 0
+
+
+def test_router_block1_mass_equals_dense_mass():
+    """B = 1: every block is one token, so sum_g r_g = sum_s S_dense(s)."""
+    x = make_inputs("c0")
+    for t in (0, 9):
+        p = int(x.q_len[t])
+        r, _ = O.router_values(x.q[t], x.w[t], x.k[0], p, 1)
+        S = O.routed_scores(x.q[t], x.w[t], x.k[0], range(x.cfg.H), p)
+        assert r.sum() == pytest.approx(S.sum(), rel=1e-12)
+
+
+def test_router_single_block_closed_form():
+    """B >= p: one block, the mean of all visible keys."""
+    x = make_inputs("c0")
+    t = 3
+    p = int(x.q_len[t])
+    r, _ = O.router_values(x.q[t], x.w[t], x.k[0], p, 4096)
+    mean = np.mean(x.k[0, :p].astype(np.float64), axis=0)
+    expect = x.w[t].astype(np.float64) * np.maximum(x.q[t].astype(np.float64) @ mean, 0)
+    np.testing.assert_allclose(r, expect, rtol=1e-12, atol=1e-15)
+
+
+def test_router_partial_block_and_causality():
+    x = make_inputs("c0")
+    t = 0
+    p = int(x.q_len[t])          # 497 = 15 * 32 + 17: partial last block of 17 tokens
+    assert p % x.cfg.B == 17
+    k2 = x.k.copy()
+    k2[0, p:] = 100.0            # tokens the query cannot see
+    r1, _ = O.router_values(x.q[t], x.w[t], x.k[0], p, x.cfg.B)
+    r2, _ = O.router_values(x.q[t], x.w[t], k2[0], p, x.cfg.B)
+    np.testing.assert_array_equal(r1, r2)
+    # a partial block of identical keys v pools to v itself
+    k3 = x.k[0].astype(np.float64).copy()
+    v = k3[0].copy()
+    k3[15 * 32:p] = v
+    r3, _ = O.router_values(x.q[t], x.w[t], k3, p, x.cfg.B)
+    full = O.pool_keys(k3[None, :480], x.cfg.B)[0]
+    a = np.maximum(x.q[t].astype(np.float64) @ full.T, 0).sum(axis=1) + np.maximum(x.q[t] @ v, 0)
+    np.testing.assert_allclose(r3, x.w[t] * a, rtol=1e-12)
+
+
+def test_router_scale_invariance():
+    x = make_inputs("c0")
+    h0, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h)
+    h1, _ = O.route(x.q, x.w * 4.0, x.k * 2.0, x.q_seq, x.q_len, x.cfg.B, x.cfg.h)
+    np.testing.assert_array_equal(h0, h1)
+
+
+def test_router_h_equals_H():
+    x = make_inputs("c0")
+    heads, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.H)
+    assert np.all(heads == np.arange(x.cfg.H))
+
+
+# ------------------------------------------------------------------ routed scores
+def test_scores_bruteforce_loops():
+    x = make_inputs("c0")
+    t, heads = 2, [1, 6]
+    p = int(x.q_len[t])
+    S = O.routed_scores(x.q[t], x.w[t], x.k[0], heads, p)
+    for s in (0, 17, p - 1):
+        tot = 0.0
+        for g in heads:
+            dot = 0.0
+            for c in range(x.cfg.d):
+                dot += float(x.q[t, g, c]) * float(x.k[0, s, c])
+            tot += float(x.w[t, g]) * max(dot, 0.0)
+        assert S[s] == pytest.approx(tot, rel=1e-12, abs=1e-15)
+    assert S.shape == (p,)
+
+
+def test_scores_single_head_is_relu_matvec():
+    x = make_inputs("c0")
+    p = 300
+    q1 = x.q[:1, :1]
+    w1 = np.ones((1, 1))
+    S = O.routed_scores(q1[0], w1[0], x.k[0], [0], p)
+    ref = np.maximum(np.dot(x.k[0, :p].astype(np.float64), q1[0, 0].astype(np.float64)), 0)
+    np.testing.assert_allclose(S, ref, rtol=1e-13, atol=1e-16)
+
+
+def test_scores_einsum_crosscheck():
+    x = make_inputs("c0")
+    t, heads = 7, [0, 3]
+    p = int(x.q_len[t])
+    S = O.routed_scores(x.q[t], x.w[t], x.k[0], heads, p)
+    D = np.einsum("sd,gd->sg", x.k[0, :p].astype(np.float64), x.q[t, heads].astype(np.float64))
+    ref = (np.clip(D, 0, None) * x.w[t, heads].astype(np.float64)).sum(axis=1)
+    np.testing.assert_allclose(S, ref, rtol=1e-12, atol=1e-15)
+
+
+def test_routed_h_equals_H_is_dense_bitwise():
+    x = make_inputs("c0")
+    hh, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.H)
+    ri, rv = O.score_topk(x.q, x.w, x.k, hh, x.q_seq, x.q_len, x.cfg.topk)
+    di, dv = O.dsa_index_dense(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.topk)
+    np.testing.assert_array_equal(ri, di)
+    np.testing.assert_array_equal(rv, dv)
+
+
+# ------------------------------------------------------------------ top-k
+def _rank_count_select(S, k):
+    p = len(S)
+    sel = []
+    for s in range(p):
+        better = sum(1 for u in range(p) if S[u] > S[s] or (S[u] == S[s] and u < s))
+        if better < k:
+            sel.append(s)
+    return sel
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_topk_rank_count_bruteforce(seed):
+    rng = np.random.default_rng(seed)
+    S = rng.integers(0, 6, size=90).astype(np.float64)          # many exact ties
+    for k in (1, 10, 37, 90, 120):
+        idx, val = O.select_topk(S, k)
+        n = min(k, len(S))
+        assert idx[:n].tolist() == _rank_count_select(S, k)
+        assert np.all(idx[n:] == -1)
+        np.testing.assert_array_equal(val[:n], S[idx[:n]])
+
+
+def test_topk_all_when_short():
+    S = np.array([3.0, 1.0, 2.0])
+    idx, _ = O.select_topk(S, 8)
+    assert idx.tolist() == [0, 1, 2, -1, -1, -1, -1, -1]
+
+
+def test_topk_matches_stable_sort_gauss():
+    rng = np.random.default_rng(5)
+    S = rng.standard_normal(5000)
+    idx, _ = O.select_topk(S, 700)
+    ref = np.sort(np.argsort(-S, kind="stable")[:700])
+    np.testing.assert_array_equal(idx, ref)
+
+
+# ------------------------------------------------------------------ MISA†
+def test_hier_full_candidates_is_dense():
+    for mode in ("gauss", "grid"):
+        x = make_inputs("c0", mode=mode)
+        kc = int(x.q_len.max())               # k' >= p: every token is a candidate
+        _, _, idx, val = O.misa_hier_indexer(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h,
+                                             kc, x.cfg.topk)
+        di, dv = O.dsa_index_dense(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.topk)
+        np.testing.assert_array_equal(idx, di)
+        np.testing.assert_array_equal(val, dv)
+
+
+def test_hier_kc_equals_k_is_misa_set():
+    x = make_inputs("c0")
+    heads, _, mi, _ = O.misa_indexer(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h, x.cfg.topk)
+    _, _, hi, _ = O.misa_hier_indexer(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h,
+                                      x.cfg.topk, x.cfg.topk)
+    np.testing.assert_array_equal(mi, hi)
+
+
+def test_hier_recall_identity_and_monotone():
+    x = make_inputs("c0")
+    di, _ = O.dsa_index_dense(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.topk)
+    prev = None
+    for kc in (64, 128, 256):
+        _, cand, idx, _ = O.misa_hier_indexer(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h,
+                                              kc, x.cfg.topk)
+        rec = []
+        for t in range(x.cfg.T):
+            F, C, D = set(idx[t]) - {-1}, set(cand[t]) - {-1}, set(di[t]) - {-1}
+            assert F & D == C & D
+            rec.append(len(C & D))
+        if prev is not None:
+            assert all(a >= b for a, b in zip(rec, prev))
+        prev = rec
+
+
+def test_hier_h_equals_H_is_dense():
+    x = make_inputs("c0")
+    _, _, hi, _ = O.misa_hier_indexer(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.H,
+                                      128, x.cfg.topk)
+    di, _ = O.dsa_index_dense(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.topk)
+    np.testing.assert_array_equal(hi, di)
+
+
+# ------------------------------------------------------------------ causality / prefill
+def test_prefill_row_equals_decode_call():
+    x = make_inputs("c2", L=256, T=256)
+    heads, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h, queries=[200])
+    idx_p, val_p = O.score_topk(x.q, x.w, x.k, heads, x.q_seq, x.q_len, 64, queries=[200])
+    # a decode call on the same sequence truncated to p = t + 1 = 201 tokens
+    kt = x.k[:, :201]
+    hd, _ = O.route(x.q[200:201], x.w[200:201], kt, np.array([0]), np.array([201]), x.cfg.B, x.cfg.h)
+    np.testing.assert_array_equal(hd, heads)
+    idx_d, val_d = O.score_topk(x.q[200:201], x.w[200:201], kt, hd, np.array([0]), np.array([201]), 64)
+    np.testing.assert_array_equal(idx_p, idx_d)
+    np.testing.assert_array_equal(val_p, val_d)
+
+
+def test_grid_mode_exactness_bounds():
+    """In grid mode every score is a multiple of 2^-10 well below 2^24 units, so
+    fp32 reproduces it exactly in any summation order."""
+    x = make_inputs("c0", mode="grid")
+    di, dv = O.dsa_index_dense(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.topk)
+    units = dv * 2 ** 10
+    assert np.all(units == np.round(units)) and np.abs(units).max() < 2 ** 24
+
+
+def test_mac_count_formula():
+    # O(h L + H M) per query: d * (h * p + H * ceil(p / B))
+    assert O.mac_count([5], 3, 1, 2, 2) == 2 * (1 * 5 + 3 * 3)
+    assert O.mac_count([32768] * 4, 64, 8, 128, 64) == 4 * 128 * (8 * 32768 + 64 * 512)
