@@ -1,0 +1,198 @@
+/*
+ * misa.h — C ABI of the MISA routed token indexer for AMD Instinct MI355X (gfx950).
+ *
+ * The library implements the indexer of DeepSeek-Sparse-Attention-style
+ * inference as described on the MISA pages (arXiv 2605.07363, "MISA: Mixture of
+ * Indexer Sparse Attention for Long-Context LLM Inference": the abstract, and
+ * gist.science's "Technische Samenvatting" with its sections "Probleemstelling",
+ * "Methodologie: MISA" and "Hiërarchische Variant (MISA†)"):
+ *
+ *   1. mean-pool the indexer keys into blocks of B tokens      (misa_pool_keys)
+ *   2. a router scores all H heads on the pooled keys and keeps
+ *      the top-h heads of each query                           (misa_route)
+ *   3. only the routed heads score every visible prefix token,
+ *      S[t][s] = sum_{g in R_t} w[t][g] * max(q[t][g] . k[s], 0),
+ *      and a per-query top-k keeps the selected tokens         (misa_score_topk)
+ *   4. MISA†: the routed pass keeps k' candidates, the dense
+ *      H-head indexer re-ranks them to the final k              (misa_hier_rerank)
+ *   5. the dense DSA indexer, all H heads                      (dsa_index_dense)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All array arguments are DEVICE pointers to caller-owned memory. The library
+ *    never retains, frees or allocates them, and allocates no device memory of
+ *    its own: scratch space is the caller's workspace `ws` of at least
+ *    misa_workspace_bytes(...) bytes (256-byte aligned). A workspace may be
+ *    reused by later calls on the same stream; calls that overlap in time must
+ *    not share one.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the legacy default
+ *    stream). Work is enqueued asynchronously on it; no call synchronizes.
+ *  - Layouts (row-major, contiguous):
+ *      q      bf16  [T][H][d]        per-head indexer queries
+ *      w      fp32  [T][H]           per-head weights
+ *      k      bf16  [nseq][Lmax][d]  one indexer key per token, shared by all heads
+ *      kbar   fp32  [nseq][Lmax/B][d] means of the complete blocks of B tokens
+ *      q_seq  int32 [T]              sequence of query t (0 <= q_seq < nseq)
+ *      q_len  int32 [T]              visible prefix p of query t (tokens 0..p-1;
+ *                                    a causal prefill query at position t has p = t+1)
+ *      heads  int32 [T][h]           routed head ids, ascending
+ *      idx    int32 [T][topk]        selected token ids, ascending, -1 padded
+ *      score  fp32  [T][topk]        their scores (0 in padded slots); may be NULL
+ *    q and k must be 16-byte aligned; other arrays 4-byte aligned.
+ *  - Supported sizes: d in {32, 64, 128, 256}; 1 <= H <= 64; 1 <= h <= H;
+ *    1 <= topk; T >= 0 (T = 0 is a no-op); 1 <= Lmax < 2^31; 1 <= B <= Lmax.
+ *  - Ties: tokens of equal score go to the lower token index; heads of equal
+ *    router importance go to the lower head id. Scores compare as reals (-0 == +0).
+ *  - Device-side values the host cannot check: a query with q_seq outside
+ *    [0, nseq) is treated as empty (idx all -1; routed heads 0..h-1); q_len is
+ *    clamped to [0, Lmax]; a head id outside [0, H) contributes nothing.
+ *  - Return value: MISA_OK (0) or a negative MISA_ERR_*. Arguments are checked
+ *    before anything is enqueued; on error nothing is enqueued and
+ *    misa_last_error() (thread-local) describes the problem.
+ */
+#ifndef MISA_H
+#define MISA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MISA_API __attribute__((visibility("default")))
+#else
+#define MISA_API
+#endif
+
+#define MISA_OK 0
+#define MISA_ERR_ARG (-1)        /* a size, range or null-pointer error            */
+#define MISA_ERR_ALIGN (-2)      /* a pointer is not aligned as required            */
+#define MISA_ERR_WORKSPACE (-3)  /* ws is NULL or smaller than misa_workspace_bytes */
+#define MISA_ERR_HIP (-4)        /* the HIP runtime refused a launch                */
+
+/* op codes of misa_workspace_bytes */
+#define MISA_OP_ROUTE 1
+#define MISA_OP_SCORE_TOPK 2
+#define MISA_OP_HIER_RERANK 3
+#define MISA_OP_DSA_DENSE 4
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+MISA_API int32_t misa_version(void);
+
+/* Human-readable name of a status code (static storage). */
+MISA_API const char* misa_status_string(int32_t code);
+
+/* Message describing the last error returned on the calling thread ("" if none). */
+MISA_API const char* misa_last_error(void);
+
+/*
+ * Workspace bytes needed by one call of `op` (MISA_OP_*) with these sizes.
+ * Arguments that an op does not use are ignored (kc only matters for
+ * MISA_OP_HIER_RERANK, B only for MISA_OP_ROUTE). Returns 0 if none is needed.
+ */
+MISA_API size_t misa_workspace_bytes(int32_t op, int64_t T, int32_t H, int64_t Lmax, int32_t B, int32_t topk,
+                            int32_t kc);
+
+/*
+ * Block mean-pooling of the indexer keys (MISA pages, "Methodologie: MISA":
+ * the prefix is split into blocks of B tokens and the router works on
+ * mean-pooled keys).
+ *   k     bf16 [nseq][Lmax][d]    in
+ *   kbar  fp32 [nseq][Lmax/B][d]  out: kbar[n][j] = mean of k[n][jB .. jB+B-1]
+ * Only complete blocks are written; a query's partial last block is pooled by
+ * misa_route from k. Deterministic (fixed summation order).
+ */
+MISA_API int32_t misa_pool_keys(const void* k, int64_t nseq, int64_t Lmax, int32_t d, int32_t B, float* kbar,
+                       void* stream);
+
+/*
+ * Block-pooled MoE router (MISA abstract; "Methodologie: MISA": per-head
+ * affinities with pooled keys over M = ceil(p/B) blocks, aggregated into one
+ * importance per head, top-h heads kept; cost O(H * M)).
+ * Importance of head g for query t (the last block may be partial: its mean is
+ * over the tokens the query sees):
+ *     r[t][g] = w[t][g] * sum_{j < ceil(p/B)} max(q[t][g] . Kbar_j, 0)
+ *   q, w, k, kbar, q_seq, q_len   in (kbar from misa_pool_keys with the same B)
+ *   heads       int32 [T][h]  out: the h heads of largest r, ascending id
+ *   router_key  fp32  [T][H]  out (may be NULL): r[t][g]
+ *   ws / ws_bytes             workspace, misa_workspace_bytes(MISA_OP_ROUTE, T, H, Lmax, B, 0, 0)
+ */
+MISA_API int32_t misa_route(const void* q, const float* w, const void* k, const float* kbar, const int32_t* q_seq,
+                   const int32_t* q_len, int64_t T, int32_t H, int32_t d, int64_t nseq, int64_t Lmax,
+                   int32_t B, int32_t h, int32_t* heads, float* router_key, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/*
+ * Routed token scoring + per-query top-k (MISA abstract; "Methodologie: MISA",
+ * sparse token scoring: only the h routed heads score every prefix token; the
+ * final top-k comes from these reduced scores):
+ *     S[t][s] = sum_{g in heads[t]} w[t][g] * max(q[t][g] . k[q_seq[t]][s], 0),  s < q_len[t]
+ *   heads   int32 [T][h]   in (from misa_route, or any ids in [0, H))
+ *   idx     int32 [T][topk] out: the topk best s (ties: lower s), ascending, -1 padded;
+ *                           a query with q_len <= topk gets all of its prefix
+ *   score   fp32  [T][topk] out (may be NULL)
+ *   ws / ws_bytes           misa_workspace_bytes(MISA_OP_SCORE_TOPK, T, H, Lmax, 0, topk, 0)
+ * With topk = k' this is the coarse pass of MISA† (its idx is the candidate set).
+ */
+MISA_API int32_t misa_score_topk(const void* q, const float* w, const void* k, const int32_t* heads, int32_t h,
+                        const int32_t* q_seq, const int32_t* q_len, int64_t T, int32_t H, int32_t d,
+                        int64_t nseq, int64_t Lmax, int32_t topk, int32_t* idx, float* score, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/*
+ * Fine stage of MISA† ("Hiërarchische Variant (MISA†)": the dense DSA indexer,
+ * all H heads, re-scores only the k' candidates of the routed pass and keeps the
+ * final top-k).
+ *   cand   int32 [T][kc]  in: candidate token ids, ascending, -1 padded (the idx
+ *                          output of misa_score_topk with topk = kc). Only the
+ *                          leading run of strictly increasing ids in [0, q_len)
+ *                          is used; the first entry that breaks it ends the list.
+ *   idx    int32 [T][topk] out: the topk candidates of best dense score (ties:
+ *                          lower token id), ascending token id, -1 padded
+ *   score  fp32  [T][topk] out (may be NULL): their dense scores
+ *   Requires kc >= topk.  ws: misa_workspace_bytes(MISA_OP_HIER_RERANK, T, H, Lmax, 0, topk, kc)
+ */
+MISA_API int32_t misa_hier_rerank(const void* q, const float* w, const void* k, const int32_t* cand, int32_t kc,
+                         const int32_t* q_seq, const int32_t* q_len, int64_t T, int32_t H, int32_t d,
+                         int64_t nseq, int64_t Lmax, int32_t topk, int32_t* idx, float* score, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/*
+ * Dense DSA indexer (MISA abstract; "Probleemstelling": the DSA indexer scores
+ * every prefix token with all H_I heads and keeps the top-k, shared by all
+ * heads). misa_score_topk with heads = {0..H-1}; the same summation order, so a
+ * routed call with h = H and heads 0..H-1 returns bit-identical results.
+ *   ws: misa_workspace_bytes(MISA_OP_DSA_DENSE, T, H, Lmax, 0, topk, 0)
+ */
+MISA_API int32_t dsa_index_dense(const void* q, const float* w, const void* k, const int32_t* q_seq,
+                        const int32_t* q_len, int64_t T, int32_t H, int32_t d, int64_t nseq, int64_t Lmax,
+                        int32_t topk, int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Full score rows of the routed scoring step (a diagnostic of step 3 above):
+ * scores fp32 [T][Lmax], row t filled for s < q_len[t], other entries untouched.
+ * heads may be NULL (then h must equal H: dense scores).
+ */
+MISA_API int32_t misa_debug_scores(const void* q, const float* w, const void* k, const int32_t* heads, int32_t h,
+                          const int32_t* q_seq, const int32_t* q_len, int64_t T, int32_t H, int32_t d,
+                          int64_t nseq, int64_t Lmax, float* scores, void* stream);
+
+/*
+ * Event timing of one internal kernel class, for measurement tools:
+ * kernel 1 = token scoring, 2 = top-k, 3 = router, 4 = pooling.
+ * After misa_timing_begin(kernel, capacity), each launch of that kernel (up to
+ * `capacity` launches) is bracketed by hipEventRecord on its stream;
+ * misa_timing_end waits for the recorded events and returns the summed
+ * duration in ms and the number of launches timed. Process-wide state: not for
+ * concurrent use from several threads.
+ */
+MISA_API int32_t misa_timing_begin(int32_t kernel, int32_t capacity);
+MISA_API int32_t misa_timing_end(float* total_ms, int32_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MISA_H */

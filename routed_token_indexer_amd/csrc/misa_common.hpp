@@ -1,0 +1,48 @@
+// Shared device helpers of the MISA indexer library (gfx950 / CDNA4).
+//
+// Only this library uses them; the CPU oracle shares nothing with it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace misa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// D = A(16x32) * B(32x16) + C on the matrix cores, bf16 in, fp32 accumulate.
+// Lane i supplies A row (i % 16) and B column (i % 16), 8 consecutive k-slots
+// starting at 8 * (i / 16); it receives D column (i % 16), rows 4 * (i / 16) + 0..3.
+__device__ __forceinline__ floatx4 mfma_16x16x32(const u32x4& a, const u32x4& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// Order-preserving map of a float score onto uint32: a > b  <=>  key(a) > key(b).
+// -0.0 and +0.0 map to the same key (scores compare as reals).
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_score(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+}  // namespace misa

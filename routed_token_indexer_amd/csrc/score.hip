@@ -1,0 +1,282 @@
+// Token scoring of the MISA / DSA indexer on the gfx950 matrix cores.
+//
+// MISA pages (MISA abstract; gist.science "Methodologie: MISA", sparse token
+// scoring): only the routed heads score every prefix token. The score of token s
+// for query t with head set R is
+//     S[t][s] = sum_{g in R} w[t][g] * max(q[t][g] . k[s], 0).
+// The dense DSA indexer ("Probleemstelling") is the same with R = all H heads,
+// and the MISA† fine stage ("Hiërarchische Variant") applies it to a candidate
+// list instead of the whole prefix.
+//
+// Layout of the work: a workgroup owns a tile of QT queries (their gathered
+// head rows, NHP rows per query, held in registers as MFMA A-fragments) and a
+// chunk of keys. Its four waves walk the chunk in 16-key tiles: B-fragments are
+// loaded straight from HBM (each lane reads 64 contiguous bytes of one key),
+// one 16x16x32 MFMA per (row tile, 32-dim slice), then ReLU, the head weight and
+// the per-query head sum are applied in registers and one fp32 score per
+// (query, key) is stored. The key-dimension slots are permuted identically on
+// both operands (lane group g of the wave covers dims [g*D/4, (g+1)*D/4)), which
+// leaves every dot product unchanged and makes the key loads contiguous.
+#include "misa_common.hpp"
+#include "misa_internal.hpp"
+
+namespace misa {
+
+namespace {
+
+// Row length of query t (tokens it can see, or valid candidates) and its key
+// sequence; seq = -1 marks an absent or invalid query (it produces nothing).
+__device__ __forceinline__ void query_info(const ScoreArgs& a, int64_t t, int& seq, int& n) {
+  seq = -1;
+  n = 0;
+  if (t >= a.T) return;
+  const int sq = a.q_seq[t];
+  if (sq < 0 || sq >= a.nseq) return;
+  seq = sq;
+  if (a.row_len) {
+    n = a.row_len[t];
+  } else {
+    const int p = a.q_len[t];
+    n = p < 0 ? 0 : (p > a.Lmax ? (int)a.Lmax : p);
+  }
+}
+
+// Head id of row slot hs of query t (-1: padding row or invalid id).
+__device__ __forceinline__ int row_head(const ScoreArgs& a, int64_t t, int hs) {
+  if (hs >= a.hh) return -1;
+  const int g = a.heads ? a.heads[t * a.hh + hs] : hs;
+  return (g >= 0 && g < a.H) ? g : -1;
+}
+
+template <int D, int NHP, int RT, int KT, bool GATHER>
+__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
+  constexpr int QT = (16 * RT) / NHP;       // query slots of the tile
+  constexpr int KS = D / 32;                // 32-wide k-steps
+  constexpr int DG = D / 4;                 // dims per lane group
+  // per-lane output slots: how many different slots one lane writes
+  constexpr int NOUT = NHP == 4 ? RT : (NHP == 8 ? RT : QT);
+  static_assert(QT >= 1 && (16 * RT) % NHP == 0, "row tiling");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15;                // MFMA column (key) / A row within a tile
+  const int grp = lane >> 4;                // lane group
+  const int64_t tile = (int64_t)gridDim.y - 1 - blockIdx.y;   // longest prefixes first
+  const int64_t t0 = tile * QT;
+
+  // ---- tile-wide slot info (indexed with compile-time indices only)
+  int slot_seq[QT], slot_n[QT];
+  int nmax = 0;
+#pragma unroll
+  for (int s = 0; s < QT; ++s) {
+    query_info(a, t0 + s, slot_seq[s], slot_n[s]);
+    nmax = max(nmax, slot_n[s]);
+  }
+  const int c_begin = blockIdx.x * a.chunk;
+  if (c_begin >= nmax) return;
+  const int c_end = min(c_begin + a.chunk, nmax);
+
+  // ---- A fragments (gathered query rows) and row weights, loaded once
+  u32x4 afrag[RT][KS];
+  float wrow[RT][4];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const int row = 16 * r + col;
+    const int64_t t = t0 + row / NHP;
+    int seq, n;
+    query_info(a, t, seq, n);
+    const int head = seq < 0 ? -1 : row_head(a, t, row % NHP);
+    const uint16_t* qp = a.q + ((t * a.H + (head < 0 ? 0 : head)) * D) + grp * DG;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (head >= 0) v = *reinterpret_cast<const u32x4*>(qp + ks * 8);
+      afrag[r][ks] = v;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row2 = 16 * r + 4 * grp + j;
+      const int64_t t2 = t0 + row2 / NHP;
+      int seq2, n2;
+      query_info(a, t2, seq2, n2);
+      const int hd = seq2 < 0 ? -1 : row_head(a, t2, row2 % NHP);
+      wrow[r][j] = hd < 0 ? 0.f : a.w[t2 * a.H + hd];
+    }
+  }
+
+  // ---- the slots this lane stores (slot index, its sequence and row length)
+  int out_slot[NOUT], out_seq[NOUT], out_n[NOUT];
+#pragma unroll
+  for (int i = 0; i < NOUT; ++i) {
+    out_slot[i] = NHP == 4 ? 4 * i + grp : (NHP == 8 ? 2 * i + (grp >> 1) : i);
+    query_info(a, t0 + out_slot[i], out_seq[i], out_n[i]);
+  }
+  const bool writer = NHP == 4 ? true : (NHP == 8 ? (grp & 1) == 0 : grp == 0);
+
+  // ---- one pass per distinct key source among the slots
+#pragma unroll
+  for (int lead = 0; lead < QT; ++lead) {
+    if (slot_seq[lead] < 0) continue;
+    bool first = true;
+#pragma unroll
+    for (int s = 0; s < lead; ++s)
+      if (!GATHER && slot_seq[s] == slot_seq[lead]) first = false;
+    if (!first) continue;
+    int pass_n = 0;
+#pragma unroll
+    for (int s = 0; s < QT; ++s)
+      if (s == lead || (!GATHER && slot_seq[s] == slot_seq[lead])) pass_n = max(pass_n, slot_n[s]);
+    const int p_end = min(c_end, pass_n);
+    const uint16_t* kseq = a.k + (int64_t)slot_seq[lead] * a.Lmax * D + grp * DG;
+    const int32_t* crow = GATHER ? a.cand + (t0 + lead) * a.kc : nullptr;
+    // which of this lane's output slots belong to this pass
+    bool in_pass[NOUT];
+#pragma unroll
+    for (int i = 0; i < NOUT; ++i)
+      in_pass[i] = writer && out_seq[i] >= 0 &&
+                   (GATHER ? out_slot[i] == lead : out_seq[i] == slot_seq[lead]);
+
+    for (int base = c_begin + wave * (16 * KT); base < p_end; base += 4 * 16 * KT) {
+      u32x4 bfrag[KT][KS];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const int s = base + kt * 16 + col;
+        int64_t key = -1;
+        if (s < p_end) key = GATHER ? (int64_t)crow[s] : (int64_t)s;
+        const uint16_t* kp = kseq + (key < 0 ? 0 : key) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (key >= 0) v = *reinterpret_cast<const u32x4*>(kp + ks * 8);
+          bfrag[kt][ks] = v;
+        }
+      }
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        floatx4 acc[RT];
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          acc[r] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) acc[r] = mfma_16x16x32(afrag[r][ks], bfrag[kt][ks], acc[r]);
+        }
+        // epilogue: ReLU, head weight, per-query head sum (rows 4*grp..4*grp+3 of each tile)
+        float part[RT];
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          part[r] = wrow[r][0] * fmaxf(acc[r][0], 0.f) + wrow[r][1] * fmaxf(acc[r][1], 0.f) +
+                    wrow[r][2] * fmaxf(acc[r][2], 0.f) + wrow[r][3] * fmaxf(acc[r][3], 0.f);
+        }
+        float val[NOUT];
+        if constexpr (NHP == 4) {
+#pragma unroll
+          for (int r = 0; r < RT; ++r) val[r] = part[r];
+        } else if constexpr (NHP == 8) {
+#pragma unroll
+          for (int r = 0; r < RT; ++r) val[r] = part[r] + __shfl_xor(part[r], 16, kWave);
+        } else {
+          constexpr int m = NHP / 16;
+#pragma unroll
+          for (int s = 0; s < QT; ++s) {
+            float v = 0.f;
+#pragma unroll
+            for (int i = 0; i < m; ++i) v += part[s * m + i];
+            v += __shfl_xor(v, 16, kWave);
+            v += __shfl_xor(v, 32, kWave);
+            val[s] = v;
+          }
+        }
+        const int s_out = base + kt * 16 + col;
+#pragma unroll
+        for (int i = 0; i < NOUT; ++i) {
+          if (in_pass[i] && s_out < p_end && s_out < out_n[i])
+            a.out[(t0 + out_slot[i]) * a.out_stride + s_out] = val[i] + 0.f;
+        }
+      }
+    }
+  }
+}
+
+template <int D, int NHP, int RT, int KT, bool GATHER>
+hipError_t launch_cfg(const ScoreArgs& a, int64_t ntile, int nchunk, hipStream_t st) {
+  dim3 grid(nchunk, (unsigned)ntile);
+  hipLaunchKernelGGL((score_kernel<D, NHP, RT, KT, GATHER>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// Keys per workgroup: wide tiles (prefill) take 2048-key chunks; otherwise the
+// chunk shrinks until the grid has about 2048 workgroups (at least 256 keys).
+inline int pick_chunk(int64_t ntile, int64_t max_len, bool wide) {
+  if (wide) return 2048;
+  int64_t c = 256;
+  while (c < 8192 && c * 2048 < max_len * ntile) c *= 2;
+  return (int)c;
+}
+
+template <int D, bool GATHER>
+hipError_t launch_d(ScoreArgs a, int nhp, bool wide, int64_t max_len, hipStream_t st) {
+  // rows per query nhp in {4, 8, 16, 32, 48, 64}; wide = many queries per key chunk (prefill)
+#define MISA_SCORE_CASE(NHP_, RT_, KT_)                                      \
+  {                                                                          \
+    constexpr int QT_ = (16 * RT_) / NHP_;                                   \
+    const int64_t ntile = (a.T + QT_ - 1) / QT_;                             \
+    if (a.chunk <= 0) a.chunk = pick_chunk(ntile, max_len, wide);            \
+    const int nchunk = (int)((max_len + a.chunk - 1) / a.chunk);             \
+    return launch_cfg<D, NHP_, RT_, KT_, GATHER>(a, ntile, nchunk, st);      \
+  }
+  if constexpr (!GATHER) {
+    if (wide) {
+      switch (nhp) {
+        case 4: MISA_SCORE_CASE(4, 4, 2)
+        case 8: MISA_SCORE_CASE(8, 8, 2)
+        case 16: MISA_SCORE_CASE(16, 8, 2)
+        case 32: MISA_SCORE_CASE(32, 8, 2)
+        case 48: MISA_SCORE_CASE(48, 6, 2)
+        case 64: MISA_SCORE_CASE(64, 8, 2)
+        default: return hipErrorInvalidValue;
+      }
+    }
+  }
+  {
+    switch (nhp) {
+      case 4: MISA_SCORE_CASE(4, 1, 4)
+      case 8: MISA_SCORE_CASE(8, 1, 4)
+      case 16: MISA_SCORE_CASE(16, 1, 4)
+      case 32: MISA_SCORE_CASE(32, 2, 4)
+      case 48: MISA_SCORE_CASE(48, 3, 4)
+      case 64: MISA_SCORE_CASE(64, 4, 4)
+      default: return hipErrorInvalidValue;
+    }
+  }
+#undef MISA_SCORE_CASE
+}
+
+}  // namespace
+
+int score_rows_per_query(int hh) {
+  if (hh <= 4) return 4;
+  if (hh <= 8) return 8;
+  return 16 * ((hh + 15) / 16);
+}
+
+hipError_t launch_score(const ScoreArgs& a, int d, bool gather, bool wide, int64_t max_len, hipStream_t st) {
+  const int nhp = score_rows_per_query(a.hh);
+  if (gather) {
+    switch (d) {
+      case 32: return launch_d<32, true>(a, nhp, wide, max_len, st);
+      case 64: return launch_d<64, true>(a, nhp, wide, max_len, st);
+      case 128: return launch_d<128, true>(a, nhp, wide, max_len, st);
+      case 256: return launch_d<256, true>(a, nhp, wide, max_len, st);
+    }
+  } else {
+    switch (d) {
+      case 32: return launch_d<32, false>(a, nhp, wide, max_len, st);
+      case 64: return launch_d<64, false>(a, nhp, wide, max_len, st);
+      case 128: return launch_d<128, false>(a, nhp, wide, max_len, st);
+      case 256: return launch_d<256, false>(a, nhp, wide, max_len, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace misa

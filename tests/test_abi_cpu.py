@@ -1,0 +1,145 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point include/misa.h declares, sizes workspaces, and rejects bad
+arguments before enqueuing anything (every call here fails validation, so no
+kernel is ever launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "misa.h")
+LIB = os.path.join(ROOT, "routed_token_indexer_amd", "libmisa.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmisa.so not built")
+
+
+def declared_symbols():
+    txt = open(HEADER).read()
+    return re.findall(r"^MISA_API\s+[\w\s\*]+?\b(\w+)\s*\(", txt, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def L():
+    from routed_token_indexer_amd import _lib
+    return _lib.lib()
+
+
+def test_header_declares_the_five_indexer_calls():
+    syms = declared_symbols()
+    for name in ("misa_pool_keys", "misa_route", "misa_score_topk", "misa_hier_rerank", "dsa_index_dense"):
+        assert name in syms
+
+
+def test_every_declared_symbol_is_exported(L):
+    syms = declared_symbols()
+    assert len(syms) >= 12
+    raw = ctypes.CDLL(LIB)
+    for name in syms:
+        assert hasattr(raw, name), name
+
+
+def test_binding_covers_every_symbol():
+    from routed_token_indexer_amd import _lib
+    assert set(declared_symbols()) == set(_lib._SIGNATURES)
+
+
+def test_version_and_status(L):
+    assert L.misa_version() >= 100
+    assert L.misa_status_string(0) == b"MISA_OK"
+    assert L.misa_status_string(-3) == b"MISA_ERR_WORKSPACE"
+    assert L.misa_status_string(-99) == b"MISA_ERR_UNKNOWN"
+
+
+def test_workspace_sizes(L):
+    from routed_token_indexer_amd import _lib as B
+    # scores of every (query, token) pair, fp32, rounded to 256 bytes
+    assert B.workspace_bytes(B.OP_SCORE_TOPK, 4, 64, 131072, 0, 8192) == 4 * 131072 * 4
+    assert B.workspace_bytes(B.OP_DSA_DENSE, 3, 8, 100, 0, 10) == 1280
+    assert B.workspace_bytes(B.OP_HIER_RERANK, 4, 64, 131072, 0, 2048, 8192) == 4 * 8192 * 4 + 256
+    assert B.workspace_bytes(B.OP_SCORE_TOPK, 0, 64, 131072, 0, 8192) == 0
+    # the router splits long prefixes over chunks for few queries, one chunk for many
+    assert B.workspace_bytes(B.OP_ROUTE, 4, 64, 131072, 128) > 0
+    assert B.workspace_bytes(B.OP_ROUTE, 16384, 64, 16384, 64) == 0
+
+
+FAKE = ctypes.c_void_p(1 << 20)      # aligned, never dereferenced: validation fails first
+
+
+def _err(L):
+    return L.misa_last_error().decode()
+
+
+def test_route_rejects_bad_sizes(L):
+    rc = L.misa_route(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 100, 4, 4096, 64, 8, FAKE, None, FAKE, 1 << 20, None)
+    assert rc == -1 and "d = 100" in _err(L)
+    rc = L.misa_route(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 128, 4, 4096, 64, 65, FAKE, None, FAKE, 1 << 20, None)
+    assert rc == -1 and "h = 65" in _err(L)
+    rc = L.misa_route(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 65, 128, 4, 4096, 64, 8, FAKE, None, FAKE, 1 << 20, None)
+    assert rc == -1 and "H = 65" in _err(L)
+    rc = L.misa_route(None, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 128, 4, 4096, 64, 8, FAKE, None, FAKE, 1 << 20, None)
+    assert rc == -1 and "null" in _err(L)
+    rc = L.misa_route(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 128, 4, 4096, 0, 8, FAKE, None, FAKE, 1 << 20, None)
+    assert rc == -1 and "B = 0" in _err(L)
+
+
+def test_route_rejects_small_workspace(L):
+    rc = L.misa_route(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 128, 4, 131072, 128, 8, FAKE, None, FAKE, 16, None)
+    assert rc == -3 and "workspace" in _err(L)
+    rc = L.misa_route(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 128, 4, 131072, 128, 8, FAKE, None, None, 0, None)
+    assert rc == -3
+
+
+def test_alignment_errors(L):
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    rc = L.misa_score_topk(odd, FAKE, FAKE, FAKE, 8, FAKE, FAKE, 4, 64, 128, 4, 4096, 64, FAKE, None, FAKE,
+                           1 << 30, None)
+    assert rc == -2
+    ws_odd = ctypes.c_void_p((1 << 20) + 64)
+    rc = L.dsa_index_dense(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 128, 4, 4096, 64, FAKE, None, ws_odd, 1 << 30, None)
+    assert rc == -2 and "256-byte" in _err(L)
+
+
+def test_score_topk_and_dense_checks(L):
+    rc = L.misa_score_topk(FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE, 4, 64, 128, 4, 4096, 0, FAKE, None, FAKE, 1 << 30,
+                           None)
+    assert rc == -1 and "topk" in _err(L)
+    rc = L.misa_score_topk(FAKE, FAKE, FAKE, None, 8, FAKE, FAKE, 4, 64, 128, 4, 4096, 64, FAKE, None, FAKE, 1 << 30,
+                           None)
+    assert rc == -1 and "heads" in _err(L)
+    rc = L.misa_score_topk(FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE, 4, 64, 128, 4, 4096, 64, None, None, FAKE, 1 << 30,
+                           None)
+    assert rc == -1 and "idx" in _err(L)
+    rc = L.dsa_index_dense(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 128, 0, 4096, 64, FAKE, None, FAKE, 1 << 30, None)
+    assert rc == -1 and "nseq" in _err(L)
+    rc = L.dsa_index_dense(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 128, 4, 4096, 64, FAKE, None, FAKE, 100, None)
+    assert rc == -3
+
+
+def test_hier_rerank_checks(L):
+    rc = L.misa_hier_rerank(FAKE, FAKE, FAKE, FAKE, 100, FAKE, FAKE, 4, 64, 128, 4, 4096, 200, FAKE, None, FAKE,
+                            1 << 30, None)
+    assert rc == -1 and "kc = 100 < topk = 200" in _err(L)
+    rc = L.misa_hier_rerank(FAKE, FAKE, FAKE, None, 300, FAKE, FAKE, 4, 64, 128, 4, 4096, 200, FAKE, None, FAKE,
+                            1 << 30, None)
+    assert rc == -1 and "cand" in _err(L)
+
+
+def test_pool_checks(L):
+    assert L.misa_pool_keys(FAKE, 4, 4096, 128, 0, FAKE, None) == -1
+    assert L.misa_pool_keys(FAKE, 4, 4096, 128, 8192, FAKE, None) == -1
+    assert L.misa_pool_keys(None, 4, 4096, 128, 64, FAKE, None) == -1
+    assert L.misa_pool_keys(FAKE, 0, 4096, 128, 64, FAKE, None) == 0      # nothing to do
+
+
+def test_empty_batch_is_a_noop(L):
+    # T = 0: valid, nothing enqueued, no pointer touched
+    assert L.misa_score_topk(None, None, None, None, 8, None, None, 0, 64, 128, 4, 4096, 64, None, None, None, 0,
+                             None) == 0
+    assert L.dsa_index_dense(None, None, None, None, None, 0, 64, 128, 4, 4096, 64, None, None, None, 0, None) == 0
+
+
+def test_timing_api_arguments(L):
+    assert L.misa_timing_begin(9, 10) == -1
+    assert L.misa_timing_begin(1, 0) == -1

@@ -1,0 +1,301 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle on the same seeded
+inputs. Reduced shapes span several tiles and ragged tails; both value modes
+(Gaussian: tolerances; integer grid: bit-exact)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import misa_oracle as O
+from routed_token_indexer_amd import _lib as M
+from routed_token_indexer_amd.workloads import make_inputs
+
+from parity import (OverlapTally, check_router, check_scores, oracle_rows, run_misa, selected_scores_ok,
+                    upload)
+
+pytestmark = pytest.mark.gpu
+
+# reduced shapes: (config, overrides) -- lengths chosen off the 16-key tile and block grids
+CASES = {
+    "c0": ("c0", {}),
+    "c1r": ("c1", dict(L=3001, T=4, nseq=4, topk=256)),
+    "c3r": ("c3", dict(L=2500, T=16, nseq=16, topk=300)),
+    "c4r": ("c4", dict(L=5000, T=4, nseq=4, kc=1024, topk=256)),
+    "c2r": ("c2", dict(L=700, T=700, topk=128)),
+}
+MODES = ["gauss", "grid"]
+
+_cache = {}
+
+
+def get(case, mode):
+    key = (case, mode)
+    if key not in _cache:
+        name, ov = CASES[case]
+        x = make_inputs(name, mode=mode, **ov)
+        print(f"[parity] case={case} mode={mode} T={x.cfg.T} L={x.cfg.L} H={x.cfg.H} d={x.cfg.d}", flush=True)
+        _cache[key] = (x, upload(x))
+    return _cache[key]
+
+
+def queries_of(x, limit=48):
+    T = x.cfg.T
+    if T <= limit:
+        return list(range(T))
+    rng = np.random.default_rng(7)
+    pick = set(rng.choice(T, size=limit - 6, replace=False).tolist())
+    pick |= {0, 1, x.cfg.topk - 1, x.cfg.topk, T - 2, T - 1}
+    return sorted(t for t in pick if 0 <= t < T)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("case", list(CASES))
+def test_pool(case, mode):
+    x, dev = get(case, mode)
+    kb = M.pool_keys(dev["k"], x.cfg.B).cpu().numpy()
+    ref = O.pool_keys(x.k, x.cfg.B)
+    if mode == "grid":
+        np.testing.assert_array_equal(kb, ref.astype(np.float32))
+    else:
+        np.testing.assert_allclose(kb, ref, rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("case", list(CASES))
+def test_route(case, mode):
+    x, dev = get(case, mode)
+    kbar = M.pool_keys(dev["k"], x.cfg.B)
+    rk = torch.empty((x.cfg.T, x.cfg.H), dtype=torch.float32, device="cuda")
+    heads = M.route(dev["q"], dev["w"], dev["k"], kbar, dev["q_seq"], dev["q_len"], x.cfg.B, x.cfg.h,
+                    router_key=rk).cpu().numpy()
+    qs = queries_of(x)
+    check_router(x, heads[qs], qs, x.cfg.h, exact=(mode == "grid"))
+    _, r = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h, queries=qs)
+    np.testing.assert_allclose(rk.cpu().numpy()[qs], r, rtol=2e-5 if mode == "gauss" else 1e-6,
+                               atol=1e-6 * np.abs(r).max())
+    assert np.all(np.diff(heads, axis=1) > 0)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("case", list(CASES))
+def test_debug_scores_rows(case, mode):
+    x, dev = get(case, mode)
+    qs = queries_of(x)
+    ho, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h)
+    hd = torch.from_numpy(ho).cuda()
+    S = M.debug_scores(dev["q"], dev["w"], dev["k"], hd, dev["q_seq"], dev["q_len"]).cpu().numpy()
+    rows = oracle_rows(x, ho[qs], qs)
+    for t, row in zip(qs, rows):
+        check_scores(S[t, :len(row)], row, exact=(mode == "grid"), label=f"{case}/{mode} t={t}")
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("case", list(CASES))
+def test_score_topk(case, mode):
+    """Top-k with the oracle's head sets (decoupled from the router)."""
+    x, dev = get(case, mode)
+    exact = mode == "grid"
+    ho, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h)
+    _, _, idx, sc = run_misa(dev, x.cfg, heads=ho)
+    qs = queries_of(x)
+    oi, _ = O.score_topk(x.q, x.w, x.k, ho[qs], x.q_seq, x.q_len, x.cfg.topk, queries=qs)
+    rows = oracle_rows(x, ho[qs], qs)
+    tally = OverlapTally()
+    for i, t in enumerate(qs):
+        tally.add(idx[t], oi[i], rows[i], x.cfg.topk, exact, label=f"{case}/{mode} t={t}")
+        selected_scores_ok(idx[t], sc[t], rows[i], x.cfg.topk, exact, label=f"{case}/{mode} t={t}")
+    tally.check()
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("case", list(CASES))
+def test_misa_end_to_end(case, mode):
+    """pool -> route -> score_topk on the GPU against the oracle's whole MISA indexer."""
+    x, dev = get(case, mode)
+    exact = mode == "grid"
+    _, heads, idx, sc = run_misa(dev, x.cfg)
+    qs = queries_of(x)
+    use = check_router(x, heads[qs], qs, x.cfg.h, exact)
+    oi, _ = O.score_topk(x.q, x.w, x.k, use, x.q_seq, x.q_len, x.cfg.topk, queries=qs)
+    rows = oracle_rows(x, use, qs)
+    tally = OverlapTally()
+    for i, t in enumerate(qs):
+        tally.add(idx[t], oi[i], rows[i], x.cfg.topk, exact, label=f"{case}/{mode} t={t}")
+    tally.check()
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("case", list(CASES))
+def test_dense(case, mode):
+    x, dev = get(case, mode)
+    exact = mode == "grid"
+    idx, sc = M.dsa_index_dense(dev["q"], dev["w"], dev["k"], dev["q_seq"], dev["q_len"], x.cfg.topk)
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    qs = queries_of(x, limit=24)
+    oi, _ = O.dsa_index_dense(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.topk, queries=qs)
+    all_heads = np.tile(np.arange(x.cfg.H), (len(qs), 1))
+    rows = oracle_rows(x, all_heads, qs)
+    tally = OverlapTally()
+    for i, t in enumerate(qs):
+        tally.add(idx[t], oi[i], rows[i], x.cfg.topk, exact, label=f"{case}/{mode} t={t}")
+        selected_scores_ok(idx[t], sc[t], rows[i], x.cfg.topk, exact, label=f"{case}/{mode} t={t}")
+    tally.check()
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("case", ["c0", "c1r", "c4r"])
+def test_hier_rerank(case, mode):
+    """MISA†: the GPU re-rank of a candidate set against the oracle's re-rank of the
+    same set, and the GPU's whole coarse-to-fine pass against the oracle's."""
+    x, dev = get(case, mode)
+    exact = mode == "grid"
+    kc = x.cfg.kc or 4 * x.cfg.topk
+    ho, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h)
+    hd = torch.from_numpy(ho).cuda()
+    cand, _ = M.score_topk(dev["q"], dev["w"], dev["k"], hd, dev["q_seq"], dev["q_len"], kc)
+    idx, sc = M.hier_rerank(dev["q"], dev["w"], dev["k"], cand, dev["q_seq"], dev["q_len"], x.cfg.topk)
+    cand, idx, sc = cand.cpu().numpy(), idx.cpu().numpy(), sc.cpu().numpy()
+    qs = queries_of(x)
+    # the same candidate set on both sides
+    ri, rv = O.hier_rerank(x.q, x.w, x.k, cand[qs], x.q_seq, x.q_len, x.cfg.topk, queries=qs)
+    tally = OverlapTally()
+    for i, t in enumerate(qs):
+        dense_row = O.routed_scores(x.q[t], x.w[t], x.k[x.q_seq[t]], range(x.cfg.H), int(x.q_len[t]))
+        tally.add(idx[t], ri[i], dense_row, x.cfg.topk, exact, label=f"{case}/{mode} t={t}")
+        selected_scores_ok(idx[t], sc[t], dense_row, x.cfg.topk, exact, label=f"{case}/{mode} t={t}")
+        assert set(idx[t][idx[t] >= 0].tolist()) <= set(cand[t][cand[t] >= 0].tolist())
+    tally.check()
+    # end to end against the oracle's MISA† with the same heads
+    _, oc, oi, _ = O.misa_hier_indexer(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h, kc, x.cfg.topk,
+                                       queries=qs)
+    hits = sum(len(np.intersect1d(idx[t][idx[t] >= 0], oi[i][oi[i] >= 0])) for i, t in enumerate(qs))
+    tot = sum(min(x.cfg.topk, int(x.q_len[t])) for t in qs)
+    if exact:
+        for i, t in enumerate(qs):
+            np.testing.assert_array_equal(idx[t], oi[i])
+            np.testing.assert_array_equal(cand[t], oc[i])
+    else:
+        assert hits / tot >= 0.99
+
+
+# ------------------------------------------------------------------ invariants on the GPU
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("case", ["c0", "c1r", "c2r"])
+def test_routed_all_heads_is_dense_bitwise(case, mode):
+    x, dev = get(case, mode)
+    allh = torch.arange(x.cfg.H, dtype=torch.int32, device="cuda").repeat(x.cfg.T, 1).contiguous()
+    ri, rs = M.score_topk(dev["q"], dev["w"], dev["k"], allh, dev["q_seq"], dev["q_len"], x.cfg.topk)
+    di, ds = M.dsa_index_dense(dev["q"], dev["w"], dev["k"], dev["q_seq"], dev["q_len"], x.cfg.topk)
+    assert torch.equal(ri, di) and torch.equal(rs, ds)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("case", ["c0", "c1r"])
+def test_hier_full_candidates_is_dense_bitwise(case, mode):
+    x, dev = get(case, mode)
+    ho, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h)
+    hd = torch.from_numpy(ho).cuda()
+    kc = x.cfg.L
+    cand, _ = M.score_topk(dev["q"], dev["w"], dev["k"], hd, dev["q_seq"], dev["q_len"], kc)
+    hi, hs = M.hier_rerank(dev["q"], dev["w"], dev["k"], cand, dev["q_seq"], dev["q_len"], x.cfg.topk)
+    di, ds = M.dsa_index_dense(dev["q"], dev["w"], dev["k"], dev["q_seq"], dev["q_len"], x.cfg.topk)
+    assert torch.equal(hi, di) and torch.equal(hs, ds)
+
+
+def test_prefill_row_equals_decode_call():
+    """Causality: a prefill query at position t gives what a decode call with p = t + 1 gives."""
+    x, dev = get("c2r", "grid")
+    ho, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h)
+    hd = torch.from_numpy(ho).cuda()
+    pi, ps = M.score_topk(dev["q"], dev["w"], dev["k"], hd, dev["q_seq"], dev["q_len"], x.cfg.topk)
+    for t in (5, 127, 128, 450, 699):
+        sl = slice(t, t + 1)
+        di, ds = M.score_topk(dev["q"][sl].contiguous(), dev["w"][sl].contiguous(), dev["k"], hd[sl].contiguous(),
+                              dev["q_seq"][sl].contiguous(), dev["q_len"][sl].contiguous(), x.cfg.topk)
+        assert torch.equal(pi[t], di[0]) and torch.equal(ps[t], ds[0])
+
+
+# ------------------------------------------------------------------ edge cases
+def test_empty_and_invalid_queries():
+    x, dev = get("c1r", "grid")
+    q_len = dev["q_len"].clone()
+    q_seq = dev["q_seq"].clone()
+    q_len[0] = 0          # empty prefix
+    q_seq[1] = 99         # sequence out of range: treated as empty
+    q_len[2] = 10 ** 9    # clamped to Lmax
+    kbar = M.pool_keys(dev["k"], x.cfg.B)
+    heads = M.route(dev["q"], dev["w"], dev["k"], kbar, q_seq, q_len, x.cfg.B, x.cfg.h)
+    idx, sc = M.score_topk(dev["q"], dev["w"], dev["k"], heads, q_seq, q_len, x.cfg.topk)
+    di, _ = M.dsa_index_dense(dev["q"], dev["w"], dev["k"], q_seq, q_len, x.cfg.topk)
+    h = heads.cpu().numpy()
+    assert h[0].tolist() == list(range(x.cfg.h)) and h[1].tolist() == list(range(x.cfg.h))
+    for out in (idx, di):
+        o = out.cpu().numpy()
+        assert np.all(o[0] == -1) and np.all(o[1] == -1)
+    hi = h[2:3]
+    oi, _ = O.score_topk(x.q, x.w, x.k, hi, x.q_seq, x.q_len, x.cfg.topk, queries=[2])
+    np.testing.assert_array_equal(idx.cpu().numpy()[2], oi[0])
+
+
+def test_short_prefix_takes_all():
+    x, dev = get("c2r", "gauss")
+    ho, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h)
+    _, _, idx, sc = run_misa(dev, x.cfg, heads=ho)
+    for t in (0, 1, 63, 126, 127):
+        p = t + 1
+        assert idx[t][:p].tolist() == list(range(p))
+        assert np.all(idx[t][p:] == -1) and np.all(sc[t][p:] == 0)
+
+
+@pytest.mark.parametrize("topk", [1, 2, 3000, 3001, 5000])
+def test_topk_extremes(topk):
+    x, dev = get("c1r", "grid")
+    ho, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h)
+    _, _, idx, _ = run_misa(dev, x.cfg, heads=ho, topk=topk)
+    oi, _ = O.score_topk(x.q, x.w, x.k, ho, x.q_seq, x.q_len, topk)
+    np.testing.assert_array_equal(idx, oi)
+
+
+def test_all_equal_scores_tie_break():
+    """Every score equal (zero keys): the lowest token indices win."""
+    x, dev = get("c1r", "grid")
+    k0 = torch.zeros_like(dev["k"])
+    idx, sc = M.dsa_index_dense(dev["q"], dev["w"], k0, dev["q_seq"], dev["q_len"], 100)
+    assert torch.equal(idx.cpu(), torch.arange(100, dtype=torch.int32).repeat(4, 1))
+    assert torch.all(sc == 0)
+
+
+def test_empty_batch_noop():
+    x, dev = get("c0", "grid")
+    e = lambda t: t[:0].contiguous()
+    idx, sc = M.dsa_index_dense(e(dev["q"]), e(dev["w"]), dev["k"], e(dev["q_seq"]), e(dev["q_len"]), 8)
+    assert idx.shape == (0, 8)
+
+
+@pytest.mark.parametrize("d", [32, 64, 256])
+@pytest.mark.parametrize("H,h", [(8, 2), (40, 5), (64, 16)])
+def test_shapes_head_dims(d, H, h):
+    """Other head dims and head counts (padding rows, 48-row tiles), grid-exact."""
+    x = make_inputs("c1", mode="grid", L=1200, T=3, nseq=3, H=H, d=d, h=h, B=64, topk=100)
+    dev = upload(x)
+    _, heads, idx, sc = run_misa(dev, x.cfg)
+    ho = check_router(x, heads, list(range(3)), h, exact=True)
+    oi, _ = O.score_topk(x.q, x.w, x.k, ho, x.q_seq, x.q_len, 100)
+    np.testing.assert_array_equal(idx, oi)
+    di, _ = M.dsa_index_dense(dev["q"], dev["w"], dev["k"], dev["q_seq"], dev["q_len"], 100)
+    od, _ = O.dsa_index_dense(x.q, x.w, x.k, x.q_seq, x.q_len, 100)
+    np.testing.assert_array_equal(di.cpu().numpy(), od)
+
+
+def test_non_power_of_two_block():
+    x = make_inputs("c1", mode="gauss", L=2000, T=4, nseq=4, B=48, topk=200)
+    dev = upload(x)
+    kb = M.pool_keys(dev["k"], 48).cpu().numpy()
+    np.testing.assert_allclose(kb, O.pool_keys(x.k, 48), rtol=1e-5, atol=1e-6)
+    _, heads, idx, _ = run_misa(dev, x.cfg)
+    use = check_router(x, heads, list(range(4)), x.cfg.h, exact=False)
+    oi, _ = O.score_topk(x.q, x.w, x.k, use, x.q_seq, x.q_len, 200)
+    rows = oracle_rows(x, use, range(4))
+    tally = OverlapTally()
+    for t in range(4):
+        tally.add(idx[t], oi[t], rows[t], 200, exact=False)
+    tally.check()
