@@ -146,11 +146,13 @@ MISA_API int32_t misa_score_topk(const void* q, const float* w, const void* k, c
  * all H heads, re-scores only the k' candidates of the routed pass and keeps the
  * final top-k).
  *   cand   int32 [T][kc]  in: candidate token ids, ascending, -1 padded (the idx
- *                          output of misa_score_topk with topk = kc). Only the
- *                          leading run of strictly increasing ids in [0, q_len)
- *                          is used; the first entry that breaks it ends the list.
+ *                          output of misa_score_topk with topk = kc). Entries
+ *                          outside [0, q_len) are not candidates; each valid
+ *                          entry is scored once per occurrence.
  *   idx    int32 [T][topk] out: the topk candidates of best dense score (ties:
- *                          lower token id), ascending token id, -1 padded
+ *                          lower candidate slot, i.e. lower token id for an
+ *                          ascending list), in candidate-slot order (ascending
+ *                          token id), -1 padded when fewer than topk are valid
  *   score  fp32  [T][topk] out (may be NULL): their dense scores
  *   Requires kc >= topk.  ws: misa_workspace_bytes(MISA_OP_HIER_RERANK, T, H, Lmax, 0, topk, kc)
  */
@@ -181,7 +183,8 @@ MISA_API int32_t misa_debug_scores(const void* q, const float* w, const void* k,
 
 /*
  * Event timing of one internal kernel class, for measurement tools:
- * kernel 1 = token scoring, 2 = top-k, 3 = router, 4 = pooling.
+ * kernel 1 = token scoring over prefixes (routed or dense), 2 = top-k,
+ * 3 = router, 4 = pooling, 5 = token scoring over candidate lists (re-rank).
  * After misa_timing_begin(kernel, capacity), each launch of that kernel (up to
  * `capacity` launches) is bracketed by hipEventRecord on its stream;
  * misa_timing_end waits for the recorded events and returns the summed

@@ -30,6 +30,7 @@ KERNEL_SCORE = 1
 KERNEL_TOPK = 2
 KERNEL_ROUTE = 3
 KERNEL_POOL = 4
+KERNEL_GATHER_SCORE = 5
 
 _lib = None
 

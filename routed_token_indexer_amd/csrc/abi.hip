@@ -63,6 +63,14 @@ int32_t check_ws(const char* fn, void* ws, size_t ws_bytes, size_t need) {
 
 bool wide_tiles(int64_t T, int64_t nseq) { return T >= 64 && T >= 8 * nseq; }
 
+// Workspace of scoring + selection over rows of at most max_len: the fp32 score
+// rows, then (for few long rows) the split top-k's state.
+size_t select_ws_bytes(int64_t T, int64_t max_len) {
+  size_t b = round_up((size_t)T * (size_t)max_len * sizeof(float));
+  if (misa::use_split_topk(T, max_len)) b += round_up(misa::split_topk_ws_bytes(T, max_len));
+  return b;
+}
+
 // ---------------------------------------------------------------- timing
 struct Timing {
   std::mutex mu;
@@ -115,9 +123,9 @@ size_t misa_workspace_bytes(int32_t op, int64_t T, int32_t H, int64_t Lmax, int3
     }
     case MISA_OP_SCORE_TOPK:
     case MISA_OP_DSA_DENSE:
-      return round_up((size_t)T * (size_t)Lmax * sizeof(float));
+      return select_ws_bytes(T, Lmax);
     case MISA_OP_HIER_RERANK:
-      return round_up((size_t)T * (size_t)(kc > 0 ? kc : 0) * sizeof(float)) + round_up((size_t)T * sizeof(int32_t));
+      return select_ws_bytes(T, kc > 0 ? kc : 0);
   }
   return 0;
 }
@@ -181,10 +189,9 @@ namespace {
 
 // Scoring (routed / dense / gathered) into `scores`, then top-k.
 int32_t score_and_select(const char* fn, const void* q, const float* w, const void* k, const int32_t* heads,
-                         int32_t hh, const int32_t* cand, int32_t kc, const int32_t* row_len,
-                         const int32_t* q_seq, const int32_t* q_len, int64_t T, int32_t H, int32_t d,
-                         int64_t nseq, int64_t Lmax, int32_t topk, int32_t* idx, float* score, float* scores,
-                         int64_t stride, hipStream_t st) {
+                         int32_t hh, const int32_t* cand, int32_t kc, const int32_t* q_seq, const int32_t* q_len,
+                         int64_t T, int32_t H, int32_t d, int64_t nseq, int64_t Lmax, int32_t topk, int32_t* idx,
+                         float* score, float* scores, int64_t stride, hipStream_t st) {
   misa::ScoreArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.w = w;
@@ -194,7 +201,6 @@ int32_t score_and_select(const char* fn, const void* q, const float* w, const vo
   a.q_seq = q_seq;
   a.q_len = q_len;
   a.cand = cand;
-  a.row_len = row_len;
   a.kc = kc;
   a.T = T;
   a.H = H;
@@ -203,16 +209,29 @@ int32_t score_and_select(const char* fn, const void* q, const float* w, const vo
   a.out = scores;
   a.out_stride = stride;
   a.chunk = 0;
+  a.hist = nullptr;
   const bool gather = cand != nullptr;
-  misa::timing_before(misa::KID_SCORE, st);
-  hipError_t e = misa::launch_score(a, d, gather, !gather && wide_tiles(T, nseq), gather ? kc : Lmax, st);
-  misa::timing_after(misa::KID_SCORE, st);
+  const int64_t max_len = gather ? kc : Lmax;
+  const bool wide = !gather && wide_tiles(T, nseq);
+  const bool split = idx && misa::use_split_topk(T, max_len);
+  misa::SplitTopkWs sw{};
+  hipError_t e = hipSuccess;
+  if (split) {
+    void* base = reinterpret_cast<char*>(scores) + round_up((size_t)T * (size_t)stride * sizeof(float));
+    sw = misa::split_topk_carve(base, T, max_len);
+    e = misa::launch_zero(sw.hist, misa::split_topk_zero_words(T), st);
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (!wide) a.hist = sw.hist;   // the decode scoring kernel builds the level-1 histogram
+  }
+  const int kid = gather ? misa::KID_GATHER_SCORE : misa::KID_SCORE;
+  misa::timing_before(kid, st);
+  e = misa::launch_score(a, d, gather, wide, max_len, st);
+  misa::timing_after(kid, st);
   if (e != hipSuccess) return hip_status(e, fn);
   if (!idx) return ok();
   misa::TopkArgs b{};
   b.scores = scores;
   b.stride = stride;
-  b.row_len = row_len;
   b.q_seq = q_seq;
   b.q_len = q_len;
   b.nseq = nseq;
@@ -224,7 +243,7 @@ int32_t score_and_select(const char* fn, const void* q, const float* w, const vo
   b.idx = idx;
   b.score = score;
   misa::timing_before(misa::KID_TOPK, st);
-  e = misa::launch_topk(b, st);
+  e = split ? misa::launch_topk_split(b, sw, a.hist != nullptr, st) : misa::launch_topk(b, st);
   misa::timing_after(misa::KID_TOPK, st);
   return hip_status(e, fn);
 }
@@ -254,8 +273,8 @@ int32_t misa_score_topk(const void* q, const float* w, const void* k, const int3
   if (rc) return rc;
   rc = check_ws(fn, ws, ws_bytes, misa_workspace_bytes(MISA_OP_SCORE_TOPK, T, H, Lmax, 0, topk, 0));
   if (rc) return rc;
-  return score_and_select(fn, q, w, k, heads, h, nullptr, 0, nullptr, q_seq, q_len, T, H, d, nseq, Lmax, topk, idx,
-                          score, static_cast<float*>(ws), Lmax, (hipStream_t)stream);
+  return score_and_select(fn, q, w, k, heads, h, nullptr, 0, q_seq, q_len, T, H, d, nseq, Lmax, topk, idx, score,
+                          static_cast<float*>(ws), Lmax, (hipStream_t)stream);
 }
 
 int32_t dsa_index_dense(const void* q, const float* w, const void* k, const int32_t* q_seq, const int32_t* q_len,
@@ -270,8 +289,8 @@ int32_t dsa_index_dense(const void* q, const float* w, const void* k, const int3
   if (rc) return rc;
   rc = check_ws(fn, ws, ws_bytes, misa_workspace_bytes(MISA_OP_DSA_DENSE, T, H, Lmax, 0, topk, 0));
   if (rc) return rc;
-  return score_and_select(fn, q, w, k, nullptr, H, nullptr, 0, nullptr, q_seq, q_len, T, H, d, nseq, Lmax, topk, idx,
-                          score, static_cast<float*>(ws), Lmax, (hipStream_t)stream);
+  return score_and_select(fn, q, w, k, nullptr, H, nullptr, 0, q_seq, q_len, T, H, d, nseq, Lmax, topk, idx, score,
+                          static_cast<float*>(ws), Lmax, (hipStream_t)stream);
 }
 
 int32_t misa_hier_rerank(const void* q, const float* w, const void* k, const int32_t* cand, int32_t kc,
@@ -290,13 +309,8 @@ int32_t misa_hier_rerank(const void* q, const float* w, const void* k, const int
   if (rc) return rc;
   rc = check_ws(fn, ws, ws_bytes, misa_workspace_bytes(MISA_OP_HIER_RERANK, T, H, Lmax, 0, topk, kc));
   if (rc) return rc;
-  float* scores = static_cast<float*>(ws);
-  int32_t* row_len = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + round_up((size_t)T * kc * sizeof(float)));
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t e = misa::launch_cand_count(cand, kc, q_seq, q_len, T, nseq, Lmax, row_len, st);
-  if (e != hipSuccess) return hip_status(e, fn);
-  return score_and_select(fn, q, w, k, nullptr, H, cand, kc, row_len, q_seq, q_len, T, H, d, nseq, Lmax, topk, idx,
-                          score, scores, kc, st);
+  return score_and_select(fn, q, w, k, nullptr, H, cand, kc, q_seq, q_len, T, H, d, nseq, Lmax, topk, idx, score,
+                          static_cast<float*>(ws), kc, (hipStream_t)stream);
 }
 
 int32_t misa_debug_scores(const void* q, const float* w, const void* k, const int32_t* heads, int32_t h,
@@ -309,13 +323,13 @@ int32_t misa_debug_scores(const void* q, const float* w, const void* k, const in
   if (!heads && h != H) return fail(MISA_ERR_ARG, "%s: heads = NULL needs h == H", fn);
   if (T == 0) return ok();
   if (!scores || !aligned(scores, 4)) return fail(MISA_ERR_ARG, "%s: null or misaligned scores", fn);
-  return score_and_select(fn, q, w, k, heads, h, nullptr, 0, nullptr, q_seq, q_len, T, H, d, nseq, Lmax, 0, nullptr,
-                          nullptr, scores, Lmax, (hipStream_t)stream);
+  return score_and_select(fn, q, w, k, heads, h, nullptr, 0, q_seq, q_len, T, H, d, nseq, Lmax, 0, nullptr, nullptr,
+                          scores, Lmax, (hipStream_t)stream);
 }
 
 int32_t misa_timing_begin(int32_t kernel, int32_t capacity) {
   std::lock_guard<std::mutex> lk(g_timing.mu);
-  if (kernel < 1 || kernel > 4 || capacity < 1) return fail(MISA_ERR_ARG, "misa_timing_begin: bad kernel or capacity");
+  if (kernel < 1 || kernel > 5 || capacity < 1) return fail(MISA_ERR_ARG, "misa_timing_begin: bad kernel or capacity");
   for (hipEvent_t ev : g_timing.ev) (void)hipEventDestroy(ev);
   g_timing.ev.assign(2 * (size_t)capacity, nullptr);
   for (auto& ev : g_timing.ev) {

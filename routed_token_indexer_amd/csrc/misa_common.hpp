@@ -45,4 +45,13 @@ __device__ __forceinline__ T wave_sum(T v) {
   return v;
 }
 
+// Visible prefix of query t clamped to [0, Lmax]; -1 for an invalid sequence id.
+__device__ __forceinline__ int query_prefix_len(const int32_t* q_seq, const int32_t* q_len, int64_t nseq,
+                                                int64_t Lmax, int64_t t) {
+  const int seq = q_seq[t];
+  if (seq < 0 || seq >= nseq) return -1;
+  const int p = q_len[t];
+  return p < 0 ? 0 : (p > Lmax ? (int)Lmax : p);
+}
+
 }  // namespace misa

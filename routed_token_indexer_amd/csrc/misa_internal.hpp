@@ -16,8 +16,7 @@ struct ScoreArgs {
   int hh;                   // heads per query
   const int32_t* q_seq;     // [T]
   const int32_t* q_len;     // [T]
-  const int32_t* cand;      // [T][kc] key indices (gather mode) or null
-  const int32_t* row_len;   // [T] valid candidates per row (gather mode) or null
+  const int32_t* cand;      // [T][kc] key indices (gather mode) or null; ids outside [0, q_len) are skipped
   int kc;
   int64_t T;
   int H;
@@ -26,6 +25,7 @@ struct ScoreArgs {
   float* out;               // [T][out_stride]
   int64_t out_stride;
   int chunk;                // keys per workgroup chunk
+  uint32_t* hist;           // optional [T][4096]: level-1 histogram of the written scores (decode kernel)
 };
 
 int score_rows_per_query(int hh);
@@ -55,19 +55,22 @@ struct RouteArgs {
   int nchunk;
   int chunk_blocks;
 };
+// Decode chunking of the pooled blocks (partials workspace in floats); prefill
+// shapes (many queries per sequence) route one query per wave and need none.
 size_t route_partial_floats(int64_t T, int H, int64_t Lmax, int B, int* nchunk, int* chunk_blocks);
+bool route_is_prefill(int64_t T, int64_t nseq);
 hipError_t launch_route(const RouteArgs& a, int d, hipStream_t st);
 
 // Per-row top-k of fp32 score rows.
 struct TopkArgs {
   const float* scores;      // [T][stride]
   int64_t stride;
-  const int32_t* row_len;   // [T] or null (then q_len clamped to [0, Lmax], q_seq checked)
-  const int32_t* q_seq;
+  const int32_t* q_seq;     // rows: q_len clamped to [0, Lmax] tokens, or kc slots in gather mode
+
   const int32_t* q_len;
   int64_t nseq;
   int64_t Lmax;
-  const int32_t* imap;      // [T][kc] output index map (gather mode) or null
+  const int32_t* imap;      // [T][kc] output index map (gather mode) or null; ids outside [0, q_len) -> -1
   int kc;
   int64_t T;
   int k;
@@ -76,12 +79,33 @@ struct TopkArgs {
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 
-// Number of leading valid entries of each candidate row.
-hipError_t launch_cand_count(const int32_t* cand, int kc, const int32_t* q_seq, const int32_t* q_len,
-                             int64_t T, int64_t nseq, int64_t Lmax, int32_t* row_len, hipStream_t st);
+// Split top-k for few long rows: several workgroups per row cooperate through
+// global memory (level-1 histogram, candidate list, per-chunk offsets).
+struct SplitTopkWs {
+  uint32_t* hist;      // [T][4096] level-1 histogram (zero on entry)
+  uint32_t* state;     // [T][8]
+  uint32_t* counter;   // [T][4] candidate-list cursor (zero on entry)
+  uint32_t* ndef;      // [T][nchunk] elements above the level-1 threshold bin
+  uint32_t* off;       // unused (kept for layout stability)
+  uint32_t* eqb;       // unused (kept for layout stability)
+  uint32_t* cand;      // [T][cap][2] (key, index) of the threshold bin
+  int64_t cap;
+  int chunk;
+  int nchunk;
+};
+// Workspace layout of the split path for T rows of at most max_len scores.
+size_t split_topk_ws_bytes(int64_t T, int64_t max_len);
+SplitTopkWs split_topk_carve(void* base, int64_t T, int64_t max_len);
+// Words at the start of the carved region that must be zero before the launch.
+int64_t split_topk_zero_words(int64_t T);
+hipError_t launch_zero(uint32_t* p, int64_t words, hipStream_t st);
+bool use_split_topk(int64_t T, int64_t max_len);
+// hist_done: the level-1 histogram was already accumulated by the scoring kernel.
+hipError_t launch_topk_split(const TopkArgs& a, const SplitTopkWs& w, bool hist_done, hipStream_t st);
+
 
 // Event timing of one internal kernel class (measurement aid).
-enum KernelId { KID_NONE = 0, KID_SCORE = 1, KID_TOPK = 2, KID_ROUTE = 3, KID_POOL = 4 };
+enum KernelId { KID_NONE = 0, KID_SCORE = 1, KID_TOPK = 2, KID_ROUTE = 3, KID_POOL = 4, KID_GATHER_SCORE = 5 };
 void timing_before(int kid, hipStream_t st);
 void timing_after(int kid, hipStream_t st);
 

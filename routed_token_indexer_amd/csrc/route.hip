@@ -15,12 +15,15 @@
 // inputs whose products and sums are exact in fp32 the ranking is exact too.
 // Ties go to the lower head id; the routed set is written in ascending head id.
 //
-// Work split: route_partial_kernel (grid = block chunks x queries) accumulates
-// sum_j max(q_g . Kbar_j, 0) for every head over its chunk of pooled blocks (one
-// lane per (head, block) pair, q_g held in registers, pooled-key rows read
-// through the cache). With one chunk per query (prefill) the same workgroup then
-// finalises; otherwise route_final_kernel sums the chunk partials in chunk order
-// (deterministic), adds the partial-block term and selects the heads.
+// The affinities q_g . Kbar_j run on the matrix cores: the query's head rows
+// are MFMA A-fragments, 16 pooled blocks form a B tile. Pooled keys are fp32,
+// so each B value is split into bf16 hi + lo (two MFMAs): hi + lo carries 16
+// significant bits, and pooled keys of small-integer inputs are exact in hi.
+//   decode  (few queries, long prefixes): a workgroup takes one query and a
+//           chunk of blocks, its waves split the blocks; a second small kernel
+//           sums the chunk partials in chunk order and selects the heads.
+//   prefill (many queries): a workgroup takes four queries, one per wave, and
+//           each wave walks all complete blocks of its query and selects.
 #include "misa_common.hpp"
 #include "misa_internal.hpp"
 
@@ -28,6 +31,11 @@ namespace misa {
 namespace {
 
 __device__ __forceinline__ void query_prefix(const RouteArgs& a, int64_t t, int& seq, int& p) {
+  if (t >= a.T) {
+    seq = -1;
+    p = 0;
+    return;
+  }
   seq = a.q_seq[t];
   p = a.q_len[t];
   if (seq < 0 || seq >= a.nseq) {
@@ -37,22 +45,40 @@ __device__ __forceinline__ void query_prefix(const RouteArgs& a, int64_t t, int&
   p = p < 0 ? 0 : (p > a.Lmax ? (int)a.Lmax : p);
 }
 
-// Sum of the keys of the partial last block, per dimension, into LDS (threads < D).
+// bf16 round-to-nearest-even of x, and of the remainder x - hi.
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ void split_hi_lo(float x, uint32_t& hi, uint32_t& lo) {
+  hi = bf16_rne_bits(x);
+  const float r = x - __uint_as_float(hi << 16);
+  lo = bf16_rne_bits(r);
+}
+
+// Sum of the partial block's keys into s[0..D) (all lanes of one wave).
 template <int D>
-__device__ __forceinline__ void tail_sum(const RouteArgs& a, int seq, int start, int n_tail, float* stail) {
-  const int tid = threadIdx.x;
-  if (tid < D) {
-    float s = 0.f;
-    if (n_tail > 0) {
-      const uint16_t* kp = a.k + ((int64_t)seq * a.Lmax + start) * D + tid;
-      for (int i = 0; i < n_tail; ++i) s += __uint_as_float((uint32_t)kp[(int64_t)i * D] << 16);
+__device__ __forceinline__ void wave_tail_sum(const RouteArgs& a, int seq, int start, int n_tail, float* s) {
+  const int lane = threadIdx.x & 63;
+  constexpr int PER = D / 64 > 0 ? D / 64 : 1;
+  float acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  if (n_tail > 0 && lane * PER < D) {
+    const uint16_t* kp = a.k + ((int64_t)seq * a.Lmax + start) * D + lane * PER;
+    for (int r = 0; r < n_tail; ++r) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] += __uint_as_float((uint32_t)kp[(int64_t)r * D + i] << 16);
     }
-    stail[tid] = s;
+  }
+  if (lane * PER < D) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) s[lane * PER + i] = acc[i];
   }
 }
 
-// Rank heads by rho (ties: lower id) and write the routed set; runs in wave 0,
-// lane g < H holds head g's complete-block aggregate A and partial-block dot x.
+// Rank heads by rho (ties: lower id) and write the routed set. Runs in one
+// wave; lane g < H holds head g's complete-block aggregate A and partial-block dot x.
 __device__ __forceinline__ void route_select(const RouteArgs& a, int64_t t, int lane, float A, float x,
                                              int n_tail) {
   const bool active = lane < a.H;
@@ -82,155 +108,242 @@ __device__ __forceinline__ void route_select(const RouteArgs& a, int64_t t, int 
   if (active && a.router_key) a.router_key[t * a.H + lane] = r;
 }
 
-template <int D, int HP>
-__global__ __launch_bounds__(256) void route_partial_kernel(RouteArgs a) {
-  constexpr int BPW = 64 / HP;     // blocks per wave step
-  constexpr bool PACK = D > 128;   // keep q as packed bf16 pairs when fp32 would not fit
+// Tail dot x_g = q_g . S_tail for lane g < H (q read from global, S_tail in LDS).
+template <int D>
+__device__ __forceinline__ float tail_dot(const RouteArgs& a, int64_t t, int lane, const float* s) {
+  float x = 0.f;
+  if (lane < a.H) {
+    const u32x4* qrow = reinterpret_cast<const u32x4*>(a.q + (t * a.H + lane) * D);
+#pragma unroll 4
+    for (int i = 0; i < D / 8; ++i) {
+      const u32x4 v = qrow[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x = fmaf(bf16_lo(v[e]), s[8 * i + 2 * e], x);
+        x = fmaf(bf16_hi(v[e]), s[8 * i + 2 * e + 1], x);
+      }
+    }
+  }
+  return x;
+}
+
+// Per-head sums over block tiles [jb, je) (tiles of 16 blocks, stepping `stride`
+// tiles) of max(q_g . Kbar_j, 0), for the RTQ row tiles of query t.
+// On return, lanes with (lane & 15) == 0 of group g hold rows 4g..4g+3 of each tile.
+template <int D, int RTQ>
+__device__ __forceinline__ void block_affinity(const RouteArgs& a, int64_t t, int seq, int jb, int je, int stride,
+                                               float (&rs)[RTQ][4]) {
+  constexpr int KS = D / 32;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  u32x4 afrag[RTQ][KS];
+#pragma unroll
+  for (int r = 0; r < RTQ; ++r) {
+    const int head = 16 * r + col;
+    const bool hv = seq >= 0 && head < a.H;
+    const uint16_t* qp = a.q + (t * a.H + (hv ? head : 0)) * D + grp * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (hv) v = *reinterpret_cast<const u32x4*>(qp + ks * 32);
+      afrag[r][ks] = v;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rs[r][j] = 0.f;
+  }
+  const int64_t nblk = a.Lmax / a.B;
+  for (int j0 = jb; j0 < je; j0 += 16 * stride) {
+    const int j = j0 + col;
+    const bool bv = j < je;
+    const float* kb = a.kbar + ((int64_t)(seq < 0 ? 0 : seq) * nblk + (bv ? j : 0)) * D + grp * 8;
+    u32x4 bhi[KS], blo[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      floatx4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
+      if (bv) {
+        v0 = *reinterpret_cast<const floatx4*>(kb + ks * 32);
+        v1 = *reinterpret_cast<const floatx4*>(kb + ks * 32 + 4);
+      }
+      uint32_t h[8], l[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        split_hi_lo(v0[e], h[e], l[e]);
+        split_hi_lo(v1[e], h[4 + e], l[4 + e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bhi[ks][e] = h[2 * e] | (h[2 * e + 1] << 16);
+        blo[ks][e] = l[2 * e] | (l[2 * e + 1] << 16);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RTQ; ++r) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        acc = mfma_16x16x32(afrag[r][ks], bhi[ks], acc);
+        acc = mfma_16x16x32(afrag[r][ks], blo[ks], acc);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) rs[r][jj] += fmaxf(acc[jj], 0.f);
+    }
+  }
+  // sum over the 16 block columns (fixed xor tree)
+#pragma unroll
+  for (int r = 0; r < RTQ; ++r)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      float v = rs[r][jj];
+      v += __shfl_xor(v, 1, kWave);
+      v += __shfl_xor(v, 2, kWave);
+      v += __shfl_xor(v, 4, kWave);
+      v += __shfl_xor(v, 8, kWave);
+      rs[r][jj] = v;
+    }
+}
+
+// decode: grid (nchunk, T); the four waves split the chunk's blocks.
+template <int D, int RTQ>
+__global__ __launch_bounds__(256) void route_decode_kernel(RouteArgs a) {
   __shared__ float red[4][64];
   __shared__ float stail[D];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane % HP, bs = lane / HP;
   const int64_t t = blockIdx.y;
   const int c = blockIdx.x;
   int seq, p;
   query_prefix(a, t, seq, p);
   const int nfull = p / a.B;
-  const int64_t nblk = a.Lmax / a.B;
-
-  constexpr int NQ = PACK ? D / 2 : D;
-  float qf[PACK ? 1 : D];
-  uint32_t qp[PACK ? D / 2 : 1];
-  {
-    const bool hv = g < a.H && seq >= 0;
-    const u32x4* src = reinterpret_cast<const u32x4*>(a.q + (t * a.H + (hv ? g : 0)) * D);
+  const int jb = c * a.chunk_blocks + wave * 16;
+  const int je = min((c + 1) * a.chunk_blocks, nfull);
+  float rs[RTQ][4];
+  block_affinity<D, RTQ>(a, t, seq, jb, je, 4, rs);
+  if ((lane & 15) == 0) {
 #pragma unroll
-    for (int i = 0; i < D / 8; ++i) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (hv) v = src[i];
+    for (int r = 0; r < RTQ; ++r)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (PACK) {
-          qp[4 * i + e] = v[e];
-        } else {
-          qf[8 * i + 2 * e] = bf16_lo(v[e]);
-          qf[8 * i + 2 * e + 1] = bf16_hi(v[e]);
-        }
-      }
-    }
+      for (int jj = 0; jj < 4; ++jj) red[wave][16 * r + 4 * (lane >> 4) + jj] = rs[r][jj];
   }
-  (void)NQ;
-  auto qv = [&](int i) -> float {
-    if constexpr (PACK) return (i & 1) ? bf16_hi(qp[i >> 1]) : bf16_lo(qp[i >> 1]);
-    else return qf[i];
-  };
-
-  float acc = 0.f;
-  const int j0 = c * a.chunk_blocks, j1 = min(j0 + a.chunk_blocks, nfull);
-  for (int j = j0 + wave * BPW + bs; j < j1; j += 4 * BPW) {
-    const floatx4* kb = reinterpret_cast<const floatx4*>(a.kbar + ((int64_t)seq * nblk + j) * D);
-    float dot = 0.f;
-#pragma unroll
-    for (int i = 0; i < D / 4; ++i) {
-      const floatx4 v = kb[i];
-      dot = fmaf(qv(4 * i), v[0], dot);
-      dot = fmaf(qv(4 * i + 1), v[1], dot);
-      dot = fmaf(qv(4 * i + 2), v[2], dot);
-      dot = fmaf(qv(4 * i + 3), v[3], dot);
-    }
-    acc += fmaxf(dot, 0.f);
-  }
-#pragma unroll
-  for (int off = HP; off < 64; off <<= 1) acc += __shfl_xor(acc, off, kWave);
-  red[wave][lane] = acc;
   __syncthreads();
+  const int tid = threadIdx.x;
+  const float A = tid < 64 ? ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid] : 0.f;
   if (a.nchunk > 1) {
-    if (threadIdx.x < a.H) {
-      const int tid = threadIdx.x;
-      a.partial[(t * a.nchunk + c) * a.H + tid] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
-    }
+    if (tid < a.H) a.partial[(t * a.nchunk + c) * a.H + tid] = A;
     return;
   }
-  // single chunk: finalise here (q_g is still in wave 0's registers, lane g < H)
+  if (wave != 0) return;
   const int n_tail = p - nfull * a.B;
-  tail_sum<D>(a, seq, nfull * a.B, n_tail, stail);
-  __syncthreads();
-  if (wave == 0) {
-    const float A = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
-    float x = 0.f;
-    if (n_tail > 0) {
-#pragma unroll
-      for (int i = 0; i < D; ++i) x = fmaf(qv(i), stail[i], x);
-    }
-    route_select(a, t, lane, A, x, n_tail);
-  }
+  wave_tail_sum<D>(a, seq, nfull * a.B, n_tail, stail);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const float x = n_tail > 0 ? tail_dot<D>(a, t, lane, stail) : 0.f;
+  route_select(a, t, lane, A, x, n_tail);
 }
 
+// decode, several chunks: sum the partials in chunk order, add the tail, select.
 template <int D>
-__global__ __launch_bounds__(256) void route_final_kernel(RouteArgs a) {
+__global__ __launch_bounds__(64) void route_final_kernel(RouteArgs a) {
   __shared__ float stail[D];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x;
   const int64_t t = blockIdx.x;
   int seq, p;
   query_prefix(a, t, seq, p);
   const int nfull = p / a.B;
   const int n_tail = p - nfull * a.B;
-  tail_sum<D>(a, seq, nfull * a.B, n_tail, stail);
-  __syncthreads();
-  if (wave != 0) return;
-  float A = 0.f, x = 0.f;
+  float A = 0.f;
   if (lane < a.H) {
     const float* pp = a.partial + t * a.nchunk * a.H + lane;
-    for (int c = 0; c < a.nchunk; ++c) A += pp[(int64_t)c * a.H];
-    if (n_tail > 0 && seq >= 0) {
-      const uint32_t* qrow = reinterpret_cast<const uint32_t*>(a.q + (t * a.H + lane) * D);
-      for (int i = 0; i < D / 2; ++i) {
-        const uint32_t v = qrow[i];
-        x = fmaf(bf16_lo(v), stail[2 * i], x);
-        x = fmaf(bf16_hi(v), stail[2 * i + 1], x);
-      }
+    int c = 0;
+    for (; c + 4 <= a.nchunk; c += 4) {
+      const float v0 = pp[(int64_t)c * a.H], v1 = pp[(int64_t)(c + 1) * a.H];
+      const float v2 = pp[(int64_t)(c + 2) * a.H], v3 = pp[(int64_t)(c + 3) * a.H];
+      A = (((A + v0) + v1) + v2) + v3;
     }
+    for (; c < a.nchunk; ++c) A += pp[(int64_t)c * a.H];
   }
+  wave_tail_sum<D>(a, seq, nfull * a.B, n_tail, stail);
+  __syncthreads();
+  const float x = n_tail > 0 ? tail_dot<D>(a, t, lane, stail) : 0.f;
   route_select(a, t, lane, A, x, n_tail);
 }
 
-template <int D>
-hipError_t launch_route_d(const RouteArgs& a, hipStream_t st) {
-  dim3 grid(a.nchunk, (unsigned)a.T);
-  const int hp = a.H <= 8 ? 8 : (a.H <= 16 ? 16 : (a.H <= 32 ? 32 : 64));
-  switch (hp) {
-    case 8: hipLaunchKernelGGL((route_partial_kernel<D, 8>), grid, dim3(256), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((route_partial_kernel<D, 16>), grid, dim3(256), 0, st, a); break;
-    case 32: hipLaunchKernelGGL((route_partial_kernel<D, 32>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((route_partial_kernel<D, 64>), grid, dim3(256), 0, st, a); break;
+// prefill: grid (ceil(T / 4)); wave w routes query 4 * blockIdx.x + w over all its complete blocks.
+template <int D, int RTQ>
+__global__ __launch_bounds__(256) void route_prefill_kernel(RouteArgs a) {
+  __shared__ float red[4][64];
+  __shared__ float stail[4][D];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t >= a.T) return;
+  int seq, p;
+  query_prefix(a, t, seq, p);
+  const int nfull = p / a.B;
+  float rs[RTQ][4];
+  block_affinity<D, RTQ>(a, t, seq, 0, nfull, 1, rs);
+  if ((lane & 15) == 0) {
+#pragma unroll
+    for (int r = 0; r < RTQ; ++r)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) red[wave][16 * r + 4 * (lane >> 4) + jj] = rs[r][jj];
   }
+  const int n_tail = p - nfull * a.B;
+  wave_tail_sum<D>(a, seq, nfull * a.B, n_tail, stail[wave]);
+  // the wave's own LDS rows: a wave-level barrier orders the writes above with the reads below
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const float A = red[wave][lane];
+  const float x = n_tail > 0 ? tail_dot<D>(a, t, lane, stail[wave]) : 0.f;
+  route_select(a, t, lane, A, x, n_tail);
+}
+
+template <int D, int RTQ>
+hipError_t launch_rtq(const RouteArgs& a, bool prefill, hipStream_t st) {
+  if (prefill) {
+    hipLaunchKernelGGL((route_prefill_kernel<D, RTQ>), dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((route_decode_kernel<D, RTQ>), dim3(a.nchunk, (unsigned)a.T), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nchunk == 1) return e;
-  hipLaunchKernelGGL((route_final_kernel<D>), dim3((unsigned)a.T), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((route_final_kernel<D>), dim3((unsigned)a.T), dim3(64), 0, st, a);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_route_d(const RouteArgs& a, bool prefill, hipStream_t st) {
+  switch ((a.H + 15) / 16) {
+    case 1: return launch_rtq<D, 1>(a, prefill, st);
+    case 2: return launch_rtq<D, 2>(a, prefill, st);
+    case 3: return launch_rtq<D, 3>(a, prefill, st);
+    default: return launch_rtq<D, 4>(a, prefill, st);
+  }
 }
 
 }  // namespace
 
-// Chunking of the pooled blocks: enough workgroups to cover the chip when
-// there are few queries, one chunk per query when there are many.
+bool route_is_prefill(int64_t T, int64_t nseq) { return T >= 64 && T >= 8 * nseq; }
+
+// Chunking of the pooled blocks in decode: 64 blocks per wave-set step; enough
+// chunks to give the chip about 256 workgroups. Prefill needs no partials.
 size_t route_partial_floats(int64_t T, int H, int64_t Lmax, int B, int* nchunk, int* chunk_blocks) {
-  const int64_t mmax = (Lmax + B - 1) / B;
-  int64_t cb = 16;
-  while (cb < mmax && cb * 2048 < mmax * T) cb *= 2;
-  if (cb > mmax) cb = mmax < 1 ? 1 : mmax;
-  const int64_t nc = (mmax + cb - 1) / cb;
-  *nchunk = (int)(nc < 1 ? 1 : nc);
+  const int64_t mmax = Lmax / B;
+  int64_t cb = 64;
+  while (cb < mmax && ((mmax + cb - 1) / cb) * T > 256) cb *= 2;
+  const int64_t nc = mmax < 1 ? 1 : (mmax + cb - 1) / cb;
+  *nchunk = (int)nc;
   *chunk_blocks = (int)cb;
-  return *nchunk > 1 ? (size_t)T * (size_t)(*nchunk) * (size_t)H : 0;
+  return nc > 1 ? (size_t)T * (size_t)nc * (size_t)H : 0;
 }
 
 hipError_t launch_route(const RouteArgs& a, int d, hipStream_t st) {
   if (a.T == 0) return hipSuccess;
+  const bool prefill = route_is_prefill(a.T, a.nseq);
   switch (d) {
-    case 32: return launch_route_d<32>(a, st);
-    case 64: return launch_route_d<64>(a, st);
-    case 128: return launch_route_d<128>(a, st);
-    case 256: return launch_route_d<256>(a, st);
+    case 32: return launch_route_d<32>(a, prefill, st);
+    case 64: return launch_route_d<64>(a, prefill, st);
+    case 128: return launch_route_d<128>(a, prefill, st);
+    case 256: return launch_route_d<256>(a, prefill, st);
   }
   return hipErrorInvalidValue;
 }

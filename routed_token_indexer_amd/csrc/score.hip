@@ -8,15 +8,19 @@
 // and the MISA† fine stage ("Hiërarchische Variant") applies it to a candidate
 // list instead of the whole prefix.
 //
-// Layout of the work: a workgroup owns a tile of QT queries (their gathered
-// head rows, NHP rows per query, held in registers as MFMA A-fragments) and a
-// chunk of keys. Its four waves walk the chunk in 16-key tiles: B-fragments are
-// loaded straight from HBM (each lane reads 64 contiguous bytes of one key),
-// one 16x16x32 MFMA per (row tile, 32-dim slice), then ReLU, the head weight and
-// the per-query head sum are applied in registers and one fp32 score per
-// (query, key) is stored. The key-dimension slots are permuted identically on
-// both operands (lane group g of the wave covers dims [g*D/4, (g+1)*D/4)), which
-// leaves every dot product unchanged and makes the key loads contiguous.
+// The query's gathered head rows are MFMA A-fragments held in registers; keys
+// stream from HBM as B-fragments, 16 keys per 16x16x32 MFMA column tile; ReLU,
+// the head weight and the head sum are applied to the accumulators in
+// registers and one fp32 score per (query, key) is stored. Lane i of a wave
+// supplies A row / B column (i % 16) and k-slots 8 * (i / 16) .. + 8 of each
+// 32-dim step, so one load instruction reads 64 contiguous bytes of each of 16
+// keys.
+//   decode kernel  one query per workgroup and a chunk of its keys (decode
+//                  batches and candidate lists); can also build the level-1
+//                  histogram of the split top-k for the scores it writes.
+//   wide kernel    a tile of consecutive queries of one sequence per workgroup
+//                  (causal prefill), so each key tile loaded serves the whole
+//                  query tile.
 #include "misa_common.hpp"
 #include "misa_internal.hpp"
 
@@ -33,12 +37,8 @@ __device__ __forceinline__ void query_info(const ScoreArgs& a, int64_t t, int& s
   const int sq = a.q_seq[t];
   if (sq < 0 || sq >= a.nseq) return;
   seq = sq;
-  if (a.row_len) {
-    n = a.row_len[t];
-  } else {
-    const int p = a.q_len[t];
-    n = p < 0 ? 0 : (p > a.Lmax ? (int)a.Lmax : p);
-  }
+  const int p = a.q_len[t];
+  n = p < 0 ? 0 : (p > a.Lmax ? (int)a.Lmax : p);
 }
 
 // Head id of row slot hs of query t (-1: padding row or invalid id).
@@ -52,7 +52,6 @@ template <int D, int NHP, int RT, int KT, bool GATHER>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   constexpr int QT = (16 * RT) / NHP;       // query slots of the tile
   constexpr int KS = D / 32;                // 32-wide k-steps
-  constexpr int DG = D / 4;                 // dims per lane group
   // per-lane output slots: how many different slots one lane writes
   constexpr int NOUT = NHP == 4 ? RT : (NHP == 8 ? RT : QT);
   static_assert(QT >= 1 && (16 * RT) % NHP == 0, "row tiling");
@@ -86,11 +85,11 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     int seq, n;
     query_info(a, t, seq, n);
     const int head = seq < 0 ? -1 : row_head(a, t, row % NHP);
-    const uint16_t* qp = a.q + ((t * a.H + (head < 0 ? 0 : head)) * D) + grp * DG;
+    const uint16_t* qp = a.q + ((t * a.H + (head < 0 ? 0 : head)) * D) + grp * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (head >= 0) v = *reinterpret_cast<const u32x4*>(qp + ks * 8);
+      if (head >= 0) v = *reinterpret_cast<const u32x4*>(qp + ks * 32);
       afrag[r][ks] = v;
     }
 #pragma unroll
@@ -127,7 +126,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     for (int s = 0; s < QT; ++s)
       if (s == lead || (!GATHER && slot_seq[s] == slot_seq[lead])) pass_n = max(pass_n, slot_n[s]);
     const int p_end = min(c_end, pass_n);
-    const uint16_t* kseq = a.k + (int64_t)slot_seq[lead] * a.Lmax * D + grp * DG;
+    const uint16_t* kseq = a.k + (int64_t)slot_seq[lead] * a.Lmax * D + grp * 8;
     const int32_t* crow = GATHER ? a.cand + (t0 + lead) * a.kc : nullptr;
     // which of this lane's output slots belong to this pass
     bool in_pass[NOUT];
@@ -147,7 +146,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           u32x4 v = {0u, 0u, 0u, 0u};
-          if (key >= 0) v = *reinterpret_cast<const u32x4*>(kp + ks * 8);
+          if (key >= 0) v = *reinterpret_cast<const u32x4*>(kp + ks * 32);
           bfrag[kt][ks] = v;
         }
       }
@@ -197,6 +196,169 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   }
 }
 
+// decode: grid (key chunks, T); one query per workgroup, its rows padded to RT tiles.
+// Keys do not depend on the routed heads, so the first key tile loads are issued
+// before the head ids and query rows are fetched, and every iteration prefetches
+// the next iteration's keys before computing the current one.
+template <int D, int KT, bool GATHER>
+__device__ __forceinline__ void load_key_tiles(const ScoreArgs& a, const uint16_t* kseq, const int32_t* crow, int p,
+                                               int base, int c_end, int col, u32x4 (&bf)[KT][D / 32],
+                                               bool (&valid)[KT]) {
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    const int s = base + kt * 16 + col;
+    int key = -1;
+    if (s < c_end) {
+      if constexpr (GATHER) {
+        const int id = crow[s];
+        key = (id >= 0 && id < p) ? id : -1;
+      } else {
+        key = s;
+      }
+    }
+    valid[kt] = key >= 0;
+    const uint16_t* kp = kseq + (int64_t)(key < 0 ? 0 : key) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (key >= 0) v = *reinterpret_cast<const u32x4*>(kp + ks * 32);
+      bf[kt][ks] = v;
+    }
+  }
+}
+
+template <int D, int RT, bool GATHER, bool HIST>
+__global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a) {
+  constexpr int KS = D / 32;
+  constexpr int KT = 4;   // 16-key tiles per wave iteration: 64 keys, one per lane at the end
+  __shared__ uint32_t lh[HIST ? 4096 : 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int64_t t = blockIdx.y;
+  int seq = a.q_seq[t];
+  int p = a.q_len[t];
+  if (seq < 0 || seq >= a.nseq) {
+    seq = -1;
+    p = 0;
+  }
+  p = p < 0 ? 0 : (p > a.Lmax ? (int)a.Lmax : p);
+  const int n = GATHER ? (seq < 0 ? 0 : a.kc) : p;
+  const int c_begin = blockIdx.x * a.chunk;
+  if (c_begin >= n) return;
+  const int c_end = min(c_begin + a.chunk, n);
+  if constexpr (HIST) {
+    for (int i = threadIdx.x; i < 4096; i += 256) lh[i] = 0;
+    __syncthreads();   // nothing is in flight yet
+  }
+  const uint16_t* kseq = a.k + (int64_t)seq * a.Lmax * D + grp * 8;
+  const int32_t* crow = GATHER ? a.cand + t * a.kc : nullptr;
+  float* orow = a.out + t * a.out_stride;
+
+  int base = c_begin + wave * 16 * KT;
+  u32x4 bcur[KT][KS];
+  bool vcur[KT];
+  load_key_tiles<D, KT, GATHER>(a, kseq, crow, p, base, c_end, col, bcur, vcur);
+
+  u32x4 afrag[RT][KS];
+  float wrow[RT][4];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const int head = row_head(a, t, 16 * r + col);
+    const uint16_t* qp = a.q + (t * a.H + (head < 0 ? 0 : head)) * D + grp * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (head >= 0) v = *reinterpret_cast<const u32x4*>(qp + ks * 32);
+      afrag[r][ks] = v;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int hd = row_head(a, t, 16 * r + 4 * grp + j);
+      wrow[r][j] = hd < 0 ? 0.f : a.w[t * a.H + hd];
+    }
+  }
+
+  for (; base < c_end; base += 4 * 16 * KT) {
+    u32x4 bnext[KT][KS];
+    bool vnext[KT];
+    load_key_tiles<D, KT, GATHER>(a, kseq, crow, p, base + 4 * 16 * KT, c_end, col, bnext, vnext);
+    float mine = 0.f;
+    bool mine_valid = false;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      float part = 0.f;
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = mfma_16x16x32(afrag[r][ks], bcur[kt][ks], acc);
+        part += wrow[r][0] * fmaxf(acc[0], 0.f) + wrow[r][1] * fmaxf(acc[1], 0.f) +
+                wrow[r][2] * fmaxf(acc[2], 0.f) + wrow[r][3] * fmaxf(acc[3], 0.f);
+      }
+      part += __shfl_xor(part, 16, kWave);
+      part += __shfl_xor(part, 32, kWave);
+      // every lane now holds the score of key (kt * 16 + col); lane group kt keeps it
+      if (grp == kt) {
+        mine = part;
+        mine_valid = vcur[kt];
+      }
+    }
+    const int s = base + lane;
+    if (s < c_end) {
+      const float v = mine_valid ? mine + 0.f : -INFINITY;
+      orow[s] = v;
+      if constexpr (HIST) atomicAdd(&lh[score_key(v) >> 20], 1u);
+    }
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      vcur[kt] = vnext[kt];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) bcur[kt][ks] = bnext[kt][ks];
+    }
+  }
+  if constexpr (HIST) {
+    __syncthreads();
+    uint32_t* gh = a.hist + t * 4096;
+    for (int i = threadIdx.x; i < 4096; i += 256)
+      if (lh[i]) atomicAdd(&gh[i], lh[i]);
+  }
+}
+
+template <int D, int RT, bool GATHER>
+hipError_t launch_decode(ScoreArgs a, int64_t max_len, hipStream_t st) {
+  if (a.chunk <= 0) {
+    // about 512 workgroups (two per CU), at least 256 keys each
+    int64_t c = 256;
+    while (c < 16384 && c * 512 < max_len * a.T) c *= 2;
+    a.chunk = (int)c;
+  }
+  dim3 grid((unsigned)((max_len + a.chunk - 1) / a.chunk), (unsigned)a.T);
+  if (a.hist)
+    hipLaunchKernelGGL((score_decode_kernel<D, RT, GATHER, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((score_decode_kernel<D, RT, GATHER, false>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_decode_d(const ScoreArgs& a, bool gather, int64_t max_len, hipStream_t st) {
+  const int rt = (a.hh + 15) / 16;
+  if (gather) {
+    switch (rt) {
+      case 1: return launch_decode<D, 1, true>(a, max_len, st);
+      case 2: return launch_decode<D, 2, true>(a, max_len, st);
+      case 3: return launch_decode<D, 3, true>(a, max_len, st);
+      default: return launch_decode<D, 4, true>(a, max_len, st);
+    }
+  }
+  switch (rt) {
+    case 1: return launch_decode<D, 1, false>(a, max_len, st);
+    case 2: return launch_decode<D, 2, false>(a, max_len, st);
+    case 3: return launch_decode<D, 3, false>(a, max_len, st);
+    default: return launch_decode<D, 4, false>(a, max_len, st);
+  }
+}
+
 template <int D, int NHP, int RT, int KT, bool GATHER>
 hipError_t launch_cfg(const ScoreArgs& a, int64_t ntile, int nchunk, hipStream_t st) {
   dim3 grid(nchunk, (unsigned)ntile);
@@ -224,29 +386,15 @@ hipError_t launch_d(ScoreArgs a, int nhp, bool wide, int64_t max_len, hipStream_
     const int nchunk = (int)((max_len + a.chunk - 1) / a.chunk);             \
     return launch_cfg<D, NHP_, RT_, KT_, GATHER>(a, ntile, nchunk, st);      \
   }
-  if constexpr (!GATHER) {
-    if (wide) {
-      switch (nhp) {
-        case 4: MISA_SCORE_CASE(4, 4, 2)
-        case 8: MISA_SCORE_CASE(8, 8, 2)
-        case 16: MISA_SCORE_CASE(16, 8, 2)
-        case 32: MISA_SCORE_CASE(32, 8, 2)
-        case 48: MISA_SCORE_CASE(48, 6, 2)
-        case 64: MISA_SCORE_CASE(64, 8, 2)
-        default: return hipErrorInvalidValue;
-      }
-    }
-  }
-  {
-    switch (nhp) {
-      case 4: MISA_SCORE_CASE(4, 1, 4)
-      case 8: MISA_SCORE_CASE(8, 1, 4)
-      case 16: MISA_SCORE_CASE(16, 1, 4)
-      case 32: MISA_SCORE_CASE(32, 2, 4)
-      case 48: MISA_SCORE_CASE(48, 3, 4)
-      case 64: MISA_SCORE_CASE(64, 4, 4)
-      default: return hipErrorInvalidValue;
-    }
+  (void)wide;
+  switch (nhp) {
+    case 4: MISA_SCORE_CASE(4, 4, 2)
+    case 8: MISA_SCORE_CASE(8, 8, 2)
+    case 16: MISA_SCORE_CASE(16, 8, 2)
+    case 32: MISA_SCORE_CASE(32, 8, 2)
+    case 48: MISA_SCORE_CASE(48, 6, 2)
+    case 64: MISA_SCORE_CASE(64, 8, 2)
+    default: return hipErrorInvalidValue;
   }
 #undef MISA_SCORE_CASE
 }
@@ -260,21 +408,22 @@ int score_rows_per_query(int hh) {
 }
 
 hipError_t launch_score(const ScoreArgs& a, int d, bool gather, bool wide, int64_t max_len, hipStream_t st) {
+  if (a.T == 0) return hipSuccess;
+  if (gather || !wide) {
+    switch (d) {
+      case 32: return launch_decode_d<32>(a, gather, max_len, st);
+      case 64: return launch_decode_d<64>(a, gather, max_len, st);
+      case 128: return launch_decode_d<128>(a, gather, max_len, st);
+      case 256: return launch_decode_d<256>(a, gather, max_len, st);
+    }
+    return hipErrorInvalidValue;
+  }
   const int nhp = score_rows_per_query(a.hh);
-  if (gather) {
-    switch (d) {
-      case 32: return launch_d<32, true>(a, nhp, wide, max_len, st);
-      case 64: return launch_d<64, true>(a, nhp, wide, max_len, st);
-      case 128: return launch_d<128, true>(a, nhp, wide, max_len, st);
-      case 256: return launch_d<256, true>(a, nhp, wide, max_len, st);
-    }
-  } else {
-    switch (d) {
-      case 32: return launch_d<32, false>(a, nhp, wide, max_len, st);
-      case 64: return launch_d<64, false>(a, nhp, wide, max_len, st);
-      case 128: return launch_d<128, false>(a, nhp, wide, max_len, st);
-      case 256: return launch_d<256, false>(a, nhp, wide, max_len, st);
-    }
+  switch (d) {
+    case 32: return launch_d<32, false>(a, nhp, true, max_len, st);
+    case 64: return launch_d<64, false>(a, nhp, true, max_len, st);
+    case 128: return launch_d<128, false>(a, nhp, true, max_len, st);
+    case 256: return launch_d<256, false>(a, nhp, true, max_len, st);
   }
   return hipErrorInvalidValue;
 }

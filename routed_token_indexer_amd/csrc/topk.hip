@@ -10,7 +10,9 @@
 // 32-bit key (12 + 12 + 8 bits, LDS histograms) finds the k-th key u* and how
 // many keys equal to u* are kept; then each wave compacts its contiguous
 // segment in index order with ballots, so the lowest indices among equal keys
-// win and the output comes out sorted.
+// win and the output comes out sorted. A row of at most kRowCap scores is
+// staged once into LDS as keys and every pass runs out of LDS; longer rows are
+// re-read from global memory in each pass.
 #include "misa_common.hpp"
 #include "misa_internal.hpp"
 
@@ -19,13 +21,32 @@ namespace {
 
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kRowCap = 12288;   // scores staged in LDS (48 KiB)
 
-__device__ __forceinline__ int64_t row_length(const TopkArgs& a, int64_t t) {
-  if (a.row_len) return a.row_len[t];
-  const int seq = a.q_seq[t];
-  if (seq < 0 || seq >= a.nseq) return 0;
-  const int p = a.q_len[t];
-  return p < 0 ? 0 : (p > a.Lmax ? a.Lmax : p);
+// Row geometry: n scores (the visible prefix, or kc candidate slots), and the
+// visible prefix p used to map candidate slots back to token ids.
+__device__ __forceinline__ void row_geometry(const TopkArgs& a, int64_t t, int64_t& n, int& p) {
+  p = query_prefix_len(a.q_seq, a.q_len, a.nseq, a.Lmax, t);
+  if (p < 0) {
+    p = 0;
+    n = 0;
+    return;
+  }
+  n = a.imap ? a.kc : p;
+}
+
+// Output token id of score slot e (-1 for a skipped candidate) and its score.
+__device__ __forceinline__ void out_entry(const TopkArgs& a, const int32_t* imap, int p, int64_t e, uint32_t u,
+                                          int32_t& id, float& sc) {
+  if (imap) {
+    const int32_t v = imap[e];
+    const bool ok = v >= 0 && v < p;
+    id = ok ? v : -1;
+    sc = ok ? key_score(u) : 0.f;
+  } else {
+    id = (int32_t)e;
+    sc = key_score(u);
+  }
 }
 
 // Exclusive prefix sum over the workgroup's threads (ascending thread id).
@@ -47,12 +68,15 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum) 
 
 __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(TopkArgs a) {
   __shared__ uint32_t hist[4096];
+  __shared__ uint32_t rowk[kRowCap];
   __shared__ uint32_t wsum[kTopkWaves];
   __shared__ uint32_t wgt[kTopkWaves], weq[kTopkWaves];
   __shared__ uint32_t sh_digit, sh_krem;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t = blockIdx.x;
-  const int64_t n = row_length(a, t);
+  int64_t n;
+  int p;
+  row_geometry(a, t, n, p);
   const int k = a.k;
   const float* row = a.scores + t * a.stride;
   int32_t* oi = a.idx + t * (int64_t)k;
@@ -62,8 +86,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(TopkArgs a) {
   if (n <= k) {
     for (int j = tid; j < k; j += kTopkThreads) {
       if (j < n) {
-        oi[j] = imap ? imap[j] : j;
-        if (os) os[j] = key_score(score_key(row[j]));
+        int32_t id;
+        float sc;
+        out_entry(a, imap, p, j, score_key(row[j]), id, sc);
+        oi[j] = id;
+        if (os) os[j] = sc;
       } else {
         oi[j] = -1;
         if (os) os[j] = 0.f;
@@ -71,6 +98,25 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(TopkArgs a) {
     }
     return;
   }
+
+  const bool inlds = n <= kRowCap;
+  if (inlds) {
+    for (int64_t e0 = 0; e0 < n; e0 += 4 * kTopkThreads) {
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t e = e0 + q * kTopkThreads + tid;
+        v[q] = e < n ? row[e] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t e = e0 + q * kTopkThreads + tid;
+        if (e < n) rowk[e] = score_key(v[q]);
+      }
+    }
+    __syncthreads();
+  }
+  auto key_at = [&](int64_t e) -> uint32_t { return inlds ? rowk[e] : score_key(row[e]); };
 
   // ---- radix select of the k-th largest key
   uint32_t prefix = 0, pmask = 0;
@@ -83,7 +129,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(TopkArgs a) {
     for (int i = tid; i < nb; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
     for (int64_t e = tid; e < n; e += kTopkThreads) {
-      const uint32_t u = score_key(row[e]);
+      const uint32_t u = key_at(e);
       if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
     }
     __syncthreads();
@@ -119,7 +165,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(TopkArgs a) {
   const int64_t s0 = wave * seg, s1 = min(s0 + seg, n);
   uint32_t cgt = 0, ceq = 0;
   for (int64_t e = s0 + lane; e < s1; e += 64) {
-    const uint32_t u = score_key(row[e]);
+    const uint32_t u = key_at(e);
     cgt += u > ustar ? 1u : 0u;
     ceq += u == ustar ? 1u : 0u;
   }
@@ -140,8 +186,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(TopkArgs a) {
   for (int64_t e0 = s0; e0 < s1; e0 += 64) {
     const int64_t e = e0 + lane;
     const bool in = e < s1;
-    const float sv = in ? row[e] : 0.f;
-    const uint32_t u = score_key(sv);
+    const uint32_t u = in ? key_at(e) : 0u;
     const bool gt = in && u > ustar;
     const bool eq = in && u == ustar;
     const uint64_t meq = __ballot(eq);
@@ -150,56 +195,33 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(TopkArgs a) {
     const uint64_t msel = __ballot(sel);
     const uint32_t pos = sel_run + (uint32_t)__popcll(msel & lt);
     if (sel && pos < (uint32_t)k) {
-      oi[pos] = imap ? imap[e] : (int32_t)e;
-      if (os) os[pos] = key_score(u);
+      int32_t id;
+      float sc;
+      out_entry(a, imap, p, e, u, id, sc);
+      oi[pos] = id;
+      if (os) os[pos] = sc;
     }
     eq_run += (uint32_t)__popcll(meq);
     sel_run += (uint32_t)__popcll(msel);
   }
 }
 
-__global__ __launch_bounds__(64) void cand_count_kernel(const int32_t* __restrict__ cand, int kc,
-                                                        const int32_t* __restrict__ q_seq,
-                                                        const int32_t* __restrict__ q_len, int64_t T,
-                                                        int64_t nseq, int64_t Lmax, int32_t* __restrict__ row_len) {
-  const int64_t t = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int seq = q_seq[t];
-  int p = q_len[t];
-  if (seq < 0 || seq >= nseq) p = 0;
-  p = p < 0 ? 0 : (p > Lmax ? (int)Lmax : p);
-  const int32_t* c = cand + t * (int64_t)kc;
-  int n = kc;
-  for (int j0 = 0; j0 < kc; j0 += 64) {
-    const int j = j0 + lane;
-    bool ok = true;
-    if (j < kc) {
-      const int v = c[j];
-      const int prev = j > 0 ? c[j - 1] : -1;
-      ok = v >= 0 && v < p && v > prev;
-    }
-    const uint64_t bad = __ballot(!ok);
-    if (bad) {
-      n = j0 + __ffsll((unsigned long long)bad) - 1;
-      break;
-    }
-  }
-  if (lane == 0) row_len[t] = n;
+}  // namespace
+
+__global__ __launch_bounds__(256) void zero_kernel(uint32_t* __restrict__ p, int64_t words) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (int64_t)gridDim.x * 256) p[i] = 0u;
 }
 
-}  // namespace
+hipError_t launch_zero(uint32_t* p, int64_t words, hipStream_t st) {
+  if (words <= 0) return hipSuccess;
+  const int64_t g = (words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)g), dim3(256), 0, st, p, words);
+  return hipGetLastError();
+}
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   if (a.T == 0) return hipSuccess;
   hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)a.T), dim3(kTopkThreads), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_cand_count(const int32_t* cand, int kc, const int32_t* q_seq, const int32_t* q_len,
-                             int64_t T, int64_t nseq, int64_t Lmax, int32_t* row_len, hipStream_t st) {
-  if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(cand_count_kernel, dim3((unsigned)T), dim3(64), 0, st, cand, kc, q_seq, q_len, T, nseq,
-                     Lmax, row_len);
   return hipGetLastError();
 }
 

@@ -1,0 +1,118 @@
+"""GPU parity at the full workload sizes, in the library's default launch
+configuration (the one bench.py times): DeepSeek-V3.2-like decode (4 x 32768,
+H=64), GLM-5-like decode (16 x 65536, H=32), hierarchical MISA at 128K (4 x
+131072, k'=8192 -> k=2048, plus dense DSA on the same inputs) on every query,
+and causal prefill at 16384 on a sample of rows the oracle computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import misa_oracle as O
+from routed_token_indexer_amd import _lib as M
+from routed_token_indexer_amd.workloads import make_inputs
+
+from parity import OverlapTally, check_router, oracle_rows, selected_scores_ok, upload
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+_cache = {}
+
+
+def get(name, mode):
+    if (name, mode) not in _cache:
+        _cache.clear()
+        torch.cuda.empty_cache()
+        x = make_inputs(name, mode=mode)
+        print(f"[full] {name} {mode}: T={x.cfg.T} L={x.cfg.L} H={x.cfg.H}", flush=True)
+        _cache[(name, mode)] = (x, upload(x))
+    return _cache[(name, mode)]
+
+
+def gpu_route(dev, c):
+    kbar = M.pool_keys(dev["k"], c.B)
+    return M.route(dev["q"], dev["w"], dev["k"], kbar, dev["q_seq"], dev["q_len"], c.B, c.h)
+
+
+@pytest.mark.parametrize("mode", ["gauss", "grid"])
+@pytest.mark.parametrize("name", ["c1", "c3", "c4"])
+def test_full_decode_misa(name, mode):
+    x, dev = get(name, mode)
+    c = x.cfg
+    exact = mode == "grid"
+    heads = gpu_route(dev, c)
+    idx, sc = M.score_topk(dev["q"], dev["w"], dev["k"], heads, dev["q_seq"], dev["q_len"], c.topk)
+    qs = list(range(c.T))
+    use = check_router(x, heads.cpu().numpy(), qs, c.h, exact)
+    oi, _ = O.score_topk(x.q, x.w, x.k, use, x.q_seq, x.q_len, c.topk)
+    rows = oracle_rows(x, use, qs)
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    tally = OverlapTally()
+    for t in qs:
+        tally.add(idx[t], oi[t], rows[t], c.topk, exact, label=f"{name}/{mode} t={t}")
+        selected_scores_ok(idx[t], sc[t], rows[t], c.topk, exact, label=f"{name}/{mode} t={t}")
+    print(f"[full] {name} {mode}: MISA overlap {tally.check():.5f}")
+
+
+@pytest.mark.parametrize("mode", ["gauss", "grid"])
+def test_full_c4_hier_and_dense(mode):
+    x, dev = get("c4", mode)
+    c = x.cfg
+    exact = mode == "grid"
+    heads = gpu_route(dev, c)
+    qs = list(range(c.T))
+    use = check_router(x, heads.cpu().numpy(), qs, c.h, exact)
+    hd = torch.from_numpy(use).cuda()
+    cand, _ = M.score_topk(dev["q"], dev["w"], dev["k"], hd, dev["q_seq"], dev["q_len"], c.kc)
+    idx, sc = M.hier_rerank(dev["q"], dev["w"], dev["k"], cand, dev["q_seq"], dev["q_len"], c.topk)
+    di, ds = M.dsa_index_dense(dev["q"], dev["w"], dev["k"], dev["q_seq"], dev["q_len"], c.topk)
+    cand, idx, sc, di, ds = (t.cpu().numpy() for t in (cand, idx, sc, di, ds))
+    # coarse pass against the oracle's routed top-k'
+    oc, _ = O.score_topk(x.q, x.w, x.k, use, x.q_seq, x.q_len, c.kc)
+    rows = oracle_rows(x, use, qs)
+    tally = OverlapTally()
+    for t in qs:
+        tally.add(cand[t], oc[t], rows[t], c.kc, exact, label=f"c4/{mode} coarse t={t}")
+    tally.check()
+    # fine pass: the oracle re-ranks the GPU's candidate set
+    ri, _ = O.hier_rerank(x.q, x.w, x.k, cand, x.q_seq, x.q_len, c.topk)
+    od, _ = O.dsa_index_dense(x.q, x.w, x.k, x.q_seq, x.q_len, c.topk)
+    dense_rows = [O.routed_scores(x.q[t], x.w[t], x.k[x.q_seq[t]], range(c.H), int(x.q_len[t])) for t in qs]
+    t_fine, t_dense = OverlapTally(), OverlapTally()
+    for t in qs:
+        t_fine.add(idx[t], ri[t], dense_rows[t], c.topk, exact, label=f"c4/{mode} fine t={t}")
+        selected_scores_ok(idx[t], sc[t], dense_rows[t], c.topk, exact, label=f"c4/{mode} fine t={t}")
+        t_dense.add(di[t], od[t], dense_rows[t], c.topk, exact, label=f"c4/{mode} dense t={t}")
+        selected_scores_ok(di[t], ds[t], dense_rows[t], c.topk, exact, label=f"c4/{mode} dense t={t}")
+    t_fine.check()
+    t_dense.check()
+    rec = np.mean([len(np.intersect1d(idx[t], di[t])) / c.topk for t in qs])
+    print(f"[full] c4 {mode}: MISA† recall vs dense {rec:.4f}")
+
+
+@pytest.mark.parametrize("mode", ["gauss", "grid"])
+def test_full_c2_prefill_sampled(mode):
+    x, dev = get("c2", mode)
+    c = x.cfg
+    exact = mode == "grid"
+    heads = gpu_route(dev, c)
+    idx, sc = M.score_topk(dev["q"], dev["w"], dev["k"], heads, dev["q_seq"], dev["q_len"], c.topk)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    qs = sorted(set(rng.choice(c.T, size=14, replace=False).tolist()) |
+                {0, 63, 64, 2046, 2047, 2048, 8191, 16383})
+    use = check_router(x, heads.cpu().numpy()[qs], qs, c.h, exact)
+    oi, _ = O.score_topk(x.q, x.w, x.k, use, x.q_seq, x.q_len, c.topk, queries=qs)
+    rows = oracle_rows(x, use, qs)
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    tally = OverlapTally()
+    for i, t in enumerate(qs):
+        tally.add(idx[t], oi[i], rows[i], c.topk, exact, label=f"c2/{mode} t={t}")
+        selected_scores_ok(idx[t], sc[t], rows[i], c.topk, exact, label=f"c2/{mode} t={t}")
+    tally.check()
+    # every row's output is a valid ascending set of the right size
+    q_len = x.q_len
+    n = np.minimum(q_len, c.topk)
+    assert np.all((idx >= 0).sum(axis=1) == n)
+    inner = np.where(idx[:, 1:] >= 0, np.diff(idx, axis=1) > 0, True)
+    assert np.all(inner)
+    assert np.all(idx.max(axis=1) < q_len)

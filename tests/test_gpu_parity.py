@@ -21,6 +21,9 @@ CASES = {
     "c3r": ("c3", dict(L=2500, T=16, nseq=16, topk=300)),
     "c4r": ("c4", dict(L=5000, T=4, nseq=4, kc=1024, topk=256)),
     "c2r": ("c2", dict(L=700, T=700, topk=128)),
+    # rows above 12288 scores: the multi-workgroup (split) top-k
+    "c1s": ("c1", dict(L=20001, T=4, nseq=4, topk=1000)),
+    "c4s": ("c4", dict(L=40000, T=4, nseq=4, kc=4096, topk=512)),
 }
 MODES = ["gauss", "grid"]
 
@@ -142,7 +145,7 @@ def test_dense(case, mode):
 
 
 @pytest.mark.parametrize("mode", MODES)
-@pytest.mark.parametrize("case", ["c0", "c1r", "c4r"])
+@pytest.mark.parametrize("case", ["c0", "c1r", "c4r", "c4s"])
 def test_hier_rerank(case, mode):
     """MISA†: the GPU re-rank of a candidate set against the oracle's re-rank of the
     same set, and the GPU's whole coarse-to-fine pass against the oracle's."""
@@ -179,7 +182,7 @@ def test_hier_rerank(case, mode):
 
 # ------------------------------------------------------------------ invariants on the GPU
 @pytest.mark.parametrize("mode", MODES)
-@pytest.mark.parametrize("case", ["c0", "c1r", "c2r"])
+@pytest.mark.parametrize("case", ["c0", "c1r", "c2r", "c1s"])
 def test_routed_all_heads_is_dense_bitwise(case, mode):
     x, dev = get(case, mode)
     allh = torch.arange(x.cfg.H, dtype=torch.int32, device="cuda").repeat(x.cfg.T, 1).contiguous()
@@ -246,22 +249,41 @@ def test_short_prefix_takes_all():
         assert np.all(idx[t][p:] == -1) and np.all(sc[t][p:] == 0)
 
 
-@pytest.mark.parametrize("topk", [1, 2, 3000, 3001, 5000])
-def test_topk_extremes(topk):
-    x, dev = get("c1r", "grid")
+@pytest.mark.parametrize("case,topk", [("c1r", 1), ("c1r", 2), ("c1r", 3000), ("c1r", 3001), ("c1r", 5000),
+                                        ("c1s", 1), ("c1s", 7), ("c1s", 20000), ("c1s", 20001), ("c1s", 30000)])
+def test_topk_extremes(case, topk):
+    x, dev = get(case, "grid")
     ho, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h)
     _, _, idx, _ = run_misa(dev, x.cfg, heads=ho, topk=topk)
     oi, _ = O.score_topk(x.q, x.w, x.k, ho, x.q_seq, x.q_len, topk)
     np.testing.assert_array_equal(idx, oi)
 
 
-def test_all_equal_scores_tie_break():
+@pytest.mark.parametrize("case", ["c1r", "c1s"])
+def test_all_equal_scores_tie_break(case):
     """Every score equal (zero keys): the lowest token indices win."""
-    x, dev = get("c1r", "grid")
+    x, dev = get(case, "grid")
     k0 = torch.zeros_like(dev["k"])
     idx, sc = M.dsa_index_dense(dev["q"], dev["w"], k0, dev["q_seq"], dev["q_len"], 100)
     assert torch.equal(idx.cpu(), torch.arange(100, dtype=torch.int32).repeat(4, 1))
     assert torch.all(sc == 0)
+
+
+def test_rerank_skips_invalid_candidates():
+    """Candidate ids outside [0, q_len) are not candidates; fewer valid than k pads with -1."""
+    x, dev = get("c1r", "grid")
+    p = int(x.q_len[0])
+    c = np.full((4, 64), -1, np.int32)
+    c[:, :10] = np.arange(0, 100, 10)
+    c[1, 3] = p + 5            # beyond the prefix: skipped
+    cand = torch.from_numpy(c).cuda()
+    idx, sc = M.hier_rerank(dev["q"], dev["w"], dev["k"], cand, dev["q_seq"], dev["q_len"], 16)
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    assert idx[0, :10].tolist() == list(range(0, 100, 10)) and np.all(idx[0, 10:] == -1)
+    assert sorted(idx[1][idx[1] >= 0].tolist()) == [0, 10, 20, 40, 50, 60, 70, 80, 90]
+    assert np.all(sc[0, 10:] == 0)
+    ri, rv = O.hier_rerank(x.q, x.w, x.k, c[:1], x.q_seq, x.q_len, 16, queries=[0])
+    np.testing.assert_array_equal(sc[0], rv[0].astype(np.float32))
 
 
 def test_empty_batch_noop():
