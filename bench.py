@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--warm-cache", action="store_true", help="no key-cache rotation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="skip the per-row timings")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of HIP-graph replays of the step")
     return ap.parse_args()
 
 
@@ -104,18 +106,17 @@ def main():
     ws_dense = ws(M.OP_DSA_DENSE, topk=topk)
     kbar_pf = torch.empty_like(kbars[0])
 
+    ws_step = ws(M.OP_HIER_INDEXER if hier else M.OP_INDEXER, B=B, topk=topk, kc=kc)
+
     def step(i):
+        # one call of the whole indexer: route -> routed scoring -> top-k (-> dense re-rank)
         kk = ks[i % ncopy]
-        if prefill:
-            kb = M.pool_keys(kk, B, kbar=kbar_pf)
-        else:
-            kb = kbars[i % ncopy]
-        M.route(q, w, kk, kb, q_seq, q_len, B, h, heads=heads, ws=ws_route)
+        kb = M.pool_keys(kk, B, kbar=kbar_pf) if prefill else kbars[i % ncopy]
         if hier:
-            M.score_topk(q, w, kk, heads, q_seq, q_len, kc, idx=cand, want_score=False, ws=ws_score)
-            M.hier_rerank(q, w, kk, cand, q_seq, q_len, topk, idx=idx, score=sc, ws=ws_rerank)
+            M.hier_indexer(q, w, kk, kb, q_seq, q_len, B, h, kc, topk, heads=heads, cand=cand, idx=idx, score=sc,
+                           ws=ws_step)
         else:
-            M.score_topk(q, w, kk, heads, q_seq, q_len, topk, idx=idx, score=sc, ws=ws_score)
+            M.indexer(q, w, kk, kb, q_seq, q_len, B, h, topk, heads=heads, idx=idx, score=sc, ws=ws_step)
 
     def timed(fn, steps, warmup):
         for i in range(warmup):
@@ -129,21 +130,46 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
-    # ---- the timed region: K steps, with the scoring kernel bracketed by HIP events on its stream
+    # ---- eager timed region: K steps, the scoring kernel bracketed by HIP events on its stream
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     M.timing_begin(M.KERNEL_SCORE, capacity=4 * args.steps + 16)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
     e0.record()
     for i in range(args.steps):
         step(i)
     e1.record()
     torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_eager = e0.elapsed_time(e1) / args.steps
     score_ms, score_n = M.timing_end()
+
+    # ---- graph timed region: the step (one per key-cache copy) captured once, replayed
+    ms_graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            step(0)                      # warm the capture stream
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=cap):
+                for i in range(ncopy):
+                    step(i)
+        torch.cuda.synchronize()
+        reps = max(1, -(-args.steps // ncopy))
+        for _ in range(max(1, args.warmup // ncopy)):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(reps):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        ms_graph = g0.elapsed_time(g1) / (reps * ncopy)
+    ms_step = ms_graph if ms_graph is not None else ms_eager
+    t_wall = ms_step * args.steps * 1e-3
 
     tokens = int(x.q_len.astype(np.int64).sum())
     value = tokens / (ms_step * 1e-3) / 1e9
@@ -175,6 +201,9 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "ms_per_query": round(ms_step / T, 6),
+        "timing": ("HIP graph replay of the step (captured once per key-cache copy)" if ms_graph is not None
+                   else "eager launches"),
+        "ms_per_step_eager": round(ms_eager, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -184,8 +213,9 @@ def main():
             "workload": c.description, "name": c.name, "T": T, "L": L, "H": H, "d": d, "B": B, "h": h,
             "topk": topk, "kc": kc or None, "tokens_per_step": tokens,
             "cache": "warm" if args.warm_cache else f"cold (rotating {ncopy} key-cache copies)",
-            "step": ("pool+route+score_topk" if prefill else
-                     "route+score_topk(k')+hier_rerank(k)" if hier else "route+score_topk"),
+            "step": ("misa_pool_keys + misa_indexer (route, routed scoring, top-k)" if prefill else
+                     "misa_hier_indexer (route, routed scoring, top-k', dense re-rank, top-k)" if hier else
+                     "misa_indexer (route, routed scoring, top-k)"),
         },
         "roofline": roof,
         "wall_s_timed_region": round(t_wall, 4),

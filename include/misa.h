@@ -77,6 +77,8 @@ extern "C" {
 #define MISA_OP_SCORE_TOPK 2
 #define MISA_OP_HIER_RERANK 3
 #define MISA_OP_DSA_DENSE 4
+#define MISA_OP_INDEXER 5
+#define MISA_OP_HIER_INDEXER 6
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 MISA_API int32_t misa_version(void);
@@ -171,6 +173,37 @@ MISA_API int32_t misa_hier_rerank(const void* q, const float* w, const void* k, 
 MISA_API int32_t dsa_index_dense(const void* q, const float* w, const void* k, const int32_t* q_seq,
                         const int32_t* q_len, int64_t T, int32_t H, int32_t d, int64_t nseq, int64_t Lmax,
                         int32_t topk, int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The whole MISA indexer in one call: misa_route followed by misa_score_topk
+ * (MISA abstract; "Methodologie: MISA"), with bit-identical results. For decode
+ * shapes (fewer than 8 queries per sequence on average) it runs as one pipeline
+ * of four launches: router partials, head selection fused into the routed
+ * scoring, and a two-launch top-k; otherwise it makes the separate calls.
+ *   kbar     fp32 [nseq][Lmax/B][d] from misa_pool_keys (the pooled-key cache)
+ *   heads    int32 [T][h] out, may be NULL: the routed heads
+ *   idx / score as misa_score_topk
+ *   ws: misa_workspace_bytes(MISA_OP_INDEXER, T, H, Lmax, B, topk, 0)
+ */
+MISA_API int32_t misa_indexer(const void* q, const float* w, const void* k, const float* kbar, const int32_t* q_seq,
+                              const int32_t* q_len, int64_t T, int32_t H, int32_t d, int64_t nseq, int64_t Lmax,
+                              int32_t B, int32_t h, int32_t topk, int32_t* heads, int32_t* idx, float* score,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The whole MISA† indexer in one call: misa_route, misa_score_topk with
+ * topk = kc (the enlarged candidate set) and misa_hier_rerank to topk
+ * ("Hiërarchische Variant (MISA†)"), with bit-identical results. For decode
+ * shapes it runs as six launches, the candidates' dense re-scoring fused into
+ * the coarse pass's compaction.
+ *   heads  int32 [T][h] out, may be NULL;  cand  int32 [T][kc] out, may be NULL
+ *   ws: misa_workspace_bytes(MISA_OP_HIER_INDEXER, T, H, Lmax, B, topk, kc)
+ */
+MISA_API int32_t misa_hier_indexer(const void* q, const float* w, const void* k, const float* kbar,
+                                   const int32_t* q_seq, const int32_t* q_len, int64_t T, int32_t H, int32_t d,
+                                   int64_t nseq, int64_t Lmax, int32_t B, int32_t h, int32_t kc, int32_t topk,
+                                   int32_t* heads, int32_t* cand, int32_t* idx, float* score, void* ws,
+                                   size_t ws_bytes, void* stream);
 
 /*
  * Full score rows of the routed scoring step (a diagnostic of step 3 above):

@@ -7,7 +7,8 @@ first indexer call does, and raises if it has not been built.
 """
 __version__ = "0.1.0"
 
-_EXPORTS = ("pool_keys", "route", "score_topk", "hier_rerank", "dsa_index_dense", "debug_scores",
+_EXPORTS = ("pool_keys", "route", "score_topk", "hier_rerank", "dsa_index_dense", "indexer", "hier_indexer",
+            "debug_scores",
             "workspace_bytes", "timing_begin", "timing_end", "MisaError")
 
 

@@ -25,6 +25,8 @@ OP_ROUTE = 1
 OP_SCORE_TOPK = 2
 OP_HIER_RERANK = 3
 OP_DSA_DENSE = 4
+OP_INDEXER = 5
+OP_HIER_INDEXER = 6
 
 KERNEL_SCORE = 1
 KERNEL_TOPK = 2
@@ -52,6 +54,10 @@ _SIGNATURES = {
                                 _P]),
     "dsa_index_dense": (_I32, [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I64, _I64, _I32, _P, _P, _P, _SZ, _P]),
     "misa_debug_scores": (_I32, [_P, _P, _P, _P, _I32, _P, _P, _I64, _I32, _I32, _I64, _I64, _P, _P]),
+    "misa_indexer": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P,
+                            _SZ, _P]),
+    "misa_hier_indexer": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I64, _I64, _I32, _I32, _I32, _I32, _P, _P,
+                                 _P, _P, _P, _SZ, _P]),
     "misa_timing_begin": (_I32, [_I32, _I32]),
     "misa_timing_end": (_I32, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)]),
 }
@@ -189,6 +195,35 @@ def dsa_index_dense(q, w, k, q_seq, q_len, topk: int, idx=None, score=None, want
     _check("dsa_index_dense", lib().dsa_index_dense(_ptr(q), _ptr(w), _ptr(k), _ptr(q_seq), _ptr(q_len), T, H, d,
                                                     nseq, L, topk, _ptr(idx), _ptr(score), _ptr(ws), ws.numel(),
                                                     _stream(stream)))
+    return idx, score
+
+
+def indexer(q, w, k, kbar, q_seq, q_len, B: int, h: int, topk: int, heads=None, idx=None, score=None,
+            want_score=True, ws=None, stream=None):
+    """Whole MISA indexer (route + routed scoring + top-k) in one call."""
+    _req(q, torch.bfloat16, "q", 3)
+    T, H, d = q.shape
+    nseq, L, _ = k.shape
+    idx, score = _outs(T, topk, q.device, idx, score, want_score)
+    ws = _workspace(ws, workspace_bytes(OP_INDEXER, T, H, L, B, topk), q.device)
+    _check("misa_indexer", lib().misa_indexer(_ptr(q), _ptr(w), _ptr(k), _ptr(kbar), _ptr(q_seq), _ptr(q_len), T, H,
+                                              d, nseq, L, B, h, topk, _ptr(heads), _ptr(idx), _ptr(score), _ptr(ws),
+                                              ws.numel(), _stream(stream)))
+    return idx, score
+
+
+def hier_indexer(q, w, k, kbar, q_seq, q_len, B: int, h: int, kc: int, topk: int, heads=None, cand=None, idx=None,
+                 score=None, want_score=True, ws=None, stream=None):
+    """Whole MISA† indexer (route + routed top-k' + dense re-rank to top-k) in one call."""
+    _req(q, torch.bfloat16, "q", 3)
+    T, H, d = q.shape
+    nseq, L, _ = k.shape
+    idx, score = _outs(T, topk, q.device, idx, score, want_score)
+    ws = _workspace(ws, workspace_bytes(OP_HIER_INDEXER, T, H, L, B, topk, kc), q.device)
+    _check("misa_hier_indexer", lib().misa_hier_indexer(_ptr(q), _ptr(w), _ptr(k), _ptr(kbar), _ptr(q_seq),
+                                                        _ptr(q_len), T, H, d, nseq, L, B, h, kc, topk, _ptr(heads),
+                                                        _ptr(cand), _ptr(idx), _ptr(score), _ptr(ws), ws.numel(),
+                                                        _stream(stream)))
     return idx, score
 
 

@@ -7,7 +7,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/misa.h"
+#include "misa.h"
 #include "misa_internal.hpp"
 
 namespace {
@@ -71,6 +71,47 @@ size_t select_ws_bytes(int64_t T, int64_t max_len) {
   return b;
 }
 
+// Workspace of the fused decode pipeline (misa_indexer / misa_hier_indexer):
+// router partials and partial-block dots, the coarse score rows and their split
+// top-k state, and for MISA† the candidate list, its dense scores and their
+// split top-k state.
+struct FusedLayout {
+  size_t bytes = 0;
+  int nchunk_r = 1, chunk_blocks = 1;
+  float* partial = nullptr;
+  float* xtail = nullptr;
+  float* scores = nullptr;
+  misa::SplitTopkWs sw{};
+  int32_t* cand = nullptr;
+  float* rr_scores = nullptr;
+  misa::SplitTopkWs rw{};
+};
+
+FusedLayout fused_layout(int64_t T, int H, int64_t Lmax, int B, int64_t kc, void* base) {
+  FusedLayout f;
+  (void)misa::route_partial_floats(T, H, Lmax, B, &f.nchunk_r, &f.chunk_blocks);
+  char* p = static_cast<char*>(base);
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> char* {
+    char* r = p ? p + off : nullptr;
+    off += round_up(bytes);
+    return r;
+  };
+  f.partial = reinterpret_cast<float*>(take((size_t)T * f.nchunk_r * H * 4));
+  f.xtail = reinterpret_cast<float*>(take((size_t)T * H * 4));
+  f.scores = reinterpret_cast<float*>(take((size_t)T * Lmax * 4));
+  char* sw = take(misa::split_topk_ws_bytes(T, Lmax));
+  if (p) f.sw = misa::split_topk_carve(sw, T, Lmax);
+  if (kc > 0) {
+    f.cand = reinterpret_cast<int32_t*>(take((size_t)T * kc * 4));
+    f.rr_scores = reinterpret_cast<float*>(take((size_t)T * kc * 4));
+    char* rw = take(misa::split_topk_ws_bytes(T, kc));
+    if (p) f.rw = misa::split_topk_carve(rw, T, kc);
+  }
+  f.bytes = off;
+  return f;
+}
+
 // ---------------------------------------------------------------- timing
 struct Timing {
   std::mutex mu;
@@ -126,6 +167,17 @@ size_t misa_workspace_bytes(int32_t op, int64_t T, int32_t H, int64_t Lmax, int3
       return select_ws_bytes(T, Lmax);
     case MISA_OP_HIER_RERANK:
       return select_ws_bytes(T, kc > 0 ? kc : 0);
+    case MISA_OP_INDEXER:
+    case MISA_OP_HIER_INDEXER: {
+      if (B < 1 || H < 1) return 0;
+      const bool hier = op == MISA_OP_HIER_INDEXER;
+      const FusedLayout f = fused_layout(T, H, Lmax, B, hier ? kc : 0, nullptr);
+      size_t sep = misa_workspace_bytes(MISA_OP_ROUTE, T, H, Lmax, B, 0, 0) + round_up((size_t)T * H * 4);
+      size_t sc = misa_workspace_bytes(MISA_OP_SCORE_TOPK, T, H, Lmax, B, hier ? kc : topk, 0);
+      if (hier) sc += round_up((size_t)T * (size_t)kc * 4) + misa_workspace_bytes(MISA_OP_HIER_RERANK, T, H, Lmax, B, topk, kc);
+      sep += sc;
+      return f.bytes > sep ? f.bytes : sep;
+    }
   }
   return 0;
 }
@@ -311,6 +363,171 @@ int32_t misa_hier_rerank(const void* q, const float* w, const void* k, const int
   if (rc) return rc;
   return score_and_select(fn, q, w, k, nullptr, H, cand, kc, q_seq, q_len, T, H, d, nseq, Lmax, topk, idx, score,
                           static_cast<float*>(ws), kc, (hipStream_t)stream);
+}
+
+namespace {
+
+// The fused decode pipeline (decode shapes) or the separate calls (prefill shapes).
+int32_t run_indexer(const char* fn, bool hier, const void* q, const float* w, const void* k, const float* kbar,
+                    const int32_t* q_seq, const int32_t* q_len, int64_t T, int32_t H, int32_t d, int64_t nseq,
+                    int64_t Lmax, int32_t B, int32_t h, int32_t kc, int32_t topk, int32_t* heads, int32_t* cand,
+                    int32_t* idx, float* score, void* ws, size_t ws_bytes, hipStream_t st) {
+  int32_t rc = check_common(fn, q, w, k, q_seq, q_len, T, H, d, nseq, Lmax);
+  if (rc) return rc;
+  if (B < 1 || B > Lmax) return fail(MISA_ERR_ARG, "%s: B = %d not in [1, Lmax]", fn, B);
+  if (h < 1 || h > H) return fail(MISA_ERR_ARG, "%s: h = %d not in [1, H = %d]", fn, h, H);
+  if (topk < 1) return fail(MISA_ERR_ARG, "%s: topk = %d < 1", fn, topk);
+  if (hier && kc < topk) return fail(MISA_ERR_ARG, "%s: kc = %d < topk = %d", fn, kc, topk);
+  if (T == 0) return ok();
+  if (!kbar || !aligned(kbar, 16)) return fail(MISA_ERR_ARG, "%s: kbar must be a 16-byte aligned pointer", fn);
+  rc = check_outputs(fn, topk, idx, score);
+  if (rc) return rc;
+  if (!aligned(heads, 4) || !aligned(cand, 4)) return fail(MISA_ERR_ALIGN, "%s: heads/cand must be 4-byte aligned", fn);
+  const int32_t op = hier ? MISA_OP_HIER_INDEXER : MISA_OP_INDEXER;
+  rc = check_ws(fn, ws, ws_bytes, misa_workspace_bytes(op, T, H, Lmax, B, topk, hier ? kc : 0));
+  if (rc) return rc;
+
+  const bool fused = !wide_tiles(T, nseq) && misa::split_topk_always_ok(Lmax) &&
+                     (!hier || misa::split_topk_always_ok(kc));
+  if (!fused) {
+    char* p = static_cast<char*>(ws);
+    const size_t rws = misa_workspace_bytes(MISA_OP_ROUTE, T, H, Lmax, B, 0, 0);
+    int32_t* hd = heads ? heads : reinterpret_cast<int32_t*>(p + rws);
+    char* rest = p + rws + round_up((size_t)T * H * 4);
+    rc = misa_route(q, w, k, kbar, q_seq, q_len, T, H, d, nseq, Lmax, B, h, hd, nullptr, p, rws, st);
+    if (rc) return rc;
+    if (!hier)
+      return misa_score_topk(q, w, k, hd, h, q_seq, q_len, T, H, d, nseq, Lmax, topk, idx, score, rest,
+                             select_ws_bytes(T, Lmax), st);
+    int32_t* cd = cand ? cand : reinterpret_cast<int32_t*>(rest);
+    char* rest2 = rest + round_up((size_t)T * (size_t)kc * 4);
+    rc = misa_score_topk(q, w, k, hd, h, q_seq, q_len, T, H, d, nseq, Lmax, kc, cd, nullptr, rest2,
+                         select_ws_bytes(T, Lmax), st);
+    if (rc) return rc;
+    return misa_hier_rerank(q, w, k, cd, kc, q_seq, q_len, T, H, d, nseq, Lmax, topk, idx, score, rest2,
+                            select_ws_bytes(T, kc), st);
+  }
+
+  FusedLayout f = fused_layout(T, H, Lmax, B, hier ? kc : 0, ws);
+  // 1. router partials (+ partial-block dots), clearing the top-k state of the later launches
+  misa::RouteArgs ra{};
+  ra.q = static_cast<const uint16_t*>(q);
+  ra.w = w;
+  ra.k = static_cast<const uint16_t*>(k);
+  ra.kbar = kbar;
+  ra.q_seq = q_seq;
+  ra.q_len = q_len;
+  ra.T = T;
+  ra.H = H;
+  ra.nseq = nseq;
+  ra.Lmax = Lmax;
+  ra.B = B;
+  ra.h = h;
+  ra.partial = f.partial;
+  ra.nchunk = f.nchunk_r;
+  ra.chunk_blocks = f.chunk_blocks;
+  ra.fused = true;
+  ra.xtail = f.xtail;
+  ra.zero[0] = f.sw.hist;
+  ra.zero_words[0] = misa::split_topk_zero_words(T);
+  ra.zero[1] = hier ? f.rw.hist : nullptr;
+  ra.zero_words[1] = hier ? misa::split_topk_zero_words(T) : 0;
+  misa::timing_before(misa::KID_ROUTE, st);
+  hipError_t e = misa::launch_route(ra, d, st);
+  misa::timing_after(misa::KID_ROUTE, st);
+  if (e != hipSuccess) return hip_status(e, fn);
+  // 2. head selection + routed scoring + level-1 histogram
+  misa::ScoreArgs sa{};
+  sa.q = ra.q;
+  sa.w = w;
+  sa.k = ra.k;
+  sa.heads = nullptr;
+  sa.hh = h;
+  sa.q_seq = q_seq;
+  sa.q_len = q_len;
+  sa.T = T;
+  sa.H = H;
+  sa.nseq = nseq;
+  sa.Lmax = Lmax;
+  sa.out = f.scores;
+  sa.out_stride = Lmax;
+  sa.hist = f.sw.hist;
+  sa.partial = f.partial;
+  sa.xtail = f.xtail;
+  sa.nchunk_r = f.nchunk_r;
+  sa.B = B;
+  sa.heads_out = heads;
+  misa::timing_before(misa::KID_SCORE, st);
+  e = misa::launch_score(sa, d, false, false, Lmax, st);
+  misa::timing_after(misa::KID_SCORE, st);
+  if (e != hipSuccess) return hip_status(e, fn);
+  // 3. top-k of the routed scores
+  misa::TopkArgs b{};
+  b.scores = f.scores;
+  b.stride = Lmax;
+  b.q_seq = q_seq;
+  b.q_len = q_len;
+  b.nseq = nseq;
+  b.Lmax = Lmax;
+  b.T = T;
+  misa::timing_before(misa::KID_TOPK, st);
+  if (!hier) {
+    b.k = topk;
+    b.idx = idx;
+    b.score = score;
+    e = misa::launch_topk_split(b, f.sw, true, st);
+  } else {
+    int32_t* cd = cand ? cand : f.cand;
+    b.k = kc;
+    b.idx = cd;
+    b.score = nullptr;
+    misa::RescoreArgs r{};
+    r.q = ra.q;
+    r.w = w;
+    r.k = ra.k;
+    r.H = H;
+    r.d = d;
+    r.scores = f.rr_scores;
+    r.hist = f.rw.hist;
+    e = misa::launch_topk_split_rescore(b, f.sw, r, st);
+    if (e == hipSuccess) {
+      // 4. MISA† fine stage: top-k of the candidates' dense scores
+      misa::TopkArgs b2{};
+      b2.scores = f.rr_scores;
+      b2.stride = kc;
+      b2.q_seq = q_seq;
+      b2.q_len = q_len;
+      b2.nseq = nseq;
+      b2.Lmax = Lmax;
+      b2.imap = cd;
+      b2.kc = kc;
+      b2.T = T;
+      b2.k = topk;
+      b2.idx = idx;
+      b2.score = score;
+      e = misa::launch_topk_split(b2, f.rw, true, st);
+    }
+  }
+  misa::timing_after(misa::KID_TOPK, st);
+  return hip_status(e, fn);
+}
+
+}  // namespace
+
+int32_t misa_indexer(const void* q, const float* w, const void* k, const float* kbar, const int32_t* q_seq,
+                     const int32_t* q_len, int64_t T, int32_t H, int32_t d, int64_t nseq, int64_t Lmax, int32_t B,
+                     int32_t h, int32_t topk, int32_t* heads, int32_t* idx, float* score, void* ws, size_t ws_bytes,
+                     void* stream) {
+  return run_indexer("misa_indexer", false, q, w, k, kbar, q_seq, q_len, T, H, d, nseq, Lmax, B, h, 0, topk, heads,
+                     nullptr, idx, score, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int32_t misa_hier_indexer(const void* q, const float* w, const void* k, const float* kbar, const int32_t* q_seq,
+                          const int32_t* q_len, int64_t T, int32_t H, int32_t d, int64_t nseq, int64_t Lmax,
+                          int32_t B, int32_t h, int32_t kc, int32_t topk, int32_t* heads, int32_t* cand, int32_t* idx,
+                          float* score, void* ws, size_t ws_bytes, void* stream) {
+  return run_indexer("misa_hier_indexer", true, q, w, k, kbar, q_seq, q_len, T, H, d, nseq, Lmax, B, h, kc, topk,
+                     heads, cand, idx, score, ws, ws_bytes, (hipStream_t)stream);
 }
 
 int32_t misa_debug_scores(const void* q, const float* w, const void* k, const int32_t* heads, int32_t h,

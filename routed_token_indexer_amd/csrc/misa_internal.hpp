@@ -26,6 +26,13 @@ struct ScoreArgs {
   int64_t out_stride;
   int chunk;                // keys per workgroup chunk
   uint32_t* hist;           // optional [T][4096]: level-1 histogram of the written scores (decode kernel)
+  // fused decode pipeline: heads selected in the kernel from the router's partials
+  const float* partial;     // [T][nchunk_r][H] or null (then heads come from `heads`)
+  const float* xtail;       // [T][H]
+  int nchunk_r;
+  int B;
+  int32_t* heads_out;       // optional [T][hh], written by chunk 0
+  float* router_key;        // optional [T][H], written by chunk 0
 };
 
 int score_rows_per_query(int hh);
@@ -51,9 +58,15 @@ struct RouteArgs {
   int32_t* heads;           // [T][h]
   float* router_key;        // [T][H] or null
   float* partial;           // workspace [T][nchunk][H]
-  int32_t* counter;         // workspace [T]
+  int32_t* counter;         // unused
   int nchunk;
   int chunk_blocks;
+  // fused decode pipeline: always emit partials, the partial-block dot into
+  // xtail [T][H], select nothing, and zero the two regions below
+  bool fused;
+  float* xtail;
+  uint32_t* zero[2];
+  int64_t zero_words[2];
 };
 // Decode chunking of the pooled blocks (partials workspace in floats); prefill
 // shapes (many queries per sequence) route one query per wave and need none.
@@ -84,11 +97,11 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 struct SplitTopkWs {
   uint32_t* hist;      // [T][4096] level-1 histogram (zero on entry)
   uint32_t* state;     // [T][8]
-  uint32_t* counter;   // [T][4] candidate-list cursor (zero on entry)
+  uint32_t* counter;   // [T][4] (zero on entry; unused by the current kernels)
   uint32_t* ndef;      // [T][nchunk] elements above the level-1 threshold bin
-  uint32_t* off;       // unused (kept for layout stability)
-  uint32_t* eqb;       // unused (kept for layout stability)
-  uint32_t* cand;      // [T][cap][2] (key, index) of the threshold bin
+  uint32_t* ccnt;      // [T][nchunk] candidates of the threshold bin in each chunk
+  uint32_t* eqb;       // unused
+  uint32_t* cand;      // [T][nchunk][chunk][2] (key, index) of the threshold bin, per-chunk regions
   int64_t cap;
   int chunk;
   int nchunk;
@@ -102,6 +115,22 @@ hipError_t launch_zero(uint32_t* p, int64_t words, hipStream_t st);
 bool use_split_topk(int64_t T, int64_t max_len);
 // hist_done: the level-1 histogram was already accumulated by the scoring kernel.
 hipError_t launch_topk_split(const TopkArgs& a, const SplitTopkWs& w, bool hist_done, hipStream_t st);
+// rows of this length can always take the split path (whatever T)
+bool split_topk_always_ok(int64_t max_len);
+
+// Dense re-scoring of the kept candidates, fused into the coarse pass of MISA†.
+struct RescoreArgs {
+  const uint16_t* q;
+  const float* w;
+  const uint16_t* k;
+  int H;
+  int d;
+  float* scores;            // [T][kc] dense score of each candidate slot
+  uint32_t* hist;           // [T][4096] level-1 histogram of those scores (zero on entry)
+};
+// filter + compact of the coarse pass (level-1 histogram already built), the
+// compact writing the candidate list (a.idx, k = kc) and its dense scores.
+hipError_t launch_topk_split_rescore(const TopkArgs& a, const SplitTopkWs& w, const RescoreArgs& r, hipStream_t st);
 
 
 // Event timing of one internal kernel class (measurement aid).

@@ -1,0 +1,162 @@
+// Device building blocks of token scoring and head selection, shared by the
+// scoring kernels and the fused decode pipeline so that every path computes
+// bit-identical scores and routed head sets.
+#pragma once
+
+#include "misa_common.hpp"
+#include "misa_internal.hpp"
+
+namespace misa {
+
+// 16-key column tiles of B fragments: lane (grp, col) holds key col of each tile,
+// k-slots 8 * grp .. + 8 of every 32-dim step.
+template <int D, int KT>
+struct KeyTiles {
+  u32x4 b[KT][D / 32];
+  bool valid[KT];
+};
+
+// key_of(s) -> key row index of position s in [.., c_end), or -1 (zero tile column).
+template <int D, int KT, typename KeyOf>
+__device__ __forceinline__ void load_key_tiles(const uint16_t* kseq_lane, int base, int c_end, int col, KeyOf key_of,
+                                               KeyTiles<D, KT>& out) {
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    const int s = base + kt * 16 + col;
+    const int key = s < c_end ? key_of(s) : -1;
+    out.valid[kt] = key >= 0;
+    const uint16_t* kp = kseq_lane + (int64_t)(key < 0 ? 0 : key) * D;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (key >= 0) v = *reinterpret_cast<const u32x4*>(kp + ks * 32);
+      out.b[kt][ks] = v;
+    }
+  }
+}
+
+// A fragments and row weights of one query: row r*16 + i holds head head_of(row)
+// (-1: a zero row with weight 0).
+template <int D, int RT, typename HeadOf>
+__device__ __forceinline__ void load_query_rows(const uint16_t* q, const float* w, int64_t t, int H, int col, int grp,
+                                                HeadOf head_of, u32x4 (&afrag)[RT][D / 32], float (&wrow)[RT][4]) {
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const int head = head_of(16 * r + col);
+    const uint16_t* qp = q + (t * H + (head < 0 ? 0 : head)) * D + grp * 8;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (head >= 0) v = *reinterpret_cast<const u32x4*>(qp + ks * 32);
+      afrag[r][ks] = v;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int hd = head_of(16 * r + 4 * grp + j);
+      wrow[r][j] = hd < 0 ? 0.f : w[t * H + hd];
+    }
+  }
+}
+
+// Scores of 4 tiles (64 keys): ReLU, head weight and head sum on the MFMA
+// accumulators. Lane (grp, col) returns the score of key 16 * grp + col of the
+// group and whether that key was valid (invalid keys score -inf).
+template <int D, int RT>
+__device__ __forceinline__ float score_four_tiles(const u32x4 (&afrag)[RT][D / 32], const float (&wrow)[RT][4],
+                                                  const KeyTiles<D, 4>& tiles, int grp) {
+  float mine = 0.f;
+  bool mine_valid = false;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    float part = 0.f;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) acc = mfma_16x16x32(afrag[r][ks], tiles.b[kt][ks], acc);
+      part += wrow[r][0] * fmaxf(acc[0], 0.f) + wrow[r][1] * fmaxf(acc[1], 0.f) +
+              wrow[r][2] * fmaxf(acc[2], 0.f) + wrow[r][3] * fmaxf(acc[3], 0.f);
+    }
+    part += __shfl_xor(part, 16, kWave);
+    part += __shfl_xor(part, 32, kWave);
+    if (grp == kt) {
+      mine = part;
+      mine_valid = tiles.valid[kt];
+    }
+  }
+  return mine_valid ? mine + 0.f : -INFINITY;
+}
+
+// Score of one 16-key tile with the A fragments read from an LDS copy of the
+// query's rows (row stride ldq bf16; rows beyond the heads are zero) and the row
+// weights from LDS. Per key this is exactly the MFMA / epilogue sequence of
+// score_four_tiles, so the scores are the same bit for bit; every lane of the
+// wave returns the score of key col of the tile (-inf if invalid).
+template <int D, int RT>
+__device__ __forceinline__ float score_one_tile_lds(const uint16_t* s_q, int ldq, const float* s_w,
+                                                    const KeyTiles<D, 1>& tile, int grp, int col) {
+  float part = 0.f;
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    const uint16_t* qa = s_q + (16 * r + col) * ldq + grp * 8;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      acc = mfma_16x16x32(*reinterpret_cast<const u32x4*>(qa + ks * 32), tile.b[0][ks], acc);
+    const float* wr = s_w + 16 * r + 4 * grp;
+    part += wr[0] * fmaxf(acc[0], 0.f) + wr[1] * fmaxf(acc[1], 0.f) + wr[2] * fmaxf(acc[2], 0.f) +
+            wr[3] * fmaxf(acc[3], 0.f);
+  }
+  part += __shfl_xor(part, 16, kWave);
+  part += __shfl_xor(part, 32, kWave);
+  return tile.valid[0] ? part + 0.f : -INFINITY;
+}
+
+// Head ranking of the router (one wave; lane g < H holds head g's complete-block
+// aggregate A and partial-block dot x). rho_g = w_g * (n_tail * A_g + max(x_g, 0))
+// (n_tail = 0: rho_g = w_g * A_g); ties go to the lower head id. Returns whether
+// this lane's head is routed and its position among the routed heads (ascending
+// id), and the importance r_g = rho_g / n_tail.
+__device__ __forceinline__ bool route_rank(int H, int h, int lane, float w, float A, float x, int n_tail, int& pos,
+                                           float& r) {
+  const bool active = lane < H;
+  float rho;
+  if (n_tail > 0) {
+    const float xt = fmaxf(x, 0.f);
+    rho = w * ((float)n_tail * A + xt);
+    r = w * (A + xt / (float)n_tail);
+  } else {
+    rho = w * A;
+    r = rho;
+  }
+  rho += 0.f;   // -0 -> +0
+  r += 0.f;
+  int rank = 0;
+  for (int j = 0; j < H; ++j) {
+    const float o = __shfl(rho, j, kWave);
+    rank += (o > rho || (o == rho && j < lane)) ? 1 : 0;
+  }
+  const bool sel = active && rank < h;
+  const uint64_t m = __ballot(sel);
+  pos = __popcll(m & ((1ull << lane) - 1ull));
+  return sel;
+}
+
+// Complete-block aggregate of head `lane` from the router's chunk partials,
+// summed in chunk order.
+__device__ __forceinline__ float sum_partials(const float* partial, int64_t t, int nchunk, int H, int lane) {
+  float A = 0.f;
+  if (lane < H) {
+    const float* pp = partial + t * nchunk * H + lane;
+    int c = 0;
+    for (; c + 4 <= nchunk; c += 4) {
+      const float v0 = pp[(int64_t)c * H], v1 = pp[(int64_t)(c + 1) * H];
+      const float v2 = pp[(int64_t)(c + 2) * H], v3 = pp[(int64_t)(c + 3) * H];
+      A = (((A + v0) + v1) + v2) + v3;
+    }
+    for (; c < nchunk; ++c) A += pp[(int64_t)c * H];
+  }
+  return A;
+}
+
+}  // namespace misa

@@ -26,6 +26,7 @@
 //           each wave walks all complete blocks of its query and selects.
 #include "misa_common.hpp"
 #include "misa_internal.hpp"
+#include "misa_score_dev.hpp"
 
 namespace misa {
 namespace {
@@ -81,31 +82,12 @@ __device__ __forceinline__ void wave_tail_sum(const RouteArgs& a, int seq, int s
 // wave; lane g < H holds head g's complete-block aggregate A and partial-block dot x.
 __device__ __forceinline__ void route_select(const RouteArgs& a, int64_t t, int lane, float A, float x,
                                              int n_tail) {
-  const bool active = lane < a.H;
-  const float w = active ? a.w[t * a.H + lane] : 0.f;
-  float rho, r;
-  if (n_tail > 0) {
-    const float xt = fmaxf(x, 0.f);
-    rho = w * ((float)n_tail * A + xt);
-    r = w * (A + xt / (float)n_tail);
-  } else {
-    rho = w * A;
-    r = rho;
-  }
-  rho += 0.f;   // -0 -> +0
-  r += 0.f;
-  int rank = 0;
-  for (int j = 0; j < a.H; ++j) {
-    const float o = __shfl(rho, j, kWave);
-    rank += (o > rho || (o == rho && j < lane)) ? 1 : 0;
-  }
-  const bool sel = active && rank < a.h;
-  const uint64_t m = __ballot(sel);
-  if (sel) {
-    const int pos = __popcll(m & ((1ull << lane) - 1ull));
-    a.heads[t * a.h + pos] = lane;
-  }
-  if (active && a.router_key) a.router_key[t * a.H + lane] = r;
+  const float w = lane < a.H ? a.w[t * a.H + lane] : 0.f;
+  int pos;
+  float r;
+  const bool sel = route_rank(a.H, a.h, lane, w, A, x, n_tail, pos, r);
+  if (sel) a.heads[t * a.h + pos] = lane;
+  if (lane < a.H && a.router_key) a.router_key[t * a.H + lane] = r;
 }
 
 // Tail dot x_g = q_g . S_tail for lane g < H (q read from global, S_tail in LDS).
@@ -226,6 +208,25 @@ __global__ __launch_bounds__(256) void route_decode_kernel(RouteArgs a) {
   __syncthreads();
   const int tid = threadIdx.x;
   const float A = tid < 64 ? ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid] : 0.f;
+  if (a.fused) {
+    // fused decode pipeline: emit the chunk partial and (chunk 0) the partial-block
+    // dot; the scoring kernel sums them and selects the heads. Every workgroup also
+    // clears a slice of the later launches' zero-initialised state.
+    if (tid < a.H) a.partial[(t * a.nchunk + c) * a.H + tid] = A;
+    const int64_t lin = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    const int64_t nwg = (int64_t)gridDim.x * gridDim.y;
+    for (int z = 0; z < 2; ++z)
+      for (int64_t i = lin * 256 + tid; i < a.zero_words[z]; i += nwg * 256) a.zero[z][i] = 0u;
+    if (c != 0 || wave != 0) return;
+    const int n_tail = p - nfull * a.B;
+    wave_tail_sum<D>(a, seq, nfull * a.B, n_tail, stail);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const float x = n_tail > 0 ? tail_dot<D>(a, t, lane, stail) : 0.f;
+    if (lane < a.H) a.xtail[t * a.H + lane] = x;
+    return;
+  }
   if (a.nchunk > 1) {
     if (tid < a.H) a.partial[(t * a.nchunk + c) * a.H + tid] = A;
     return;
@@ -250,17 +251,7 @@ __global__ __launch_bounds__(64) void route_final_kernel(RouteArgs a) {
   query_prefix(a, t, seq, p);
   const int nfull = p / a.B;
   const int n_tail = p - nfull * a.B;
-  float A = 0.f;
-  if (lane < a.H) {
-    const float* pp = a.partial + t * a.nchunk * a.H + lane;
-    int c = 0;
-    for (; c + 4 <= a.nchunk; c += 4) {
-      const float v0 = pp[(int64_t)c * a.H], v1 = pp[(int64_t)(c + 1) * a.H];
-      const float v2 = pp[(int64_t)(c + 2) * a.H], v3 = pp[(int64_t)(c + 3) * a.H];
-      A = (((A + v0) + v1) + v2) + v3;
-    }
-    for (; c < a.nchunk; ++c) A += pp[(int64_t)c * a.H];
-  }
+  const float A = sum_partials(a.partial, t, a.nchunk, a.H, lane);
   wave_tail_sum<D>(a, seq, nfull * a.B, n_tail, stail);
   __syncthreads();
   const float x = n_tail > 0 ? tail_dot<D>(a, t, lane, stail) : 0.f;
@@ -299,13 +290,13 @@ __global__ __launch_bounds__(256) void route_prefill_kernel(RouteArgs a) {
 
 template <int D, int RTQ>
 hipError_t launch_rtq(const RouteArgs& a, bool prefill, hipStream_t st) {
-  if (prefill) {
+  if (prefill && !a.fused) {
     hipLaunchKernelGGL((route_prefill_kernel<D, RTQ>), dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, st, a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((route_decode_kernel<D, RTQ>), dim3(a.nchunk, (unsigned)a.T), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.nchunk == 1) return e;
+  if (e != hipSuccess || a.nchunk == 1 || a.fused) return e;
   hipLaunchKernelGGL((route_final_kernel<D>), dim3((unsigned)a.T), dim3(64), 0, st, a);
   return hipGetLastError();
 }

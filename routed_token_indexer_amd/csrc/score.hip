@@ -23,6 +23,7 @@
 //                  query tile.
 #include "misa_common.hpp"
 #include "misa_internal.hpp"
+#include "misa_score_dev.hpp"
 
 namespace misa {
 
@@ -197,41 +198,16 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 }
 
 // decode: grid (key chunks, T); one query per workgroup, its rows padded to RT tiles.
-// Keys do not depend on the routed heads, so the first key tile loads are issued
-// before the head ids and query rows are fetched, and every iteration prefetches
-// the next iteration's keys before computing the current one.
-template <int D, int KT, bool GATHER>
-__device__ __forceinline__ void load_key_tiles(const ScoreArgs& a, const uint16_t* kseq, const int32_t* crow, int p,
-                                               int base, int c_end, int col, u32x4 (&bf)[KT][D / 32],
-                                               bool (&valid)[KT]) {
-#pragma unroll
-  for (int kt = 0; kt < KT; ++kt) {
-    const int s = base + kt * 16 + col;
-    int key = -1;
-    if (s < c_end) {
-      if constexpr (GATHER) {
-        const int id = crow[s];
-        key = (id >= 0 && id < p) ? id : -1;
-      } else {
-        key = s;
-      }
-    }
-    valid[kt] = key >= 0;
-    const uint16_t* kp = kseq + (int64_t)(key < 0 ? 0 : key) * D;
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (key >= 0) v = *reinterpret_cast<const u32x4*>(kp + ks * 32);
-      bf[kt][ks] = v;
-    }
-  }
-}
-
+// Keys do not depend on the routed heads, so the first key tiles are requested
+// before the head ids and query rows, and every iteration prefetches the next
+// iteration's keys before computing the current one. With a.partial set, the
+// workgroup first selects the query's routed heads itself from the router's
+// chunk partials (the fused decode pipeline).
 template <int D, int RT, bool GATHER, bool HIST>
 __global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a) {
-  constexpr int KS = D / 32;
   constexpr int KT = 4;   // 16-key tiles per wave iteration: 64 keys, one per lane at the end
   __shared__ uint32_t lh[HIST ? 4096 : 1];
+  __shared__ int s_heads[64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int64_t t = blockIdx.y;
@@ -244,77 +220,66 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a) {
   p = p < 0 ? 0 : (p > a.Lmax ? (int)a.Lmax : p);
   const int n = GATHER ? (seq < 0 ? 0 : a.kc) : p;
   const int c_begin = blockIdx.x * a.chunk;
-  if (c_begin >= n) return;
+  const bool fused_route = a.partial != nullptr;
+  if (c_begin >= n && !(fused_route && blockIdx.x == 0)) return;
   const int c_end = min(c_begin + a.chunk, n);
-  if constexpr (HIST) {
-    for (int i = threadIdx.x; i < 4096; i += 256) lh[i] = 0;
-    __syncthreads();   // nothing is in flight yet
-  }
-  const uint16_t* kseq = a.k + (int64_t)seq * a.Lmax * D + grp * 8;
+  const uint16_t* kseq = a.k + (int64_t)(seq < 0 ? 0 : seq) * a.Lmax * D + grp * 8;
   const int32_t* crow = GATHER ? a.cand + t * a.kc : nullptr;
-  float* orow = a.out + t * a.out_stride;
+  auto key_of = [&](int s) -> int {
+    if constexpr (GATHER) {
+      const int id = crow[s];
+      return (id >= 0 && id < p) ? id : -1;
+    } else {
+      return s;
+    }
+  };
 
   int base = c_begin + wave * 16 * KT;
-  u32x4 bcur[KT][KS];
-  bool vcur[KT];
-  load_key_tiles<D, KT, GATHER>(a, kseq, crow, p, base, c_end, col, bcur, vcur);
+  KeyTiles<D, KT> cur;
+  load_key_tiles<D, KT>(kseq, base, c_end, col, key_of, cur);
 
-  u32x4 afrag[RT][KS];
+  if (HIST || fused_route) {
+    if constexpr (HIST) {
+      for (int i = threadIdx.x; i < 4096; i += 256) lh[i] = 0;
+    }
+    if (fused_route && wave == 0) {
+      const float A = sum_partials(a.partial, t, a.nchunk_r, a.H, lane);
+      const float x = lane < a.H ? a.xtail[t * a.H + lane] : 0.f;
+      const float wg = lane < a.H ? a.w[t * a.H + lane] : 0.f;
+      const int n_tail = p - (p / a.B) * a.B;
+      int pos;
+      float r;
+      const bool sel = route_rank(a.H, a.hh, lane, wg, A, x, n_tail, pos, r);
+      if (sel) s_heads[pos] = lane;
+      if (blockIdx.x == 0) {
+        if (sel && a.heads_out) a.heads_out[t * a.hh + pos] = lane;
+        if (lane < a.H && a.router_key) a.router_key[t * a.H + lane] = r;
+      }
+    }
+    __syncthreads();
+  }
+  if (c_begin >= n) return;
+
+  u32x4 afrag[RT][D / 32];
   float wrow[RT][4];
-#pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    const int head = row_head(a, t, 16 * r + col);
-    const uint16_t* qp = a.q + (t * a.H + (head < 0 ? 0 : head)) * D + grp * 8;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (head >= 0) v = *reinterpret_cast<const u32x4*>(qp + ks * 32);
-      afrag[r][ks] = v;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int hd = row_head(a, t, 16 * r + 4 * grp + j);
-      wrow[r][j] = hd < 0 ? 0.f : a.w[t * a.H + hd];
-    }
+  if (fused_route) {
+    load_query_rows<D, RT>(a.q, a.w, t, a.H, col, grp, [&](int row) { return row < a.hh ? s_heads[row] : -1; },
+                           afrag, wrow);
+  } else {
+    load_query_rows<D, RT>(a.q, a.w, t, a.H, col, grp, [&](int row) { return row_head(a, t, row); }, afrag, wrow);
   }
 
+  float* orow = a.out + t * a.out_stride;
   for (; base < c_end; base += 4 * 16 * KT) {
-    u32x4 bnext[KT][KS];
-    bool vnext[KT];
-    load_key_tiles<D, KT, GATHER>(a, kseq, crow, p, base + 4 * 16 * KT, c_end, col, bnext, vnext);
-    float mine = 0.f;
-    bool mine_valid = false;
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      float part = 0.f;
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma_16x16x32(afrag[r][ks], bcur[kt][ks], acc);
-        part += wrow[r][0] * fmaxf(acc[0], 0.f) + wrow[r][1] * fmaxf(acc[1], 0.f) +
-                wrow[r][2] * fmaxf(acc[2], 0.f) + wrow[r][3] * fmaxf(acc[3], 0.f);
-      }
-      part += __shfl_xor(part, 16, kWave);
-      part += __shfl_xor(part, 32, kWave);
-      // every lane now holds the score of key (kt * 16 + col); lane group kt keeps it
-      if (grp == kt) {
-        mine = part;
-        mine_valid = vcur[kt];
-      }
-    }
+    KeyTiles<D, KT> nxt;
+    load_key_tiles<D, KT>(kseq, base + 4 * 16 * KT, c_end, col, key_of, nxt);
+    const float v = score_four_tiles<D, RT>(afrag, wrow, cur, grp);
     const int s = base + lane;
     if (s < c_end) {
-      const float v = mine_valid ? mine + 0.f : -INFINITY;
       orow[s] = v;
       if constexpr (HIST) atomicAdd(&lh[score_key(v) >> 20], 1u);
     }
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      vcur[kt] = vnext[kt];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) bcur[kt][ks] = bnext[kt][ks];
-    }
+    cur = nxt;
   }
   if constexpr (HIST) {
     __syncthreads();

@@ -321,3 +321,33 @@ def test_non_power_of_two_block():
     for t in range(4):
         tally.add(idx[t], oi[t], rows[t], 200, exact=False)
     tally.check()
+
+
+# ------------------------------------------------------------------ fused entry points
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("case", list(CASES))
+def test_fused_indexers_match_separate_calls(case, mode):
+    """misa_indexer / misa_hier_indexer give bit-identical results to route +
+    score_topk (+ hier_rerank) made separately (decode shapes run the fused
+    pipeline, prefill shapes fall back to the separate calls)."""
+    x, dev = get(case, mode)
+    c = x.cfg
+    kc = c.kc or min(4 * c.topk, c.L)
+    kbar = M.pool_keys(dev["k"], c.B)
+    hd = M.route(dev["q"], dev["w"], dev["k"], kbar, dev["q_seq"], dev["q_len"], c.B, c.h)
+    i1, s1 = M.score_topk(dev["q"], dev["w"], dev["k"], hd, dev["q_seq"], dev["q_len"], c.topk)
+    cand1, _ = M.score_topk(dev["q"], dev["w"], dev["k"], hd, dev["q_seq"], dev["q_len"], kc)
+    j1, t1 = M.hier_rerank(dev["q"], dev["w"], dev["k"], cand1, dev["q_seq"], dev["q_len"], c.topk)
+    for rep in range(2):                       # the second call reuses a dirty workspace
+        h2 = torch.full_like(hd, -7)
+        i2, s2 = M.indexer(dev["q"], dev["w"], dev["k"], kbar, dev["q_seq"], dev["q_len"], c.B, c.h, c.topk,
+                           heads=h2)
+        h3 = torch.full_like(hd, -7)
+        cand3 = torch.full_like(cand1, -7)
+        j3, t3 = M.hier_indexer(dev["q"], dev["w"], dev["k"], kbar, dev["q_seq"], dev["q_len"], c.B, c.h, kc,
+                                c.topk, heads=h3, cand=cand3)
+        torch.cuda.synchronize()
+        assert torch.equal(h2, hd) and torch.equal(h3, hd)
+        assert torch.equal(i2, i1) and torch.equal(s2, s1)
+        assert torch.equal(cand3, cand1)
+        assert torch.equal(j3, j1) and torch.equal(t3, t1)
