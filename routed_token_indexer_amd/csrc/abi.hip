@@ -409,6 +409,10 @@ int32_t run_indexer(const char* fn, bool hier, const void* q, const float* w, co
   }
 
   FusedLayout f = fused_layout(T, H, Lmax, B, hier ? kc : 0, ws);
+  // coarse selection: split over chunks for long rows (MISA† always: its
+  // compaction also re-scores the kept tokens); one workgroup per row otherwise
+  const bool coarse_split = hier || misa::use_split_topk(T, Lmax);
+  const bool fine_split = hier && kc > misa::topk_row_reg_max();
   // 1. router partials (+ partial-block dots), clearing the top-k state of the later launches
   misa::RouteArgs ra{};
   ra.q = static_cast<const uint16_t*>(q);
@@ -428,10 +432,10 @@ int32_t run_indexer(const char* fn, bool hier, const void* q, const float* w, co
   ra.chunk_blocks = f.chunk_blocks;
   ra.fused = true;
   ra.xtail = f.xtail;
-  ra.zero[0] = f.sw.hist;
-  ra.zero_words[0] = misa::split_topk_zero_words(T);
-  ra.zero[1] = hier ? f.rw.hist : nullptr;
-  ra.zero_words[1] = hier ? misa::split_topk_zero_words(T) : 0;
+  ra.zero[0] = coarse_split ? f.sw.hist : nullptr;
+  ra.zero_words[0] = coarse_split ? misa::split_topk_zero_words(T) : 0;
+  ra.zero[1] = fine_split ? f.rw.hist : nullptr;
+  ra.zero_words[1] = fine_split ? misa::split_topk_zero_words(T) : 0;
   misa::timing_before(misa::KID_ROUTE, st);
   hipError_t e = misa::launch_route(ra, d, st);
   misa::timing_after(misa::KID_ROUTE, st);
@@ -451,7 +455,7 @@ int32_t run_indexer(const char* fn, bool hier, const void* q, const float* w, co
   sa.Lmax = Lmax;
   sa.out = f.scores;
   sa.out_stride = Lmax;
-  sa.hist = f.sw.hist;
+  sa.hist = coarse_split ? f.sw.hist : nullptr;
   sa.partial = f.partial;
   sa.xtail = f.xtail;
   sa.nchunk_r = f.nchunk_r;
@@ -475,7 +479,7 @@ int32_t run_indexer(const char* fn, bool hier, const void* q, const float* w, co
     b.k = topk;
     b.idx = idx;
     b.score = score;
-    e = misa::launch_topk_split(b, f.sw, true, st);
+    e = coarse_split ? misa::launch_topk_split(b, f.sw, true, st) : misa::launch_topk(b, st);
   } else {
     int32_t* cd = cand ? cand : f.cand;
     b.k = kc;
@@ -488,7 +492,7 @@ int32_t run_indexer(const char* fn, bool hier, const void* q, const float* w, co
     r.H = H;
     r.d = d;
     r.scores = f.rr_scores;
-    r.hist = f.rw.hist;
+    r.hist = fine_split ? f.rw.hist : nullptr;   // level-1 histogram of the split fine stage
     e = misa::launch_topk_split_rescore(b, f.sw, r, st);
     if (e == hipSuccess) {
       // 4. MISA† fine stage: top-k of the candidates' dense scores
@@ -505,7 +509,7 @@ int32_t run_indexer(const char* fn, bool hier, const void* q, const float* w, co
       b2.k = topk;
       b2.idx = idx;
       b2.score = score;
-      e = misa::launch_topk_split(b2, f.rw, true, st);
+      e = fine_split ? misa::launch_topk_split(b2, f.rw, true, st) : misa::launch_topk(b2, st);
     }
   }
   misa::timing_after(misa::KID_TOPK, st);

@@ -25,6 +25,17 @@ __device__ __forceinline__ floatx4 mfma_16x16x32(const u32x4& a, const u32x4& b,
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
+// Raw buffer view of [p, p + bytes) (gfx9 descriptor word 3). The hardware
+// range check drops stores at byte offsets >= bytes and returns 0 for such
+// loads, so a ragged tail needs no branch around the access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void buffer_store_f32(float v, __amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, (int)byte_off, 0, 0);
+}
+
 // Order-preserving map of a float score onto uint32: a > b  <=>  key(a) > key(b).
 // -0.0 and +0.0 map to the same key (scores compare as reals).
 __device__ __forceinline__ uint32_t score_key(float s) {

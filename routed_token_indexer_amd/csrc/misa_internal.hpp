@@ -91,17 +91,20 @@ struct TopkArgs {
   float* score;             // [T][k] or null
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+// Longest row the register-resident single-workgroup top-k handles.
+int64_t topk_row_reg_max();
 
 // Split top-k for few long rows: several workgroups per row cooperate through
 // global memory (level-1 histogram, candidate list, per-chunk offsets).
 struct SplitTopkWs {
   uint32_t* hist;      // [T][4096] level-1 histogram (zero on entry)
-  uint32_t* state;     // [T][8]
-  uint32_t* counter;   // [T][4] (zero on entry; unused by the current kernels)
-  uint32_t* ndef;      // [T][nchunk] elements above the level-1 threshold bin
-  uint32_t* ccnt;      // [T][nchunk] candidates of the threshold bin in each chunk
-  uint32_t* eqb;       // unused
-  uint32_t* cand;      // [T][nchunk][chunk][2] (key, index) of the threshold bin, per-chunk regions
+  uint32_t* state;     // [T][8] threshold key and how many keys equal to it are kept
+  uint32_t* counter;   // [T][4] candidate-list cursor, arrivals of the filter (zero on entry)
+  uint32_t* ndef;      // [T][nchunk] keys above the level-1 threshold bin in each chunk
+  uint32_t* selb;      // [T][nchunk] output offset of each chunk
+  uint32_t* eqb;       // [T][nchunk] keys equal to the threshold key before each chunk
+  uint32_t* seg;       // [T][nchunk][2] each chunk's run of the candidate list (start, count)
+  uint32_t* cand;      // [T][cap][2] (key, index) of the level-1 threshold bin
   int64_t cap;
   int chunk;
   int nchunk;

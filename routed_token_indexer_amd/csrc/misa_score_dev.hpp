@@ -16,22 +16,24 @@ struct KeyTiles {
   bool valid[KT];
 };
 
-// key_of(s) -> key row index of position s in [.., c_end), or -1 (zero tile column).
+// key_of(s) -> key row index of position s in [.., c_end), or -1 (an invalid
+// column). Every lane loads unconditionally: an invalid column reads row
+// `fallback` (which the caller guarantees to exist) and is only marked invalid.
+// An MFMA output column depends on its own key column alone, and invalid columns
+// are replaced by -inf, so their data never reaches a score. (A per-lane
+// conditional load makes the compiler wait for each tile before the next is
+// requested, which serializes the prefetch.)
 template <int D, int KT, typename KeyOf>
 __device__ __forceinline__ void load_key_tiles(const uint16_t* kseq_lane, int base, int c_end, int col, KeyOf key_of,
-                                               KeyTiles<D, KT>& out) {
+                                               int fallback, KeyTiles<D, KT>& out) {
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
     const int s = base + kt * 16 + col;
     const int key = s < c_end ? key_of(s) : -1;
     out.valid[kt] = key >= 0;
-    const uint16_t* kp = kseq_lane + (int64_t)(key < 0 ? 0 : key) * D;
+    const uint16_t* kp = kseq_lane + (int64_t)(key < 0 ? fallback : key) * D;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (key >= 0) v = *reinterpret_cast<const u32x4*>(kp + ks * 32);
-      out.b[kt][ks] = v;
-    }
+    for (int ks = 0; ks < D / 32; ++ks) out.b[kt][ks] = *reinterpret_cast<const u32x4*>(kp + ks * 32);
   }
 }
 
@@ -131,9 +133,12 @@ __device__ __forceinline__ bool route_rank(int H, int h, int lane, float w, floa
   }
   rho += 0.f;   // -0 -> +0
   r += 0.f;
+  // j is uniform, so each comparison value is read with v_readlane (no LDS
+  // round trip per head)
   int rank = 0;
+  const int rho_bits = __float_as_int(rho);
   for (int j = 0; j < H; ++j) {
-    const float o = __shfl(rho, j, kWave);
+    const float o = __int_as_float(__builtin_amdgcn_readlane(rho_bits, j));
     rank += (o > rho || (o == rho && j < lane)) ? 1 : 0;
   }
   const bool sel = active && rank < h;
@@ -143,20 +148,41 @@ __device__ __forceinline__ bool route_rank(int H, int h, int lane, float w, floa
 }
 
 // Complete-block aggregate of head `lane` from the router's chunk partials,
-// summed in chunk order.
-__device__ __forceinline__ float sum_partials(const float* partial, int64_t t, int nchunk, int H, int lane) {
+// summed in chunk order. The first kPartialBatch partials are requested
+// together (one memory round trip for the usual chunk counts); the sum is the
+// same sequential chunk-order sum whatever the batching.
+constexpr int kPartialBatch = 16;
+
+struct PartialBatch {
+  float v[kPartialBatch];
+};
+
+// Requests the first kPartialBatch partials of head `lane` (clamped, in-bounds
+// addresses; entries past nchunk are ignored by finish_partials).
+__device__ __forceinline__ void load_partials(const float* partial, int64_t t, int nchunk, int H, int lane,
+                                              PartialBatch& pb) {
+  const float* pp = partial + t * nchunk * H + (lane < H ? lane : H - 1);
+#pragma unroll
+  for (int j = 0; j < kPartialBatch; ++j) pb.v[j] = pp[(int64_t)(j < nchunk ? j : 0) * H];
+}
+
+__device__ __forceinline__ float finish_partials(const float* partial, int64_t t, int nchunk, int H, int lane,
+                                                 const PartialBatch& pb) {
   float A = 0.f;
   if (lane < H) {
+#pragma unroll
+    for (int j = 0; j < kPartialBatch; ++j)
+      if (j < nchunk) A += pb.v[j];
     const float* pp = partial + t * nchunk * H + lane;
-    int c = 0;
-    for (; c + 4 <= nchunk; c += 4) {
-      const float v0 = pp[(int64_t)c * H], v1 = pp[(int64_t)(c + 1) * H];
-      const float v2 = pp[(int64_t)(c + 2) * H], v3 = pp[(int64_t)(c + 3) * H];
-      A = (((A + v0) + v1) + v2) + v3;
-    }
-    for (; c < nchunk; ++c) A += pp[(int64_t)c * H];
+    for (int c = kPartialBatch; c < nchunk; ++c) A += pp[(int64_t)c * H];
   }
   return A;
+}
+
+__device__ __forceinline__ float sum_partials(const float* partial, int64_t t, int nchunk, int H, int lane) {
+  PartialBatch pb;
+  load_partials(partial, t, nchunk, H, lane, pb);
+  return finish_partials(partial, t, nchunk, H, lane, pb);
 }
 
 }  // namespace misa

@@ -198,19 +198,50 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 }
 
 // decode: grid (key chunks, T); one query per workgroup, its rows padded to RT tiles.
-// Keys do not depend on the routed heads, so the first key tiles are requested
-// before the head ids and query rows, and every iteration prefetches the next
-// iteration's keys before computing the current one. With a.partial set, the
-// workgroup first selects the query's routed heads itself from the router's
-// chunk partials (the fused decode pipeline).
+// Startup is ordered for a memory system that the key stream is about to
+// saturate: everything that does not depend on the query's sequence (its H
+// query rows, which are staged in LDS, its weights, the routed head ids or the
+// router's chunk partials) is requested first, then the first key tiles, and
+// only then are the routed heads selected and the A fragments read from LDS.
+// Every iteration prefetches the next iteration's keys before computing the
+// current one. With a.partial set, the workgroup selects the query's routed
+// heads itself from the router's chunk partials (the fused decode pipeline).
 template <int D, int RT, bool GATHER, bool HIST>
 __global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a) {
-  constexpr int KT = 4;   // 16-key tiles per wave iteration: 64 keys, one per lane at the end
+  constexpr int KT = 4;           // 16-key tiles per wave iteration: 64 keys, one per lane at the end
+  constexpr int LDQ = D + 8;      // LDS row stride of the staged query rows (bf16)
+  constexpr int QV = D / 8;       // 16-byte pieces per query row
+  constexpr int QPT = (64 * QV + 255) / 256;   // staging pieces per thread (H <= 64)
   __shared__ uint32_t lh[HIST ? 4096 : 1];
+  __shared__ __align__(16) uint16_t s_q[64 * LDQ];
+  __shared__ float s_w[64];
   __shared__ int s_heads[64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int64_t t = blockIdx.y;
+  const bool fused_route = a.partial != nullptr;
+
+  // 1. requests that do not depend on the sequence
+  u32x4 qv[QPT];
+  const int nqv = a.H * QV;
+  const uint16_t* qsrc = a.q + t * a.H * D;
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    qv[j] = *reinterpret_cast<const u32x4*>(qsrc + (int64_t)(i < nqv ? i : 0) * 8);
+  }
+  // Issued by every lane from clamped, in-bounds addresses (a conditional load
+  // would make the compiler wait for it before the key requests go out); the
+  // pointer selects only depend on kernel arguments.
+  const int gl = lane < a.H ? lane : a.H - 1;
+  const float wg = a.w[t * a.H + gl];
+  const float x = (fused_route ? a.xtail : a.w)[t * a.H + gl];
+  PartialBatch pb;
+  load_partials(fused_route ? a.partial : a.w, t, fused_route ? a.nchunk_r : 1, a.H, lane, pb);
+  const int32_t* hp = a.heads ? a.heads + t * a.hh + (lane < a.hh ? lane : a.hh - 1) : a.q_seq + t;
+  const int hv = *hp;
+  const int head_in = a.heads ? hv : lane;
+
   int seq = a.q_seq[t];
   int p = a.q_len[t];
   if (seq < 0 || seq >= a.nseq) {
@@ -220,7 +251,6 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a) {
   p = p < 0 ? 0 : (p > a.Lmax ? (int)a.Lmax : p);
   const int n = GATHER ? (seq < 0 ? 0 : a.kc) : p;
   const int c_begin = blockIdx.x * a.chunk;
-  const bool fused_route = a.partial != nullptr;
   if (c_begin >= n && !(fused_route && blockIdx.x == 0)) return;
   const int c_end = min(c_begin + a.chunk, n);
   const uint16_t* kseq = a.k + (int64_t)(seq < 0 ? 0 : seq) * a.Lmax * D + grp * 8;
@@ -233,19 +263,36 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a) {
       return s;
     }
   };
+  // c_begin < max_len <= Lmax, so row c_begin of the (clamped) sequence exists
+  const int fallback = GATHER ? 0 : c_begin;
 
-  int base = c_begin + wave * 16 * KT;
-  KeyTiles<D, KT> cur;
-  load_key_tiles<D, KT>(kseq, base, c_end, col, key_of, cur);
+  // 2. consume the small loads before any key request of this wave goes out
+  // (workgroups dispatched a little later would otherwise find their small
+  // loads queued behind tens of MiB of key requests): stage the query rows and
+  // weights, and (wave 0) sum the router's partials.
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    if (i < nqv) *reinterpret_cast<u32x4*>(s_q + (i / QV) * LDQ + (i % QV) * 8) = qv[j];
+  }
+  float A = 0.f;
+  if (wave == 0) {
+    if (lane < a.H) s_w[lane] = wg;
+    if (fused_route) A = finish_partials(a.partial, t, a.nchunk_r, a.H, lane, pb);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 
-  if (HIST || fused_route) {
-    if constexpr (HIST) {
-      for (int i = threadIdx.x; i < 4096; i += 256) lh[i] = 0;
-    }
-    if (fused_route && wave == 0) {
-      const float A = sum_partials(a.partial, t, a.nchunk_r, a.H, lane);
-      const float x = lane < a.H ? a.xtail[t * a.H + lane] : 0.f;
-      const float wg = lane < a.H ? a.w[t * a.H + lane] : 0.f;
+  // 3. the first two iterations' key tiles (two in flight per wave)
+  constexpr int kStep = 4 * 16 * KT;   // keys per workgroup iteration
+  const int base0 = c_begin + wave * 16 * KT;
+  KeyTiles<D, KT> ta, tb;
+  load_key_tiles<D, KT>(kseq, base0, c_end, col, key_of, fallback, ta);
+  load_key_tiles<D, KT>(kseq, base0 + kStep, c_end, col, key_of, fallback, tb);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // 4. select the heads while the keys stream in
+  if (wave == 0) {
+    if (fused_route) {
       const int n_tail = p - (p / a.B) * a.B;
       int pos;
       float r;
@@ -255,32 +302,63 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a) {
         if (sel && a.heads_out) a.heads_out[t * a.hh + pos] = lane;
         if (lane < a.H && a.router_key) a.router_key[t * a.H + lane] = r;
       }
+    } else if (lane < a.hh) {
+      s_heads[lane] = (head_in >= 0 && head_in < a.H) ? head_in : -1;
     }
-    __syncthreads();
   }
+  if constexpr (HIST) {
+    for (int i = threadIdx.x; i < 4096; i += 256) lh[i] = 0;
+  }
+  __syncthreads();
   if (c_begin >= n) return;
 
   u32x4 afrag[RT][D / 32];
   float wrow[RT][4];
-  if (fused_route) {
-    load_query_rows<D, RT>(a.q, a.w, t, a.H, col, grp, [&](int row) { return row < a.hh ? s_heads[row] : -1; },
-                           afrag, wrow);
-  } else {
-    load_query_rows<D, RT>(a.q, a.w, t, a.H, col, grp, [&](int row) { return row_head(a, t, row); }, afrag, wrow);
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const int row = 16 * r + col;
+    const int head = row < a.hh ? s_heads[row] : -1;
+    const uint16_t* qa = s_q + (head < 0 ? 0 : head) * LDQ + grp * 8;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qa + ks * 32);
+      afrag[r][ks] = head < 0 ? u32x4{0u, 0u, 0u, 0u} : v;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row2 = 16 * r + 4 * grp + j;
+      const int hd = row2 < a.hh ? s_heads[row2] : -1;
+      wrow[r][j] = hd < 0 ? 0.f : s_w[hd];
+    }
   }
 
-  float* orow = a.out + t * a.out_stride;
-  for (; base < c_end; base += 4 * 16 * KT) {
-    KeyTiles<D, KT> nxt;
-    load_key_tiles<D, KT>(kseq, base + 4 * 16 * KT, c_end, col, key_of, nxt);
-    const float v = score_four_tiles<D, RT>(afrag, wrow, cur, grp);
-    const int s = base + lane;
-    if (s < c_end) {
-      orow[s] = v;
-      if constexpr (HIST) atomicAdd(&lh[score_key(v) >> 20], 1u);
-    }
-    cur = nxt;
+  // Scores of this chunk go through a buffer view of [c_begin, c_end), so the
+  // stores of lanes past c_end are dropped by the range check instead of being
+  // branched around: the loop body stays straight-line and the compiler can
+  // count the loads in flight exactly.
+  const auto ov = buffer_view(a.out + t * a.out_stride + c_begin, (uint32_t)(c_end - c_begin) * 4u);
+  auto emit = [&](const KeyTiles<D, KT>& tiles, int b) {
+    const float v = score_four_tiles<D, RT>(afrag, wrow, tiles, grp);
+    const int s = b + lane;
+    buffer_store_f32(v, ov, (uint32_t)(s - c_begin) * 4u);
+    if constexpr (HIST) atomicAdd(&lh[score_key(v) >> 20], s < c_end ? 1u : 0u);
+  };
+  // Two register sets alternate, so no in-flight tile is ever copied (a copy
+  // would wait for its load). The iteration count is uniform over the
+  // workgroup; each wave masks its own tail through c_end. Inside the loop the
+  // loads are unconditional (an odd count prefetches one spare iteration of
+  // in-bounds rows).
+  const int nit = (c_end - c_begin + kStep - 1) / kStep;
+  int it = 0;
+  for (; it + 2 < nit; it += 2) {
+    const int b = base0 + it * kStep;
+    emit(ta, b);
+    load_key_tiles<D, KT>(kseq, b + 2 * kStep, c_end, col, key_of, fallback, ta);
+    emit(tb, b + kStep);
+    load_key_tiles<D, KT>(kseq, b + 3 * kStep, c_end, col, key_of, fallback, tb);
   }
+  if (it < nit) emit(ta, base0 + it * kStep);
+  if (it + 1 < nit) emit(tb, base0 + (it + 1) * kStep);
   if constexpr (HIST) {
     __syncthreads();
     uint32_t* gh = a.hist + t * 4096;

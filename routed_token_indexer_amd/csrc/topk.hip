@@ -15,6 +15,7 @@
 // re-read from global memory in each pass.
 #include "misa_common.hpp"
 #include "misa_internal.hpp"
+#include "misa_select.hpp"
 
 namespace misa {
 namespace {
@@ -206,6 +207,137 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(TopkArgs a) {
   }
 }
 
+// Register-resident variant for rows of at most kTopkThreads * EPT scores
+// (EPT <= 32): every key stays in the registers of its lane for the whole
+// select, wave w owning the contiguous run [64 * EPT * w, 64 * EPT * (w + 1))
+// with lane l holding elements 64 * j + l of it.
+// The radix levels run on v = key - min(key) over the row's nbits-bit range,
+// 12 bits per level from the top of that range: scores concentrated in a few
+// octaves then spread over the histogram instead of piling into a handful of
+// exponent bins (which serializes the LDS atomics and leaves large threshold
+// bins), and the select usually ends after one or two levels.
+template <int EPT, bool GATHER>
+__global__ __launch_bounds__(kTopkThreads) void topk_row_reg_kernel(TopkArgs a) {
+  constexpr bool kPrefetchIds = GATHER && EPT <= 16;   // token ids held beside the keys
+  __shared__ RadixScratch rs;
+  __shared__ uint32_t wmin[kSelWaves], wmax[kSelWaves];
+  __shared__ uint32_t wgt[kSelWaves], weq[kSelWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t t = blockIdx.x;
+  int64_t n;
+  int p;
+  row_geometry(a, t, n, p);
+  const int k = a.k;
+  const float* row = a.scores + t * a.stride;
+  int32_t* oi = a.idx + t * (int64_t)k;
+  float* os = a.score ? a.score + t * (int64_t)k : nullptr;
+  const int32_t* imap = a.imap ? a.imap + t * (int64_t)a.kc : nullptr;
+
+  if (n <= k) {
+    for (int j = tid; j < k; j += kTopkThreads) {
+      if (j < n) {
+        int32_t id;
+        float sc;
+        out_entry(a, imap, p, j, score_key(row[j]), id, sc);
+        oi[j] = id;
+        if (os) os[j] = sc;
+      } else {
+        oi[j] = -1;
+        if (os) os[j] = 0.f;
+      }
+    }
+    return;
+  }
+
+  // ---- every request at once: the keys and (gather rows) their token ids
+  const int64_t base = (int64_t)wave * 64 * EPT + lane;
+  auto in_row = [&](int j) { return base + 64 * j < n; };
+  uint32_t u[EPT];
+  int32_t ids[kPrefetchIds ? EPT : 1];
+  {
+    float v[EPT];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int64_t e = base + 64 * j;
+      v[j] = row[e < n ? e : 0];
+      if constexpr (kPrefetchIds) ids[j] = imap[e < n ? e : 0];
+    }
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) u[j] = score_key(v[j]);
+  }
+  radix_clear(rs);
+  // ---- key range of the row (element 0 exists, so it stands in for the tail)
+  uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const uint32_t x = in_row(j) ? u[j] : u[0];
+    lo = min(lo, x);
+    hi = max(hi, x);
+  }
+  block_minmax(lo, hi, wmin, wmax);
+  const int nbits = hi == lo ? 0 : 32 - __clz(hi - lo);
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) u[j] -= lo;   // v = key - min; slots past the row are never visited
+
+  uint32_t prefix, pmask, krem = (uint32_t)k;
+  bool full;
+  radix_select(
+      [&](auto&& f) {
+#pragma unroll
+        for (int j = 0; j < EPT; ++j)
+          if (in_row(j)) f(u[j]);
+      },
+      nbits, prefix, pmask, krem, full, rs);
+
+  // ---- index-ordered compaction: values above the prefix, then the first krem equal to it
+  auto is_gt = [&](int j) { return in_row(j) && (u[j] & pmask) > prefix; };
+  auto is_eq = [&](int j) { return in_row(j) && (u[j] & pmask) == prefix; };
+  uint32_t cgt = 0, ceq = 0;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    cgt += (uint32_t)__popcll(__ballot(is_gt(j)));
+    ceq += (uint32_t)__popcll(__ballot(is_eq(j)));
+  }
+  if (lane == 0) {
+    wgt[wave] = cgt;
+    weq[wave] = ceq;
+  }
+  __syncthreads();
+  uint32_t eq_run = 0, sel_run = 0;
+  for (int ww = 0; ww < wave; ++ww) {
+    const uint32_t take = eq_run >= krem ? 0u : min(weq[ww], krem - eq_run);
+    sel_run += wgt[ww] + take;
+    eq_run += weq[ww];
+  }
+  const uint64_t lt = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const bool gt = is_gt(j);
+    const bool eq = is_eq(j);
+    const uint64_t meq = __ballot(eq);
+    const uint32_t eq_rank = eq_run + (uint32_t)__popcll(meq & lt);
+    const bool sel = gt || (eq && eq_rank < krem);
+    const uint64_t msel = __ballot(sel);
+    const uint32_t pos = sel_run + (uint32_t)__popcll(msel & lt);
+    if (sel && pos < (uint32_t)k) {
+      int32_t id = (int32_t)(base + 64 * j);
+      float sc = key_score(u[j] + lo);
+      if constexpr (GATHER) {
+        int32_t v;
+        if constexpr (kPrefetchIds) v = ids[j];
+        else v = imap[base + 64 * j];
+        const bool ok = v >= 0 && v < p;
+        id = ok ? v : -1;
+        sc = ok ? sc : 0.f;
+      }
+      oi[pos] = id;
+      if (os) os[pos] = sc;
+    }
+    eq_run += (uint32_t)__popcll(meq);
+    sel_run += (uint32_t)__popcll(msel);
+  }
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(256) void zero_kernel(uint32_t* __restrict__ p, int64_t words) {
@@ -221,8 +353,25 @@ hipError_t launch_zero(uint32_t* p, int64_t words, hipStream_t st) {
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   if (a.T == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)a.T), dim3(kTopkThreads), 0, st, a);
+  const int64_t max_len = a.imap ? a.kc : a.Lmax;
+  const dim3 grid((unsigned)a.T), block(kTopkThreads);
+#define MISA_TOPK_REG(EPT_)                                                     \
+  if (max_len <= (EPT_) * kTopkThreads) {                                       \
+    if (a.imap)                                                                 \
+      hipLaunchKernelGGL((topk_row_reg_kernel<EPT_, true>), grid, block, 0, st, a);  \
+    else                                                                        \
+      hipLaunchKernelGGL((topk_row_reg_kernel<EPT_, false>), grid, block, 0, st, a); \
+    return hipGetLastError();                                                   \
+  }
+  MISA_TOPK_REG(4)
+  MISA_TOPK_REG(8)
+  MISA_TOPK_REG(16)
+  MISA_TOPK_REG(32)
+#undef MISA_TOPK_REG
+  hipLaunchKernelGGL(topk_row_kernel, grid, block, 0, st, a);
   return hipGetLastError();
 }
+
+int64_t topk_row_reg_max() { return 32 * kTopkThreads; }
 
 }  // namespace misa

@@ -1,41 +1,59 @@
 // Split per-query top-k for few, long score rows (decode: a handful of queries
 // over 10^4..10^6 tokens), where one workgroup per row would leave the chip idle.
 //
-// Same selection rule as the per-row kernel (MISA pages: the indexer keeps the
+// Same selection rule as the per-row kernels (MISA pages: the indexer keeps the
 // top-k tokens of each query; order by score descending, token index
-// ascending; output in ascending token index, -1 padded), computed by three
-// launches over (row, chunk) grids:
+// ascending; output in ascending token index, -1 padded), computed by launches
+// over (row, chunk) grids:
 //   1. hist     each chunk adds its LDS histogram of the key's top 12 bits into
-//               the row's global histogram (atomics).
+//               the row's global histogram (atomics; the decode scoring kernel
+//               usually builds it instead).
 //   2. filter   each chunk reads the finished histogram, finds the threshold
-//               bin b1 (and how many of it are kept), counts its keys above b1
-//               and appends the keys of bin b1 (key, index) to the row's list.
-//   3. compact  each chunk resolves the exact k-th key u* on the candidate list
-//               (12 + 8 more bits), derives its output offset from the counts of
-//               the chunks before it, and writes its selected indices in index
-//               order (ballots inside waves, counts across waves).
-// No workgroup waits for or signals another inside a launch: on gfx950 the L2
-// of each XCD is not coherent with the others within a kernel, so everything a
-// chunk needs from other chunks comes from an earlier launch (global atomics
-// for the histogram and the list cursor).
+//               bin b1, counts its keys above b1 and appends the keys of bin b1
+//               (key, index) to the row's candidate list. The last chunk of the
+//               row to finish resolves the exact threshold key among the
+//               candidates and turns the per-chunk counts into per-chunk output
+//               offsets.
+//   3. compact  each chunk writes its kept indices in index order from its
+//               offset (ballots inside waves, counts across waves).
+// Within a launch, chunks hand data to the last one through device-coherent
+// stores (sc1: written through to memory, which every XCD's loads with sc1
+// see) completed before an atomic arrival count; the L2 write-back fence that a
+// release would add costs more than the whole selection on gfx950.
 #include "misa_common.hpp"
 #include "misa_internal.hpp"
 #include "misa_score_dev.hpp"
+#include "misa_select.hpp"
 
 namespace misa {
 namespace {
 
-constexpr int kThreads = 1024;               // 16 waves: four per SIMD hide LDS and barrier latency
+constexpr int kThreads = kSelThreads;       // 16 waves: four per SIMD hide LDS and barrier latency
 constexpr int kWaves = kThreads / 64;
-constexpr int kBins = 4096;
+constexpr int kBins = kSelBins;
 constexpr int kMaxChunks = 1024;
-constexpr int kSpec = 4;                     // candidate entries each thread requests before knowing m
-constexpr int kCandCap = kSpec * kThreads;   // candidates held in LDS
+constexpr int kCandReg = 8 * kThreads;       // candidates the last chunk holds in registers
 
-// state[t][*]: written by chunk 0 of the filter launch
-enum { ST_B1 = 0, ST_KREM1 = 1, ST_M = 2 };
-// counter[t][*]
-enum { CT_CAND = 0 };
+// state[t][*]: written by the last chunk of the filter launch
+enum { ST_THR = 0, ST_KREM = 1 };
+// counter[t][*] (zero on entry)
+enum { CT_CAND = 0, CT_DONE = 1 };
+
+__device__ __forceinline__ void store_coherent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_coherent(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_coherent(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until this thread's stores have completed (for the sc1 stores above:
+// reached memory).
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ int64_t row_len_of(const TopkArgs& a, int64_t t, int& p) {
   p = query_prefix_len(a.q_seq, a.q_len, a.nseq, a.Lmax, t);
@@ -58,68 +76,6 @@ __device__ __forceinline__ void out_entry(const int32_t* imap, int p, int64_t e,
     id = (int32_t)e;
     sc = key_score(u);
   }
-}
-
-// Sum over the workgroup (every thread gets it).
-__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* wsum) {
-  v = wave_sum(v);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) wsum[wave] = v;
-  __syncthreads();
-  uint32_t tot = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) tot += wsum[w];
-  __syncthreads();
-  return tot;
-}
-
-// Exclusive prefix sum over the workgroup's threads (ascending thread id).
-__device__ __forceinline__ uint32_t excl_scan(uint32_t v, uint32_t* wsum) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t inc = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_up(inc, off, kWave);
-    if (lane >= off) inc += o;
-  }
-  if (lane == 63) wsum[wave] = inc;
-  __syncthreads();
-  uint32_t pre = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) pre += w < wave ? wsum[w] : 0u;
-  __syncthreads();
-  return pre + inc - v;
-}
-
-// Digit d of an NB-bin histogram (scanned from the top) at which the running
-// count reaches krem: count(bins > d) < krem <= count(bins >= d). Every thread
-// returns the same (digit, krem - count(bins > d)).
-template <int NB>
-__device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t krem, uint32_t* wsum, uint32_t* sh,
-                                           uint32_t& digit, uint32_t& krem_out) {
-  constexpr int PER = NB >= kThreads ? NB / kThreads : 1;
-  const int tid = threadIdx.x;
-  uint32_t c[PER];
-  uint32_t mine = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int b = PER * tid + j;
-    c[j] = b < NB ? hist[NB - 1 - b] : 0u;
-    mine += c[j];
-  }
-  uint32_t above = excl_scan(mine, wsum);
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    if (above < krem && above + c[j] >= krem) {
-      sh[0] = (uint32_t)(NB - 1 - (PER * tid + j));
-      sh[1] = krem - above;
-    }
-    above += c[j];
-  }
-  __syncthreads();
-  digit = sh[0];
-  krem_out = sh[1];
-  __syncthreads();
 }
 
 // The chunk of a workgroup is kThreads * EPT consecutive scores; wave w owns the
@@ -168,13 +124,26 @@ __global__ __launch_bounds__(kThreads) void split_hist_kernel(TopkArgs a, SplitT
 
 // Every chunk finds the row's threshold bin b1 from the finished histogram,
 // counts its keys above b1 and appends the keys of bin b1 (key, index) to the
-// row's candidate list (one cursor reservation per workgroup).
+// row's candidate list (one cursor reservation per workgroup). The last chunk
+// of the row to arrive then
+//   - resolves the threshold key thr among the candidates: a radix select on
+//     the candidates' low 20 bits, relative to their minimum (all of them share
+//     the top 12 bits b1), and how many keys equal to thr are kept (krem; all
+//     of them when the select ended on a bin kept whole);
+//   - counts the kept candidates of every chunk, and writes each chunk's output
+//     offset (keys kept in the chunks before it) and the number of keys equal
+//     to thr in front of it, for the compaction launch.
 template <int EPT>
 __global__ __launch_bounds__(kThreads) void split_filter_kernel(TopkArgs a, SplitTopkWs w) {
   __shared__ uint32_t lh[kBins];
-  __shared__ uint32_t wsum[kWaves];
   __shared__ uint32_t sh[4];
+  __shared__ uint32_t wsum[kWaves];
   __shared__ uint32_t wcnt[kWaves], wdef[kWaves], wbase[kWaves];
+  __shared__ uint32_t s_last;
+  // the last chunk only
+  __shared__ RadixScratch rs;
+  __shared__ uint32_t wmin[kWaves], wmax[kWaves], wsum2[3][kWaves];
+  __shared__ uint32_t cgt[kMaxChunks], ceq[kMaxChunks];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t = blockIdx.y;
   const int c = blockIdx.x;
@@ -188,14 +157,8 @@ __global__ __launch_bounds__(kThreads) void split_filter_kernel(TopkArgs a, Spli
   const uint32_t* gh = w.hist + t * kBins;
   for (int i = tid; i < kBins; i += kThreads) lh[i] = gh[i];
   __syncthreads();
-  uint32_t b1, krem1;
-  find_digit<kBins>(lh, (uint32_t)a.k, wsum, sh, b1, krem1);
-  if (c == 0 && tid == 0) {
-    uint32_t* st = w.state + t * 8;
-    st[ST_B1] = b1;
-    st[ST_KREM1] = krem1;
-    st[ST_M] = lh[b1];
-  }
+  find_threshold(lh, kBins, (uint32_t)a.k, wsum, sh);
+  const uint32_t b1 = sh[0], krem1 = sh[1], m_all = lh[b1];
   uint32_t ndef = 0, ncand = 0;
   uint64_t mk[EPT];
 #pragma unroll
@@ -218,66 +181,168 @@ __global__ __launch_bounds__(kThreads) void split_filter_kernel(TopkArgs a, Spli
       nd += wdef[ww];
     }
     uint32_t b = tot ? atomicAdd(w.counter + t * 4 + CT_CAND, tot) : 0u;
+    store_coherent(reinterpret_cast<uint64_t*>(w.seg) + t * w.nchunk + c, ((uint64_t)tot << 32) | b);
     for (int ww = 0; ww < kWaves; ++ww) {
       wbase[ww] = b;
       b += wcnt[ww];
     }
-    w.ndef[t * w.nchunk + c] = nd;
+    store_coherent(w.ndef + t * w.nchunk + c, nd);
   }
   __syncthreads();
-  uint2* cand = reinterpret_cast<uint2*>(w.cand) + t * w.cap;
+  uint64_t* cand = reinterpret_cast<uint64_t*>(w.cand) + t * w.cap;
   const uint64_t lt = (1ull << lane) - 1ull;
   uint32_t run = wbase[wave];
   const int64_t base = e0 + (int64_t)wave * 64 * EPT + lane;
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
     const uint32_t pos = run + (uint32_t)__popcll(mk[j] & lt);
-    if (((mk[j] >> lane) & 1ull) && pos < (uint32_t)w.cap) cand[pos] = uint2{u[j], (uint32_t)(base + 64 * j)};
+    if (((mk[j] >> lane) & 1ull) && pos < (uint32_t)w.cap)
+      store_coherent(cand + pos, ((uint64_t)(uint32_t)(base + 64 * j) << 32) | u[j]);
     run += (uint32_t)__popcll(mk[j]);
   }
+  // ---- arrival: this chunk's list entries and count are in memory before it counts
+  wait_stores();
+  __syncthreads();
+  const int nact = (int)((n + kThreads * EPT - 1) / (kThreads * EPT));
+  if (tid == 0) {
+    const uint32_t before =
+        __hip_atomic_fetch_add(w.counter + t * 4 + CT_DONE, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = before == (uint32_t)(nact - 1) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!s_last) return;
+
+  // ---- the last chunk: exact threshold among the m candidates of bin b1.
+  // Thread i holds list entries 8i .. 8i + 7, so that per-chunk counts are
+  // differences of one prefix sum over the list order (each chunk appended its
+  // candidates as one run).
+  const uint32_t m = m_all < (uint32_t)w.cap ? m_all : (uint32_t)w.cap;
+  const bool inreg = m <= (uint32_t)kCandReg;
+  uint64_t cv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t i = (uint32_t)(8 * tid + j);
+    cv[j] = (inreg && i < m) ? load_coherent(cand + i) : 0ull;
+  }
+  uint32_t nd_c = 0;
+  uint64_t sg = 0;
+  if (tid < nact) {
+    nd_c = load_coherent(w.ndef + t * w.nchunk + tid);
+    sg = load_coherent(reinterpret_cast<const uint64_t*>(w.seg) + t * w.nchunk + tid);
+  }
+  // visit(f): f(key, index) for each of this thread's candidates
+  auto visit = [&](auto&& f) {
+    if (inreg) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if ((uint32_t)(8 * tid + j) < m) f((uint32_t)cv[j], (uint32_t)(cv[j] >> 32));
+    } else {
+      for (uint32_t i = tid; i < m; i += kThreads) {
+        const uint64_t x = load_coherent(cand + i);
+        f((uint32_t)x, (uint32_t)(x >> 32));
+      }
+    }
+  };
+  radix_clear(rs);
+  if (!inreg)
+    for (int i = tid; i < kMaxChunks; i += kThreads) {
+      cgt[i] = 0;
+      ceq[i] = 0;
+    }
+  uint32_t lo = 0xfffffu, hi = 0u;
+  visit([&](uint32_t key, uint32_t) {
+    lo = min(lo, key & 0xfffffu);
+    hi = max(hi, key & 0xfffffu);
+  });
+  block_minmax(lo, hi, wmin, wmax);
+  const int nbits = hi <= lo ? 0 : 32 - __clz(hi - lo);
+  uint32_t prefix, pmask, krem = krem1;
+  bool full;
+  radix_select([&](auto&& f) { visit([&](uint32_t key, uint32_t) { f((key & 0xfffffu) - lo); }); }, nbits, prefix,
+               pmask, krem, full, rs);
+  // kept: keys > thr, and krem keys == thr (all of them when the bin was kept whole)
+  const uint32_t thr = (b1 << 20) | (lo + prefix);
+  const uint32_t krem_eq = full ? krem : 0xffffffffu;
+  // ---- kept candidates of every chunk (keys above thr, keys equal to thr)
+  uint32_t gt_c = 0, eq_c = 0;
+  if (inreg) {
+    // prefix over the list of (above << 16 | equal), m <= 8192 keeps both
+    // halves below 2^16; the radix histograms are free again and hold it
+    uint32_t* P = &rs.hist[0][0];
+    uint32_t loc[8], run = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t key = (uint32_t)cv[j];
+      const bool ok = (uint32_t)(8 * tid + j) < m;
+      run += ok ? (((key > thr) ? 1u << 16 : 0u) | (key == thr ? 1u : 0u)) : 0u;
+      loc[j] = run;
+    }
+    uint32_t tot;
+    const uint32_t pre = block_excl_scan(run, wsum2[0], tot);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if ((uint32_t)(8 * tid + j) < m) P[8 * tid + j] = pre + loc[j];
+    __syncthreads();
+    if (tid < nact) {
+      const uint32_t start = (uint32_t)sg, cnt = (uint32_t)(sg >> 32);
+      const uint32_t hiv = cnt ? P[start + cnt - 1] : 0u, lov = (cnt && start) ? P[start - 1] : 0u;
+      gt_c = nd_c + ((hiv - lov) >> 16);
+      eq_c = (hiv - lov) & 0xffffu;
+    }
+  } else {
+    // long lists: one LDS atomic per (wave, chunk) group of list entries
+    constexpr int CH = kThreads * EPT;
+    auto count_chunks = [&](uint64_t x, bool valid) {   // called by the whole wave
+      const uint32_t key = (uint32_t)x;
+      const int cc = valid ? (int)((uint32_t)(x >> 32) / CH) : -1;
+      const uint64_t mg = __ballot(valid && key > thr), mq = __ballot(valid && key == thr);
+      uint64_t pending = __ballot(valid);
+      while (pending) {
+        const int leader = __ffsll((unsigned long long)pending) - 1;
+        const int lc = __builtin_amdgcn_readlane(cc, leader);
+        const uint64_t mask = __ballot(cc == lc) & pending;
+        if (lane == leader) {
+          const uint32_t ng = (uint32_t)__popcll(mg & mask), nq = (uint32_t)__popcll(mq & mask);
+          if (ng) atomicAdd(&cgt[lc], ng);
+          if (nq) atomicAdd(&ceq[lc], nq);
+        }
+        pending &= ~mask;
+      }
+    };
+    for (uint32_t b0 = 0; b0 < m; b0 += kThreads) {
+      const uint32_t i = b0 + tid;
+      count_chunks(i < m ? load_coherent(cand + i) : 0ull, i < m);
+    }
+    __syncthreads();
+    if (tid < nact) {
+      gt_c = nd_c + cgt[tid];
+      eq_c = ceq[tid];
+    }
+  }
+  uint32_t eq_before;
+  const uint32_t gt_before = block_excl_scan2(gt_c, eq_c, &wsum2[1][0], eq_before);
+  if (tid < nact) {
+    w.selb[t * w.nchunk + tid] = gt_before + (eq_before < krem_eq ? eq_before : krem_eq);
+    w.eqb[t * w.nchunk + tid] = eq_before;
+  }
+  if (tid == 0) {
+    w.state[t * 8 + ST_THR] = thr;
+    w.state[t * 8 + ST_KREM] = krem_eq;
+  }
 }
 
-// Visit the m candidates of a row (cached in LDS, or read from global memory
-// 8 per thread per round with all loads issued first).
-template <typename F>
-__device__ __forceinline__ void for_candidates(const uint2* gl, const uint2* lds, uint32_t m, F&& f) {
-  if (lds) {
-    for (uint32_t i = threadIdx.x; i < m; i += kThreads) {
-      const uint2 v = lds[i];
-      f(v.x, v.y);
-    }
-    return;
-  }
-  for (uint32_t b = 0; b < m; b += 8 * kThreads) {
-    uint2 v[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint32_t i = b + q * kThreads + threadIdx.x;
-      v[q] = i < m ? gl[i] : uint2{0u, 0xffffffffu};
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (v[q].y != 0xffffffffu) f(v[q].x, v[q].y);
-  }
-}
-
-// Every chunk resolves the row's exact k-th key u* from the candidate list
-// (three more digits: bits 19..12, 11..4, 3..0), counts the selected keys in
-// front of it (keys above b1 from the filter's per-chunk counts, plus the
-// candidates above / equal to u* with a lower index), then writes its selected
-// indices in index order.
+// Every chunk writes its kept indices in index order: the keys above the row's
+// threshold key thr, and of the keys equal to thr those ranked (in index
+// order) below krem. Its output offset and the number of keys equal to thr in
+// front of it come from the filter's last chunk.
 // RESCORE (the coarse pass of the fused MISA† pipeline): the kept tokens of the
 // chunk are then scored with all H heads (D-dim keys, RT row tiles) into the
-// candidate-slot score row r.scores, and the re-rank's level-1 histogram of
-// those scores is accumulated into r.hist; slots beyond a short prefix are
-// marked -1 / -inf.
+// candidate-slot score row r.scores (and, with r.hist, the re-rank's level-1
+// histogram of those scores); slots beyond a short prefix are marked -1 / -inf.
 template <int EPT, int D, int RT, bool RESCORE>
 __global__ __launch_bounds__(kThreads) void split_compact_kernel(TopkArgs a, SplitTopkWs w, RescoreArgs r) {
-  __shared__ uint32_t lh[kBins];
-  __shared__ uint32_t wsum[kWaves];
-  __shared__ uint32_t sh[4];
+  __shared__ uint32_t lh[RESCORE ? kBins : 1];
   __shared__ uint32_t wgt[kWaves], weq[kWaves], wend[kWaves];
-  __shared__ uint2 ccache[kCandCap];
   __shared__ int s_tok[RESCORE ? kThreads * EPT : 1];
   constexpr int LDQ = D + 8;   // padded row stride of the staged query rows (bf16)
   __shared__ __attribute__((aligned(16))) uint16_t s_q[RESCORE ? 16 * RT * LDQ : 8];
@@ -309,14 +374,13 @@ __global__ __launch_bounds__(kThreads) void split_compact_kernel(TopkArgs a, Spl
       *reinterpret_cast<u32x4*>(s_q + rr * LDQ + cc) = v;
     }
     if (tid < 16 * RT) s_w[tid] = tid < r.H ? r.w[t * r.H + tid] : 0.f;
+    if (r.hist)
+      for (int i = tid; i < kBins; i += kThreads) lh[i] = 0;
   }
   uint32_t off = 0, nsel = 0;
 
   if (n <= a.k) {
     const int64_t e1 = min(e0 + CH, n);
-    if constexpr (RESCORE) {
-      for (int i = tid; i < kBins; i += kThreads) lh[i] = 0;
-    }
     for (int64_t e = e0 + tid; e < e1; e += kThreads) {
       int32_t id;
       float sc;
@@ -336,71 +400,18 @@ __global__ __launch_bounds__(kThreads) void split_compact_kernel(TopkArgs a, Spl
       if (os) os[j] = 0.f;
       if constexpr (RESCORE) {
         r.scores[t * (int64_t)a.k + j] = -INFINITY;
-        atomicAdd(&lh[score_key(-INFINITY) >> 20], 1u);
+        if (r.hist) atomicAdd(&lh[score_key(-INFINITY) >> 20], 1u);
       }
     }
     if constexpr (!RESCORE) return;
   } else {
     if (e0 >= n) return;
-    // ---- everything independent is requested at once
     const uint32_t* st = w.state + t * 8;
-    const uint32_t b1 = st[ST_B1], m_all = st[ST_M];
-    uint32_t krem = st[ST_KREM1];
-    const uint32_t nd_mine = tid < c ? w.ndef[t * w.nchunk + tid] : 0u;
-    const uint2* gcand = reinterpret_cast<const uint2*>(w.cand) + t * w.cap;
-    uint2 spec[kSpec];
-#pragma unroll
-    for (int q = 0; q < kSpec; ++q) spec[q] = gcand[q * kThreads + tid];   // within the list's capacity
+    const uint32_t ustar = st[ST_THR], krem = st[ST_KREM];
+    const uint32_t sel_before = w.selb[t * w.nchunk + c], eq_before = w.eqb[t * w.nchunk + c];
     uint32_t u[EPT];
     bool in[EPT];
     load_chunk<EPT>(row, e0, n, u, in);
-    const uint32_t m = min(m_all, (uint32_t)w.cap);
-    const uint2* lds = nullptr;
-    if (m <= (uint32_t)kCandCap) {
-#pragma unroll
-      for (int q = 0; q < kSpec; ++q)
-        if ((uint32_t)(q * kThreads + tid) < m) ccache[q * kThreads + tid] = spec[q];
-      lds = ccache;
-    }
-    for (int i = tid; i < 256; i += kThreads) lh[i] = 0;
-    __syncthreads();
-    // ---- exact k-th key: digits 19..12, 11..4, 3..0 on the candidates (all share b1)
-    uint32_t prefix = b1 << 20, pmask = 0xfff00000u;
-    const int shifts[3] = {12, 4, 0};
-    const uint32_t masks[3] = {0xffu, 0xffu, 0xfu};
-#pragma unroll
-    for (int lv = 0; lv < 3; ++lv) {
-      const int shift = shifts[lv];
-      const uint32_t dm = masks[lv];
-      for_candidates(gcand, lds, m, [&](uint32_t uu, uint32_t) {
-        if ((uu & pmask) == prefix) atomicAdd(&lh[(uu >> shift) & dm], 1u);
-      });
-      __syncthreads();
-      uint32_t dg, kr;
-      if (lv < 2) find_digit<256>(lh, krem, wsum, sh, dg, kr);
-      else find_digit<16>(lh, krem, wsum, sh, dg, kr);
-      prefix |= dg << shift;
-      pmask |= dm << shift;
-      krem = kr;
-      for (int i = tid; i < 256; i += kThreads) lh[i] = 0;
-      __syncthreads();
-    }
-    const uint32_t ustar = prefix;   // the k-th key; krem keys equal to it are kept (lowest indices)
-    // ---- selected keys in front of this chunk
-    uint32_t gtb = 0, eqb = 0;
-    for_candidates(gcand, lds, m, [&](uint32_t uu, uint32_t e) {
-      if ((int64_t)e < e0) {
-        gtb += uu > ustar ? 1u : 0u;
-        eqb += uu == ustar ? 1u : 0u;
-      }
-    });
-    const uint32_t gt_before = block_sum(gtb, wsum);
-    const uint32_t eq_before = block_sum(eqb, wsum);
-    const uint32_t nd_before = block_sum(nd_mine, wsum);
-    const uint32_t sel_before = nd_before + gt_before + (eq_before < krem ? eq_before : krem);
-    if constexpr (RESCORE) {
-      for (int i = tid; i < kBins; i += kThreads) lh[i] = 0;   // the re-rank histogram from here on
-    }
     // ---- compaction of this chunk (from registers)
     uint32_t cgt = 0, ceq = 0;
 #pragma unroll
@@ -456,13 +467,14 @@ __global__ __launch_bounds__(kThreads) void split_compact_kernel(TopkArgs a, Spl
     float* rrow = r.scores + t * (int64_t)a.k;
     for (int b = wave * 16; b < (int)nsel; b += kWaves * 16) {
       KeyTiles<D, 1> tile;
-      load_key_tiles<D, 1>(kseq, b, (int)nsel, col, [&](int s) { return s_tok[s]; }, tile);
+      load_key_tiles<D, 1>(kseq, b, (int)nsel, col, [&](int s) { return s_tok[s]; }, 0, tile);
       const float v = score_one_tile_lds<D, RT>(s_q, LDQ, s_w, tile, grp, col);
       if (grp == 0 && b + col < (int)nsel) {
         rrow[off + b + col] = v;
-        atomicAdd(&lh[score_key(v) >> 20], 1u);
+        if (r.hist) atomicAdd(&lh[score_key(v) >> 20], 1u);
       }
     }
+    if (!r.hist) return;
     __syncthreads();
     uint32_t* gh = r.hist + t * kBins;
     for (int i = tid; i < kBins; i += kThreads)
@@ -480,19 +492,19 @@ inline size_t al(size_t x) { return (x + 255) / 256 * 256; }
 }  // namespace
 
 bool use_split_topk(int64_t T, int64_t max_len) {
-  // rows of up to 12288 scores are selected from LDS by one workgroup each
-  return T <= 4096 && max_len > 12288 && max_len <= (int64_t)kMaxChunks * kThreads * 4;
+  // shorter rows are selected by one workgroup each, out of registers
+  return T <= 4096 && max_len > topk_row_reg_max() && max_len <= (int64_t)kMaxChunks * kThreads * 4;
 }
 
 int64_t split_topk_zero_words(int64_t T) { return (int64_t)(al((size_t)T * (kBins + 4) * 4) / 4); }
 
-inline int64_t cand_cap(int64_t max_len) { return max_len > kCandCap ? max_len : kCandCap; }
+inline int64_t cand_cap(int64_t max_len) { return max_len; }
 
 size_t split_topk_ws_bytes(int64_t T, int64_t max_len) {
   const int chunk = split_chunk(max_len);
   const int64_t nchunk = (max_len + chunk - 1) / chunk;
   return al((size_t)T * (kBins + 4) * 4) + al((size_t)T * 8 * 4) + 3 * al((size_t)T * nchunk * 4) +
-         al((size_t)T * cand_cap(max_len) * 8);
+         al((size_t)T * nchunk * 8) + al((size_t)T * cand_cap(max_len) * 8);
 }
 
 SplitTopkWs split_topk_carve(void* base, int64_t T, int64_t max_len) {
@@ -509,10 +521,12 @@ SplitTopkWs split_topk_carve(void* base, int64_t T, int64_t max_len) {
   p += al((size_t)T * 8 * 4);
   w.ndef = reinterpret_cast<uint32_t*>(p);
   p += al((size_t)T * w.nchunk * 4);
-  w.ccnt = reinterpret_cast<uint32_t*>(p);   // unused
+  w.selb = reinterpret_cast<uint32_t*>(p);
   p += al((size_t)T * w.nchunk * 4);
   w.eqb = reinterpret_cast<uint32_t*>(p);
   p += al((size_t)T * w.nchunk * 4);
+  w.seg = reinterpret_cast<uint32_t*>(p);
+  p += al((size_t)T * w.nchunk * 8);
   w.cand = reinterpret_cast<uint32_t*>(p);
   return w;
 }

@@ -21,8 +21,10 @@ CASES = {
     "c3r": ("c3", dict(L=2500, T=16, nseq=16, topk=300)),
     "c4r": ("c4", dict(L=5000, T=4, nseq=4, kc=1024, topk=256)),
     "c2r": ("c2", dict(L=700, T=700, topk=128)),
-    # rows above 12288 scores: the multi-workgroup (split) top-k
+    # rows of 16K..32K scores: the register-resident top-k at 32 keys per lane
     "c1s": ("c1", dict(L=20001, T=4, nseq=4, topk=1000)),
+    # rows above 32K scores: the multi-workgroup (split) top-k
+    "c1x": ("c1", dict(L=40001, T=4, nseq=4, topk=1000)),
     "c4s": ("c4", dict(L=40000, T=4, nseq=4, kc=4096, topk=512)),
 }
 MODES = ["gauss", "grid"]
@@ -267,6 +269,28 @@ def test_all_equal_scores_tie_break(case):
     idx, sc = M.dsa_index_dense(dev["q"], dev["w"], k0, dev["q_seq"], dev["q_len"], 100)
     assert torch.equal(idx.cpu(), torch.arange(100, dtype=torch.int32).repeat(4, 1))
     assert torch.all(sc == 0)
+
+
+@pytest.mark.parametrize("L", [3001, 20001, 40001])
+def test_mixed_sign_scores_exact(L):
+    """Head weights of both signs give negative, zero and positive scores over a
+    wide key range: every top-k path (register-resident rows, split rows, the
+    gathered re-rank) must order them as reals, bit-exact in grid mode."""
+    x = make_inputs("c1", mode="grid", L=L, T=4, nseq=4, topk=700)
+    x.w[:, 1::3] *= -1.0
+    x.w[:, 2::3] *= -2.0
+    dev = upload(x)
+    k = L // 4
+    idx, sc = M.dsa_index_dense(dev["q"], dev["w"], dev["k"], dev["q_seq"], dev["q_len"], k)
+    oi, ov = O.dsa_index_dense(x.q, x.w, x.k, x.q_seq, x.q_len, k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), oi)
+    np.testing.assert_array_equal(sc.cpu().numpy(), ov.astype(np.float32))
+    assert (ov < 0).any() and (ov > 0).any()   # the kept set spans both signs
+    cand = torch.from_numpy(np.ascontiguousarray(oi, dtype=np.int32)).cuda()
+    ri, rv = M.hier_rerank(dev["q"], dev["w"], dev["k"], cand, dev["q_seq"], dev["q_len"], 100)
+    oi2, ov2 = O.hier_rerank(x.q, x.w, x.k, oi, x.q_seq, x.q_len, 100)
+    np.testing.assert_array_equal(ri.cpu().numpy(), oi2)
+    np.testing.assert_array_equal(rv.cpu().numpy(), ov2.astype(np.float32))
 
 
 def test_rerank_skips_invalid_candidates():
