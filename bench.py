@@ -47,7 +47,42 @@ def parse():
     ap.add_argument("--no-rows", action="store_true", help="skip the per-row timings")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of HIP-graph replays of the step")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run 5 plain device-to-device copies of 256 MiB (the reference kernel of known size "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+# HBM traffic of the scoring kernel from rocprofv3 counters (FETCH_SIZE, WRITE_SIZE,
+# scaled by a plain copy of known size), recorded in this summary together with a
+# hash of the kernel's sources; the figure is reported only while they still match.
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "score_decode_c4.md")
+KERNEL_SOURCES = ["score.hip", "misa_score_dev.hpp", "misa_common.hpp", "misa_internal.hpp"]
+
+
+def kernel_sources_sha256():
+    import hashlib
+    hsh = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "routed_token_indexer_amd", "csrc", f), "rb") as fh:
+            hsh.update(fh.read())
+    return hsh.hexdigest()
+
+
+def recorded_traffic(config_name):
+    """Bytes per launch measured for the scoring kernel, or None if not measured for
+    this workload or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_SUMMARY) as fh:
+            kv = dict(line.split(":", 1) for line in fh.read().splitlines()
+                      if line.startswith(("kernel_sources_sha256:", "traffic_bytes_per_launch:", "workload_config:")))
+    except OSError:
+        return None
+    if kv.get("workload_config", "").strip() != config_name:
+        return None
+    if kv.get("kernel_sources_sha256", "").strip() != kernel_sources_sha256():
+        return None
+    return int(kv["traffic_bytes_per_launch"].strip())
 
 
 def main():
@@ -64,6 +99,16 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        n = 256 << 20
+        src = torch.ones(n // 4, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device-to-device copy", "copies": 5, "bytes_read_per_copy": n,
+                          "bytes_written_per_copy": n}), flush=True)
+        return
     cfg = CONFIGS[args.config]
     t_gen = time.time()
     x = make_inputs(cfg, mode="gauss")
@@ -130,7 +175,8 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
-    # ---- eager timed region: K steps, the scoring kernel bracketed by HIP events on its stream
+    # ---- eager timed region: K steps; the scoring kernel's launches carry HIP events
+    # stamped at the kernel's own start and end (on its stream)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -187,7 +233,9 @@ def main():
         kernel_bytes = tokens * d * 2 + T * h * d * 2 + T * h * 4
         achieved = kernel_bytes / (per_launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(c.name),
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "algorithmic_bytes_per_launch": int(kernel_bytes)}
     roof["kernel"] = "score_kernel (routed token scoring, MFMA)"
     roof["avg_launch_us"] = round(per_launch_ms * 1e3, 2)
     roof["launches_per_step"] = score_launches_per_step

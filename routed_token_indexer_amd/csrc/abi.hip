@@ -134,6 +134,13 @@ void timing_after(int kid, hipStream_t st) {
   (void)hipEventRecord(g_timing.ev[2 * g_timing.n + 1], st);
   ++g_timing.n;
 }
+bool timing_take(int kid, hipEvent_t& start, hipEvent_t& stop) {
+  if (g_timing.kid != kid || g_timing.n >= g_timing.cap) return false;
+  start = g_timing.ev[2 * g_timing.n];
+  stop = g_timing.ev[2 * g_timing.n + 1];
+  ++g_timing.n;
+  return true;
+}
 }  // namespace misa
 
 extern "C" {
@@ -275,10 +282,7 @@ int32_t score_and_select(const char* fn, const void* q, const float* w, const vo
     if (e != hipSuccess) return hip_status(e, fn);
     if (!wide) a.hist = sw.hist;   // the decode scoring kernel builds the level-1 histogram
   }
-  const int kid = gather ? misa::KID_GATHER_SCORE : misa::KID_SCORE;
-  misa::timing_before(kid, st);
-  e = misa::launch_score(a, d, gather, wide, max_len, st);
-  misa::timing_after(kid, st);
+  e = misa::launch_score(a, d, gather, wide, max_len, st);   // timed by the launch itself
   if (e != hipSuccess) return hip_status(e, fn);
   if (!idx) return ok();
   misa::TopkArgs b{};
@@ -461,9 +465,7 @@ int32_t run_indexer(const char* fn, bool hier, const void* q, const float* w, co
   sa.nchunk_r = f.nchunk_r;
   sa.B = B;
   sa.heads_out = heads;
-  misa::timing_before(misa::KID_SCORE, st);
   e = misa::launch_score(sa, d, false, false, Lmax, st);
-  misa::timing_after(misa::KID_SCORE, st);
   if (e != hipSuccess) return hip_status(e, fn);
   // 3. top-k of the routed scores
   misa::TopkArgs b{};

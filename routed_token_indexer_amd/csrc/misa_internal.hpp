@@ -140,5 +140,8 @@ hipError_t launch_topk_split_rescore(const TopkArgs& a, const SplitTopkWs& w, co
 enum KernelId { KID_NONE = 0, KID_SCORE = 1, KID_TOPK = 2, KID_ROUTE = 3, KID_POOL = 4, KID_GATHER_SCORE = 5 };
 void timing_before(int kid, hipStream_t st);
 void timing_after(int kid, hipStream_t st);
+// Events for one launch of kernel class kid, stamped by the kernel's own start
+// and end (hipExtLaunchKernelGGL); false when that class is not being timed.
+bool timing_take(int kid, hipEvent_t& start, hipEvent_t& stop);
 
 }  // namespace misa

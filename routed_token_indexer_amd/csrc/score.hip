@@ -21,6 +21,8 @@
 //   wide kernel    a tile of consecutive queries of one sequence per workgroup
 //                  (causal prefill), so each key tile loaded serves the whole
 //                  query tile.
+#include <hip/hip_ext.h>
+
 #include "misa_common.hpp"
 #include "misa_internal.hpp"
 #include "misa_score_dev.hpp"
@@ -367,6 +369,18 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a) {
   }
 }
 
+// Launch, stamping the timing events at the kernel's own start and end when
+// the scoring kernels are being timed.
+template <typename K, typename... Args>
+hipError_t launch_timed(int kid, K kernel, dim3 grid, dim3 block, hipStream_t st, Args... args) {
+  hipEvent_t e0, e1;
+  if (timing_take(kid, e0, e1))
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, e0, e1, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+  return hipGetLastError();
+}
+
 template <int D, int RT, bool GATHER>
 hipError_t launch_decode(ScoreArgs a, int64_t max_len, hipStream_t st) {
   if (a.chunk <= 0) {
@@ -376,11 +390,9 @@ hipError_t launch_decode(ScoreArgs a, int64_t max_len, hipStream_t st) {
     a.chunk = (int)c;
   }
   dim3 grid((unsigned)((max_len + a.chunk - 1) / a.chunk), (unsigned)a.T);
-  if (a.hist)
-    hipLaunchKernelGGL((score_decode_kernel<D, RT, GATHER, true>), grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL((score_decode_kernel<D, RT, GATHER, false>), grid, dim3(256), 0, st, a);
-  return hipGetLastError();
+  const int kid = GATHER ? KID_GATHER_SCORE : KID_SCORE;
+  if (a.hist) return launch_timed(kid, score_decode_kernel<D, RT, GATHER, true>, grid, dim3(256), st, a);
+  return launch_timed(kid, score_decode_kernel<D, RT, GATHER, false>, grid, dim3(256), st, a);
 }
 
 template <int D>
@@ -405,8 +417,8 @@ hipError_t launch_decode_d(const ScoreArgs& a, bool gather, int64_t max_len, hip
 template <int D, int NHP, int RT, int KT, bool GATHER>
 hipError_t launch_cfg(const ScoreArgs& a, int64_t ntile, int nchunk, hipStream_t st) {
   dim3 grid(nchunk, (unsigned)ntile);
-  hipLaunchKernelGGL((score_kernel<D, NHP, RT, KT, GATHER>), grid, dim3(256), 0, st, a);
-  return hipGetLastError();
+  return launch_timed(GATHER ? KID_GATHER_SCORE : KID_SCORE, score_kernel<D, NHP, RT, KT, GATHER>, grid, dim3(256),
+                      st, a);
 }
 
 // Keys per workgroup: wide tiles (prefill) take 2048-key chunks; otherwise the
