@@ -22,6 +22,10 @@ __device__ __forceinline__ floatx4 mfma_16x16x32(const u32x4& a, const u32x4& b,
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// max(x, 0) as one instruction (the median of x, 0 and +inf); used by every
+// scoring path so that all of them round identically.
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, __builtin_inff()); }
+
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 

@@ -76,8 +76,8 @@ __device__ __forceinline__ float score_four_tiles(const u32x4 (&afrag)[RT][D / 3
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) acc = mfma_16x16x32(afrag[r][ks], tiles.b[kt][ks], acc);
-      part += wrow[r][0] * fmaxf(acc[0], 0.f) + wrow[r][1] * fmaxf(acc[1], 0.f) +
-              wrow[r][2] * fmaxf(acc[2], 0.f) + wrow[r][3] * fmaxf(acc[3], 0.f);
+      part += wrow[r][0] * relu(acc[0]) + wrow[r][1] * relu(acc[1]) +
+              wrow[r][2] * relu(acc[2]) + wrow[r][3] * relu(acc[3]);
     }
     part += __shfl_xor(part, 16, kWave);
     part += __shfl_xor(part, 32, kWave);
@@ -106,8 +106,8 @@ __device__ __forceinline__ float score_one_tile_lds(const uint16_t* s_q, int ldq
     for (int ks = 0; ks < D / 32; ++ks)
       acc = mfma_16x16x32(*reinterpret_cast<const u32x4*>(qa + ks * 32), tile.b[0][ks], acc);
     const float* wr = s_w + 16 * r + 4 * grp;
-    part += wr[0] * fmaxf(acc[0], 0.f) + wr[1] * fmaxf(acc[1], 0.f) + wr[2] * fmaxf(acc[2], 0.f) +
-            wr[3] * fmaxf(acc[3], 0.f);
+    part += wr[0] * relu(acc[0]) + wr[1] * relu(acc[1]) + wr[2] * relu(acc[2]) +
+            wr[3] * relu(acc[3]);
   }
   part += __shfl_xor(part, 16, kWave);
   part += __shfl_xor(part, 32, kWave);
@@ -124,7 +124,7 @@ __device__ __forceinline__ bool route_rank(int H, int h, int lane, float w, floa
   const bool active = lane < H;
   float rho;
   if (n_tail > 0) {
-    const float xt = fmaxf(x, 0.f);
+    const float xt = relu(x);
     rho = w * ((float)n_tail * A + xt);
     r = w * (A + xt / (float)n_tail);
   } else {

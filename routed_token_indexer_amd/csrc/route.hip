@@ -167,7 +167,7 @@ __device__ __forceinline__ void block_affinity(const RouteArgs& a, int64_t t, in
         acc = mfma_16x16x32(afrag[r][ks], blo[ks], acc);
       }
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) rs[r][jj] += fmaxf(acc[jj], 0.f);
+      for (int jj = 0; jj < 4; ++jj) rs[r][jj] += relu(acc[jj]);
     }
   }
   // sum over the 16 block columns (fixed xor tree)

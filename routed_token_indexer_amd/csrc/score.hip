@@ -44,133 +44,251 @@ __device__ __forceinline__ void query_info(const ScoreArgs& a, int64_t t, int& s
   n = p < 0 ? 0 : (p > a.Lmax ? (int)a.Lmax : p);
 }
 
-// Head id of row slot hs of query t (-1: padding row or invalid id).
-__device__ __forceinline__ int row_head(const ScoreArgs& a, int64_t t, int hs) {
-  if (hs >= a.hh) return -1;
-  const int g = a.heads ? a.heads[t * a.hh + hs] : hs;
-  return (g >= 0 && g < a.H) ? g : -1;
-}
-
-template <int D, int NHP, int RT, int KT, bool GATHER>
-__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
-  constexpr int QT = (16 * RT) / NHP;       // query slots of the tile
-  constexpr int KS = D / 32;                // 32-wide k-steps
-  // per-lane output slots: how many different slots one lane writes
-  constexpr int NOUT = NHP == 4 ? RT : (NHP == 8 ? RT : QT);
-  static_assert(QT >= 1 && (16 * RT) % NHP == 0, "row tiling");
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int col = lane & 15;                // MFMA column (key) / A row within a tile
-  const int grp = lane >> 4;                // lane group
-  const int64_t tile = (int64_t)gridDim.y - 1 - blockIdx.y;   // longest prefixes first
+// prefill: grid (key chunks, query tiles). A workgroup is 4 waves; wave w owns
+// the 16 * RT gathered head rows of QW consecutive queries, held as MFMA A
+// fragments for the whole launch. The workgroup's chunk of keys streams through
+// LDS in blocks of 64 keys, double buffered: one global load per key per
+// workgroup, and every wave multiplies each block into all of its rows.
+// Queries of several sequences in one tile are handled by one pass over the
+// keys per distinct sequence (rows of other sequences store nothing).
+template <int D, int NHP, int RT, int KB>
+__global__ __launch_bounds__(256, 2) void score_prefill_kernel(ScoreArgs a) {
+  constexpr int KS = D / 32;                  // 32-wide k-steps
+  constexpr int QW = (16 * RT) / NHP;         // queries per wave
+  constexpr int QT = 4 * QW;                  // queries per workgroup
+  // Row layout. Grouped (up to 16 rows per query, when a wave's tiles split evenly):
+  // tile r = M4 * i + f holds queries 4i .. 4i + 3 of the wave, row rho being head
+  // slot 4f + rho % 4 of query 4i + rho / 4, so the MFMA output rows 4g .. 4g + 3 of
+  // lane group g are 4 head slots of one query and its full head sum is a sum over
+  // f inside the lane (no cross-lane step; every lane stores). Otherwise rows run
+  // query-major (row R of the wave is slot R % NHP of query R / NHP) and the head
+  // sum crosses lane groups.
+  constexpr int M4 = NHP / 4;
+  constexpr bool GROUPED = NHP <= 16 && RT % M4 == 0;
+  constexpr int NOUT = GROUPED ? RT / M4 : (NHP <= 8 ? RT : QW);   // output slots of one lane
+  // KB: keys per LDS block
+  constexpr int LDK = D + 8;                  // LDS row stride (bf16): 16-byte pad against bank conflicts
+  constexpr int PPR = D / 8;                  // 16-byte pieces per key row
+  constexpr int LPT = KB * PPR / 256;         // pieces each thread moves per block
+  static_assert(QW >= 1 && (16 * RT) % NHP == 0 && LPT >= 1, "tiling");
+  constexpr int NROW = 4 * 16 * RT;           // head rows of the workgroup
+  __shared__ __attribute__((aligned(16))) uint16_t s_k[2][KB * LDK];
+  __shared__ __attribute__((aligned(16))) float s_w[NROW];   // row weights (0 for padding rows)
+  __shared__ int s_head[NROW];                                // row head ids (-1: padding row)
+  __shared__ int s_seq[QT], s_n[QT];
+  __shared__ int s_pseq[QT], s_pn[QT], s_np;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  // grid (tiles, chunks): consecutive workgroups take consecutive tiles of one
+  // chunk, so the round-robin spread over the XCDs mixes tiles of every length on
+  // every XCD (with the chunk as the fast index, one XCD would get every chunk-0
+  // workgroup and another only the few long tiles' last chunks)
+  const int64_t tile = (int64_t)gridDim.x - 1 - blockIdx.x;   // longest prefixes first
   const int64_t t0 = tile * QT;
+  const int chunk_id = blockIdx.y;
 
-  // ---- tile-wide slot info (indexed with compile-time indices only)
-  int slot_seq[QT], slot_n[QT];
-  int nmax = 0;
-#pragma unroll
-  for (int s = 0; s < QT; ++s) {
-    query_info(a, t0 + s, slot_seq[s], slot_n[s]);
-    nmax = max(nmax, slot_n[s]);
+  // query (within the workgroup) and head slot of workgroup row R
+  auto row_query = [&](int R) {
+    const int wv = R / (16 * RT), Rw = R % (16 * RT);
+    return wv * QW + (GROUPED ? 4 * ((Rw / 16) / M4) + (Rw % 16) / 4 : Rw / NHP);
+  };
+  auto row_slot = [&](int R) {
+    const int Rw = R % (16 * RT);
+    return GROUPED ? 4 * ((Rw / 16) % M4) + (Rw % 4) : Rw % NHP;
+  };
+
+  // ---- 1. query rows' sequences and lengths, raw head ids (all requested at once)
+  __shared__ int s_nmax, s_smin, s_smax;
+  if (tid == 0) {
+    s_nmax = 0;
+    s_smin = 0x7fffffff;
+    s_smax = -1;
   }
-  const int c_begin = blockIdx.x * a.chunk;
-  if (c_begin >= nmax) return;
-  const int c_end = min(c_begin + a.chunk, nmax);
+  constexpr int RPT = (NROW + 255) / 256;
+  int graw[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int R = tid + 256 * i;
+    const int64_t t = t0 + row_query(R);
+    const int hs = row_slot(R);
+    const int64_t tc = t < a.T ? t : 0;
+    const int hc = hs < a.hh ? hs : 0;
+    const int32_t* hp = a.heads ? a.heads + tc * a.hh + hc : a.q_seq + tc;
+    const int g = *hp;
+    graw[i] = (R < NROW && t < a.T && hs < a.hh) ? (a.heads ? g : hs) : -1;
+  }
+  int my_seq = -1, my_n = 0;
+  if (tid < QT) query_info(a, t0 + tid, my_seq, my_n);
+  __syncthreads();
+  if (tid < QT) {
+    s_seq[tid] = my_seq;
+    s_n[tid] = my_n;
+    if (my_seq >= 0) {
+      atomicMax(&s_nmax, my_n);
+      atomicMin(&s_smin, my_seq);
+      atomicMax(&s_smax, my_seq);
+    }
+  }
+  __syncthreads();
+  // a chunk past every prefix of the tile has nothing to do
+  const int c_begin = chunk_id * a.chunk;
+  if (c_begin >= s_nmax) return;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int R = tid + 256 * i;
+    if (R < NROW) {
+      const int g = graw[i];
+      s_head[R] = (s_seq[row_query(R)] >= 0 && g >= 0 && g < a.H) ? g : -1;
+    }
+  }
+  if (tid == 0) {
+    if (s_smin == s_smax) {   // one sequence: one pass over its keys
+      s_pseq[0] = s_smin;
+      s_pn[0] = s_nmax;
+      s_np = 1;
+    } else {                  // several: one pass per distinct sequence, each up to its longest prefix
+      int np = 0;
+      for (int i = 0; i < QT; ++i) {
+        const int sq = s_seq[i];
+        if (sq < 0) continue;
+        int j = 0;
+        while (j < np && s_pseq[j] != sq) ++j;
+        if (j == np) {
+          s_pseq[np] = sq;
+          s_pn[np] = 0;
+          ++np;
+        }
+        s_pn[j] = max(s_pn[j], s_n[i]);
+      }
+      s_np = np;
+    }
+  }
+  __syncthreads();
 
-  // ---- A fragments (gathered query rows) and row weights, loaded once
+  // ---- 2. A fragments of this wave's rows and the row weights (clamped, unconditional loads)
   u32x4 afrag[RT][KS];
-  float wrow[RT][4];
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
-    const int row = 16 * r + col;
-    const int64_t t = t0 + row / NHP;
-    int seq, n;
-    query_info(a, t, seq, n);
-    const int head = seq < 0 ? -1 : row_head(a, t, row % NHP);
-    const uint16_t* qp = a.q + ((t * a.H + (head < 0 ? 0 : head)) * D) + grp * 8;
+    const int R = wave * 16 * RT + 16 * r + col;
+    const int head = s_head[R];
+    const uint16_t* qp = a.q + ((head < 0 ? 0 : (t0 + row_query(R)) * a.H + head) * D) + grp * 8;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (head >= 0) v = *reinterpret_cast<const u32x4*>(qp + ks * 32);
-      afrag[r][ks] = v;
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row2 = 16 * r + 4 * grp + j;
-      const int64_t t2 = t0 + row2 / NHP;
-      int seq2, n2;
-      query_info(a, t2, seq2, n2);
-      const int hd = seq2 < 0 ? -1 : row_head(a, t2, row2 % NHP);
-      wrow[r][j] = hd < 0 ? 0.f : a.w[t2 * a.H + hd];
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + ks * 32);
+      afrag[r][ks] = head < 0 ? u32x4{0u, 0u, 0u, 0u} : v;
     }
   }
-
-  // ---- the slots this lane stores (slot index, its sequence and row length)
-  int out_slot[NOUT], out_seq[NOUT], out_n[NOUT];
+  float wv[RPT];
 #pragma unroll
-  for (int i = 0; i < NOUT; ++i) {
-    out_slot[i] = NHP == 4 ? 4 * i + grp : (NHP == 8 ? 2 * i + (grp >> 1) : i);
-    query_info(a, t0 + out_slot[i], out_seq[i], out_n[i]);
+  for (int i = 0; i < RPT; ++i) {
+    const int R = tid + 256 * i;
+    const int head = R < NROW ? s_head[R] : -1;
+    const float v = a.w[head < 0 ? 0 : (t0 + row_query(R)) * a.H + head];
+    wv[i] = head < 0 ? 0.f : v;
   }
-  const bool writer = NHP == 4 ? true : (NHP == 8 ? (grp & 1) == 0 : grp == 0);
+#pragma unroll
+  for (int i = 0; i < RPT; ++i)
+    if (tid + 256 * i < NROW) s_w[tid + 256 * i] = wv[i];
+  // the lane's output slot i is query out_q(i) of the workgroup (rows 4 * grp .. + 3 of
+  // each tile after the head sum); writer lanes hold each sum once
+  auto out_q = [&](int i) {
+    return wave * QW + (GROUPED ? 4 * i + grp : (NHP == 4 ? 4 * i + grp : (NHP == 8 ? 2 * i + (grp >> 1) : i)));
+  };
+  const bool writer = GROUPED || NHP == 4 ? true : (NHP == 8 ? (grp & 1) == 0 : grp == 0);
+  // weights of the lane's accumulator rows (4 * grp .. + 3 of each tile), kept in registers
+  __syncthreads();
+  floatx4 wreg[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) wreg[r] = *reinterpret_cast<const floatx4*>(&s_w[wave * 16 * RT + 16 * r + 4 * grp]);
+  // scores of the workgroup's query rows through a range-checked buffer view: a
+  // store outside a query's visible prefix (or chunk) goes to an offset past the
+  // view and is dropped, so the store needs no branch
+  const int64_t nrow_out = a.T - t0 < QT ? a.T - t0 : QT;
+  const auto oview = buffer_view(a.out + t0 * a.out_stride, (uint32_t)(nrow_out * a.out_stride * 4));
+  const int np = s_np;
 
-  // ---- one pass per distinct key source among the slots
+  for (int pi = 0; pi < np; ++pi) {
+    const int sq = s_pseq[pi];
+    if (c_begin >= s_pn[pi]) continue;
+    const int c_end = min(c_begin + a.chunk, s_pn[pi]);
+    const uint16_t* kseq = a.k + (int64_t)sq * a.Lmax * D;
+    const int nblk = (c_end - c_begin + KB - 1) / KB;
+    // per output slot: keys below lim are this lane's to store in this pass, at byte
+    // offset voff + 4 * key in the view
+    int lim[NOUT];
+    uint32_t voff[NOUT];
+    int lim_min = 0x7fffffff;
 #pragma unroll
-  for (int lead = 0; lead < QT; ++lead) {
-    if (slot_seq[lead] < 0) continue;
-    bool first = true;
+    for (int i = 0; i < NOUT; ++i) {
+      const int q = out_q(i);
+      lim[i] = (writer && s_seq[q] == sq) ? min(s_n[q], c_end) : 0;
+      lim_min = min(lim_min, lim[i]);
+      voff[i] = (uint32_t)((int64_t)q * a.out_stride * 4);
+    }
+    // blocks below every slot's limit store without masks (grouped rows only: there
+    // every lane is a writer)
 #pragma unroll
-    for (int s = 0; s < lead; ++s)
-      if (!GATHER && slot_seq[s] == slot_seq[lead]) first = false;
-    if (!first) continue;
-    int pass_n = 0;
+    for (int off = 32; off > 0; off >>= 1) lim_min = min(lim_min, __shfl_xor(lim_min, off, kWave));
+    // staging of one key block: thread pieces tid + 256 * i (row, 16-byte column)
+    auto load_block = [&](int b, u32x4 (&v)[LPT]) {
 #pragma unroll
-    for (int s = 0; s < QT; ++s)
-      if (s == lead || (!GATHER && slot_seq[s] == slot_seq[lead])) pass_n = max(pass_n, slot_n[s]);
-    const int p_end = min(c_end, pass_n);
-    const uint16_t* kseq = a.k + (int64_t)slot_seq[lead] * a.Lmax * D + grp * 8;
-    const int32_t* crow = GATHER ? a.cand + (t0 + lead) * a.kc : nullptr;
-    // which of this lane's output slots belong to this pass
-    bool in_pass[NOUT];
-#pragma unroll
-    for (int i = 0; i < NOUT; ++i)
-      in_pass[i] = writer && out_seq[i] >= 0 &&
-                   (GATHER ? out_slot[i] == lead : out_seq[i] == slot_seq[lead]);
-
-    for (int base = c_begin + wave * (16 * KT); base < p_end; base += 4 * 16 * KT) {
-      u32x4 bfrag[KT][KS];
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const int s = base + kt * 16 + col;
-        int64_t key = -1;
-        if (s < p_end) key = GATHER ? (int64_t)crow[s] : (int64_t)s;
-        const uint16_t* kp = kseq + (key < 0 ? 0 : key) * D;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          u32x4 v = {0u, 0u, 0u, 0u};
-          if (key >= 0) v = *reinterpret_cast<const u32x4*>(kp + ks * 32);
-          bfrag[kt][ks] = v;
-        }
+      for (int i = 0; i < LPT; ++i) {
+        const int pc = tid + 256 * i;
+        int s = c_begin + b * KB + pc / PPR;
+        s = s < a.Lmax ? s : (int)a.Lmax - 1;
+        v[i] = *reinterpret_cast<const u32x4*>(kseq + (int64_t)s * D + (pc % PPR) * 8);
       }
+    };
+    auto store_block = [&](uint16_t* buf, const u32x4 (&v)[LPT]) {
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
+      for (int i = 0; i < LPT; ++i) {
+        const int pc = tid + 256 * i;
+        *reinterpret_cast<u32x4*>(buf + (pc / PPR) * LDK + (pc % PPR) * 8) = v[i];
+      }
+    };
+    {
+      u32x4 v[LPT];
+      load_block(0, v);
+      store_block(s_k[0], v);
+    }
+    __syncthreads();
+    for (int b = 0; b < nblk; ++b) {
+      u32x4 nv[LPT];
+      load_block(b + 1 < nblk ? b + 1 : b, nv);   // the next block, requested before this one is used
+      const uint16_t* buf = s_k[b & 1];
+      const int base = c_begin + b * KB;
+      const bool unmasked = base + KB <= lim_min;
+#pragma unroll
+      for (int kt = 0; kt < KB / 16; ++kt) {
+        u32x4 bv[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          bv[ks] = *reinterpret_cast<const u32x4*>(buf + (kt * 16 + col) * LDK + grp * 8 + ks * 32);
+        // k-step outer: the RT accumulators are independent, so consecutive MFMAs
+        // never wait on each other's results
         floatx4 acc[RT];
 #pragma unroll
-        for (int r = 0; r < RT; ++r) {
-          acc[r] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int r = 0; r < RT; ++r) acc[r] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) acc[r] = mfma_16x16x32(afrag[r][ks], bfrag[kt][ks], acc[r]);
-        }
-        // epilogue: ReLU, head weight, per-query head sum (rows 4*grp..4*grp+3 of each tile)
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int r = 0; r < RT; ++r) acc[r] = mfma_16x16x32(afrag[r][ks], bv[ks], acc[r]);
         float part[RT];
 #pragma unroll
-        for (int r = 0; r < RT; ++r) {
-          part[r] = wrow[r][0] * fmaxf(acc[r][0], 0.f) + wrow[r][1] * fmaxf(acc[r][1], 0.f) +
-                    wrow[r][2] * fmaxf(acc[r][2], 0.f) + wrow[r][3] * fmaxf(acc[r][3], 0.f);
-        }
+        for (int r = 0; r < RT; ++r)
+          part[r] = wreg[r][0] * relu(acc[r][0]) + wreg[r][1] * relu(acc[r][1]) + wreg[r][2] * relu(acc[r][2]) +
+                    wreg[r][3] * relu(acc[r][3]);
+        // head sum per query: within the lane (4 rows), across lane groups, across tiles
         float val[NOUT];
-        if constexpr (NHP == 4) {
+        if constexpr (GROUPED) {
+#pragma unroll
+          for (int i = 0; i < NOUT; ++i) {
+            float v = part[M4 * i];
+#pragma unroll
+            for (int f = 1; f < M4; ++f) v += part[M4 * i + f];
+            val[i] = v;
+          }
+        } else if constexpr (NHP == 4) {
 #pragma unroll
           for (int r = 0; r < RT; ++r) val[r] = part[r];
         } else if constexpr (NHP == 8) {
@@ -179,22 +297,27 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         } else {
           constexpr int m = NHP / 16;
 #pragma unroll
-          for (int s = 0; s < QT; ++s) {
+          for (int q = 0; q < QW; ++q) {
             float v = 0.f;
 #pragma unroll
-            for (int i = 0; i < m; ++i) v += part[s * m + i];
+            for (int i = 0; i < m; ++i) v += part[q * m + i];
             v += __shfl_xor(v, 16, kWave);
             v += __shfl_xor(v, 32, kWave);
-            val[s] = v;
+            val[q] = v;
           }
         }
         const int s_out = base + kt * 16 + col;
+        if (GROUPED && unmasked) {
 #pragma unroll
-        for (int i = 0; i < NOUT; ++i) {
-          if (in_pass[i] && s_out < p_end && s_out < out_n[i])
-            a.out[(t0 + out_slot[i]) * a.out_stride + s_out] = val[i] + 0.f;
+          for (int i = 0; i < NOUT; ++i) buffer_store_f32(val[i] + 0.f, oview, voff[i] + (uint32_t)s_out * 4u);
+        } else {
+#pragma unroll
+          for (int i = 0; i < NOUT; ++i)
+            buffer_store_f32(val[i] + 0.f, oview, s_out < lim[i] ? voff[i] + (uint32_t)s_out * 4u : 0xfffffff0u);
         }
       }
+      store_block(s_k[(b + 1) & 1], nv);
+      __syncthreads();
     }
   }
 }
@@ -414,44 +537,35 @@ hipError_t launch_decode_d(const ScoreArgs& a, bool gather, int64_t max_len, hip
   }
 }
 
-template <int D, int NHP, int RT, int KT, bool GATHER>
-hipError_t launch_cfg(const ScoreArgs& a, int64_t ntile, int nchunk, hipStream_t st) {
-  dim3 grid(nchunk, (unsigned)ntile);
-  return launch_timed(GATHER ? KID_GATHER_SCORE : KID_SCORE, score_kernel<D, NHP, RT, KT, GATHER>, grid, dim3(256),
-                      st, a);
+template <int D, int NHP, int RT, int KB>
+hipError_t launch_prefill_cfg(ScoreArgs a, int64_t max_len, hipStream_t st) {
+  constexpr int QT = 4 * (16 * RT) / NHP;
+  if ((uint64_t)QT * (uint64_t)a.out_stride * 4u >= (1ull << 32) - 16) return hipErrorInvalidValue;   // view offsets
+  if (a.chunk <= 0) a.chunk = 2048;
+  const dim3 grid((unsigned)((a.T + QT - 1) / QT), (unsigned)((max_len + a.chunk - 1) / a.chunk));
+  return launch_timed(KID_SCORE, score_prefill_kernel<D, NHP, RT, KB>, grid, dim3(256), st, a);
 }
 
-// Keys per workgroup: wide tiles (prefill) take 2048-key chunks; otherwise the
-// chunk shrinks until the grid has about 2048 workgroups (at least 256 keys).
-inline int pick_chunk(int64_t ntile, int64_t max_len, bool wide) {
-  if (wide) return 2048;
-  int64_t c = 256;
-  while (c < 8192 && c * 2048 < max_len * ntile) c *= 2;
-  return (int)c;
-}
-
-template <int D, bool GATHER>
-hipError_t launch_d(ScoreArgs a, int nhp, bool wide, int64_t max_len, hipStream_t st) {
-  // rows per query nhp in {4, 8, 16, 32, 48, 64}; wide = many queries per key chunk (prefill)
-#define MISA_SCORE_CASE(NHP_, RT_, KT_)                                      \
-  {                                                                          \
-    constexpr int QT_ = (16 * RT_) / NHP_;                                   \
-    const int64_t ntile = (a.T + QT_ - 1) / QT_;                             \
-    if (a.chunk <= 0) a.chunk = pick_chunk(ntile, max_len, wide);            \
-    const int nchunk = (int)((max_len + a.chunk - 1) / a.chunk);             \
-    return launch_cfg<D, NHP_, RT_, KT_, GATHER>(a, ntile, nchunk, st);      \
-  }
-  (void)wide;
+// Row tiles per wave and keys per LDS block, sized so that the A fragments
+// (RT * D / 8 registers), the accumulators and row weights (8 * RT), one key
+// tile's B fragments and the staged next block fit 256 registers (two waves per
+// SIMD): up to d = 64 eight tiles (six for 48 rows per query); at d = 128 six
+// for 8 rows per query, otherwise four (three for 48, six being too many); at
+// d = 256 two (3 for 48, 4 for 64 rows) with 32-key blocks.
+template <int D>
+hipError_t launch_prefill(const ScoreArgs& a, int nhp, int64_t max_len, hipStream_t st) {
+  constexpr bool W = D == 256;
+  constexpr bool M = D == 128;
+  constexpr int KB = W ? 32 : 64;
   switch (nhp) {
-    case 4: MISA_SCORE_CASE(4, 4, 2)
-    case 8: MISA_SCORE_CASE(8, 8, 2)
-    case 16: MISA_SCORE_CASE(16, 8, 2)
-    case 32: MISA_SCORE_CASE(32, 8, 2)
-    case 48: MISA_SCORE_CASE(48, 6, 2)
-    case 64: MISA_SCORE_CASE(64, 8, 2)
-    default: return hipErrorInvalidValue;
+    case 4: return launch_prefill_cfg<D, 4, W ? 2 : (M ? 4 : 8), KB>(a, max_len, st);
+    case 8: return launch_prefill_cfg<D, 8, W ? 2 : (M ? 6 : 8), KB>(a, max_len, st);
+    case 16: return launch_prefill_cfg<D, 16, W ? 2 : (M ? 4 : 8), KB>(a, max_len, st);
+    case 32: return launch_prefill_cfg<D, 32, W ? 2 : (M ? 4 : 8), KB>(a, max_len, st);
+    case 48: return launch_prefill_cfg<D, 48, W ? 3 : (M ? 3 : 6), KB>(a, max_len, st);
+    case 64: return launch_prefill_cfg<D, 64, W ? 4 : (M ? 4 : 8), KB>(a, max_len, st);
   }
-#undef MISA_SCORE_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -475,10 +589,10 @@ hipError_t launch_score(const ScoreArgs& a, int d, bool gather, bool wide, int64
   }
   const int nhp = score_rows_per_query(a.hh);
   switch (d) {
-    case 32: return launch_d<32, false>(a, nhp, true, max_len, st);
-    case 64: return launch_d<64, false>(a, nhp, true, max_len, st);
-    case 128: return launch_d<128, false>(a, nhp, true, max_len, st);
-    case 256: return launch_d<256, false>(a, nhp, true, max_len, st);
+    case 32: return launch_prefill<32>(a, nhp, max_len, st);
+    case 64: return launch_prefill<64>(a, nhp, max_len, st);
+    case 128: return launch_prefill<128>(a, nhp, max_len, st);
+    case 256: return launch_prefill<256>(a, nhp, max_len, st);
   }
   return hipErrorInvalidValue;
 }

@@ -293,6 +293,61 @@ def test_mixed_sign_scores_exact(L):
     np.testing.assert_array_equal(rv.cpu().numpy(), ov2.astype(np.float32))
 
 
+@pytest.mark.parametrize("d", [32, 64, 256])
+@pytest.mark.parametrize("H,h", [(8, 2), (40, 5), (64, 16)])
+def test_prefill_shapes(d, H, h):
+    """Causal prefill through the LDS-tiled MFMA kernel for every row tiling (4, 8, 16
+    routed rows per query; 8, 48, 64 dense rows), several 64-query tiles and a ragged
+    last tile: routed and dense scores and selections bit-exact in grid mode."""
+    x = make_inputs("c2", mode="grid", L=330, T=330, H=H, d=d, h=h, B=32, topk=50)
+    dev = upload(x)
+    ho, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, h)
+    hd = torch.from_numpy(ho).cuda()
+    rows = M.debug_scores(dev["q"], dev["w"], dev["k"], hd, dev["q_seq"], dev["q_len"]).cpu().numpy()
+    for t in (0, 1, 63, 64, 65, 200, 329):
+        ref = O.routed_scores(x.q[t], x.w[t], x.k[0], ho[t], t + 1)
+        np.testing.assert_array_equal(rows[t, :t + 1], ref.astype(np.float32))
+    idx, sc = M.score_topk(dev["q"], dev["w"], dev["k"], hd, dev["q_seq"], dev["q_len"], 50)
+    oi, ov = O.score_topk(x.q, x.w, x.k, ho, x.q_seq, x.q_len, 50)
+    np.testing.assert_array_equal(idx.cpu().numpy(), oi)
+    np.testing.assert_array_equal(sc.cpu().numpy(), ov.astype(np.float32))
+    di, dv = M.dsa_index_dense(dev["q"], dev["w"], dev["k"], dev["q_seq"], dev["q_len"], 50)
+    odi, odv = O.dsa_index_dense(x.q, x.w, x.k, x.q_seq, x.q_len, 50)
+    np.testing.assert_array_equal(di.cpu().numpy(), odi)
+    np.testing.assert_array_equal(dv.cpu().numpy(), odv.astype(np.float32))
+
+
+def test_prefill_mixed_sequences():
+    """A prefill batch over three sequences with the queries in shuffled order: query
+    tiles straddle sequences (one key pass per distinct sequence in a tile), and the
+    prefixes are ragged. Grid mode, bit-exact routed and dense selections."""
+    base = make_inputs("c1", mode="grid", L=200, T=3, nseq=3, topk=40)
+    rng = np.random.default_rng(11)
+    T = 3 * 200
+    q_seq = np.repeat(np.arange(3, dtype=np.int32), 200)
+    q_len = np.tile(np.arange(1, 201, dtype=np.int32), 3)
+    perm = rng.permutation(T)
+    q_seq, q_len = q_seq[perm].copy(), q_len[perm].copy()
+    q = (rng.integers(-2, 3, size=(T, base.cfg.H, base.cfg.d)).astype(np.float32) / 16).astype(np.float32)
+    w = (rng.integers(1, 5, size=(T, base.cfg.H)).astype(np.float32) / 4).astype(np.float32)
+    from routed_token_indexer_amd.workloads import bf16_bits
+    dev = upload(base)
+    dev["q"] = torch.from_numpy(bf16_bits(q).view(np.int16)).cuda().view(torch.bfloat16).contiguous()
+    dev["w"] = torch.from_numpy(w).cuda()
+    dev["q_seq"] = torch.from_numpy(q_seq).cuda()
+    dev["q_len"] = torch.from_numpy(q_len).cuda()
+    ho, _ = O.route(q, w, base.k, q_seq, q_len, base.cfg.B, base.cfg.h)
+    hd = torch.from_numpy(ho).cuda()
+    idx, sc = M.score_topk(dev["q"], dev["w"], dev["k"], hd, dev["q_seq"], dev["q_len"], 40)
+    oi, ov = O.score_topk(q, w, base.k, ho, q_seq, q_len, 40)
+    np.testing.assert_array_equal(idx.cpu().numpy(), oi)
+    np.testing.assert_array_equal(sc.cpu().numpy(), ov.astype(np.float32))
+    di, dv = M.dsa_index_dense(dev["q"], dev["w"], dev["k"], dev["q_seq"], dev["q_len"], 40)
+    odi, odv = O.dsa_index_dense(q, w, base.k, q_seq, q_len, 40)
+    np.testing.assert_array_equal(di.cpu().numpy(), odi)
+    np.testing.assert_array_equal(dv.cpu().numpy(), odv.astype(np.float32))
+
+
 def test_rerank_skips_invalid_candidates():
     """Candidate ids outside [0, q_len) are not candidates; fewer valid than k pads with -1."""
     x, dev = get("c1r", "grid")
