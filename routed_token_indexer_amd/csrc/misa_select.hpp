@@ -1,5 +1,6 @@
-// Selection building blocks of the top-k kernels: 1024-thread workgroups,
-// order-preserving 32-bit keys (score_key), radix levels over LDS histograms.
+// Selection building blocks of the top-k kernels: workgroups of NT threads
+// (1024 by default), order-preserving 32-bit keys (score_key), radix levels over
+// LDS histograms.
 //
 // The selection rule (MISA pages: the indexer keeps the top-k tokens of each
 // query, ordered by score descending and token index ascending) is resolved as
@@ -30,16 +31,18 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
 }
 
 // Exclusive prefix sum over the workgroup in thread order, and the total.
-// One barrier; wsum[kSelWaves] must not be reused before every thread has
+// One barrier; wsum[NT / 64] must not be reused before every thread has
 // passed the next barrier.
+template <int NT = kSelThreads>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t& total) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t inc = wave_incl_scan(v);
   if (lane == 63) wsum[wave] = inc;
   __syncthreads();
   uint32_t pre = 0, tot = 0;
 #pragma unroll
-  for (int w4 = 0; w4 < kSelWaves; w4 += 4) {
+  for (int w4 = 0; w4 < NW; w4 += 4) {
     const u32x4 x = *reinterpret_cast<const u32x4*>(wsum + w4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -52,7 +55,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, 
 }
 
 // Two exclusive prefix sums at once (one barrier): returns a's and sets b's.
-// wsum2 holds 2 * kSelWaves words.
+// wsum2 holds 2 * kSelWaves words (1024-thread workgroups).
 __device__ __forceinline__ uint32_t block_excl_scan2(uint32_t a, uint32_t b, uint32_t* wsum2, uint32_t& b_excl) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t ia = wave_incl_scan(a), ib = wave_incl_scan(b);
@@ -81,21 +84,23 @@ __device__ __forceinline__ uint32_t block_excl_scan2(uint32_t a, uint32_t b, uin
 // out[1] = krem - count(bins > d) and out[2] = 1 if bin d is kept whole (its
 // count equals out[1]). Requires count(all bins) >= krem >= 1. Two barriers;
 // the caller reads out[] after the second.
+template <int NT = kSelThreads>
 __device__ __forceinline__ void find_threshold(const uint32_t* hist, int nb, uint32_t krem, uint32_t* wsum,
                                                uint32_t* out) {
+  constexpr int PMAX = kSelBins / NT;   // bins per thread at most
   const int tid = threadIdx.x;
-  const int per = nb > kSelThreads ? nb / kSelThreads : 1;   // <= 4
-  uint32_t c[4], mine = 0;
+  const int per = nb > NT ? nb / NT : 1;
+  uint32_t c[PMAX], mine = 0;
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
+  for (int jj = 0; jj < PMAX; ++jj) {
     const int b = per * tid + jj;
     c[jj] = (jj < per && b < nb) ? hist[nb - 1 - b] : 0u;
     mine += c[jj];
   }
   uint32_t tot;
-  uint32_t above = block_excl_scan(mine, wsum, tot);
+  uint32_t above = block_excl_scan<NT>(mine, wsum, tot);
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
+  for (int jj = 0; jj < PMAX; ++jj) {
     if (above < krem && above + c[jj] >= krem) {
       out[0] = (uint32_t)(nb - 1 - (per * tid + jj));
       out[1] = krem - above;
@@ -106,16 +111,19 @@ __device__ __forceinline__ void find_threshold(const uint32_t* hist, int nb, uin
   __syncthreads();
 }
 
-// Scratch of radix_select: one histogram, scan and result slot per level.
+// Scratch of radix_select for NT threads: NH histograms (one per level, or a
+// single one cleared between levels), a scan and a result slot per level.
+template <int NT = kSelThreads, int NH = 3>
 struct RadixScratch {
-  uint32_t hist[3][kSelBins];
-  uint32_t wsum[3][kSelWaves];
+  uint32_t hist[NH][kSelBins];
+  uint32_t wsum[3][NT / 64];
   uint32_t out[3][4];
 };
 
 // Zeroes the histograms (the caller puts a barrier before radix_select).
-__device__ __forceinline__ void radix_clear(RadixScratch& rs) {
-  for (int i = threadIdx.x; i < 3 * kSelBins; i += kSelThreads) (&rs.hist[0][0])[i] = 0u;
+template <int NT, int NH>
+__device__ __forceinline__ void radix_clear(RadixScratch<NT, NH>& rs) {
+  for (int i = threadIdx.x; i < NH * kSelBins; i += NT) (&rs.hist[0][0])[i] = 0u;
 }
 
 // Radix select among values v in [0, 2^nbits) (nbits <= 32) that each thread
@@ -125,9 +133,9 @@ __device__ __forceinline__ void radix_clear(RadixScratch& rs) {
 // thread) the kept values are those with (v & pmask) > prefix, then krem of
 // those with (v & pmask) == prefix (the lowest indices first). `full` tells
 // whether every one of the nbits bits was resolved.
-template <typename Visit>
+template <int NT, int NH, typename Visit>
 __device__ __forceinline__ void radix_select(Visit visit, int nbits, uint32_t& prefix, uint32_t& pmask,
-                                             uint32_t& krem, bool& full, RadixScratch& rs) {
+                                             uint32_t& krem, bool& full, RadixScratch<NT, NH>& rs) {
   prefix = 0;
   pmask = 0;
   full = true;
@@ -138,13 +146,17 @@ __device__ __forceinline__ void radix_select(Visit visit, int nbits, uint32_t& p
     const int width = top < 12 ? top : 12;
     const int shift = top - width;
     const uint32_t dm = (1u << width) - 1u;
-    uint32_t* h = rs.hist[lv];
+    uint32_t* h = rs.hist[NH == 1 ? 0 : lv];
+    if (NH == 1 && lv > 0) {   // one histogram: clear the previous level's counts first
+      for (int i = threadIdx.x; i < kSelBins; i += NT) h[i] = 0u;
+      __syncthreads();
+    }
     const uint32_t pf = prefix, pm = pmask;
     visit([&](uint32_t v) {
       if ((v & pm) == pf) atomicAdd(&h[(v >> shift) & dm], 1u);
     });
     __syncthreads();
-    find_threshold(h, 1 << width, krem, rs.wsum[lv], rs.out[lv]);
+    find_threshold<NT>(h, 1 << width, krem, rs.wsum[lv], rs.out[lv]);
     prefix |= rs.out[lv][0] << shift;
     pmask |= dm << shift;
     krem = rs.out[lv][1];
@@ -155,7 +167,8 @@ __device__ __forceinline__ void radix_select(Visit visit, int nbits, uint32_t& p
   }
 }
 
-// Minimum and maximum over the workgroup (one barrier; wmin / wmax of kSelWaves).
+// Minimum and maximum over the workgroup (one barrier; wmin / wmax of NT / 64).
+template <int NT = kSelThreads>
 __device__ __forceinline__ void block_minmax(uint32_t& lo, uint32_t& hi, uint32_t* wmin, uint32_t* wmax) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -171,7 +184,7 @@ __device__ __forceinline__ void block_minmax(uint32_t& lo, uint32_t& hi, uint32_
   lo = wmin[0];
   hi = wmax[0];
 #pragma unroll
-  for (int w = 1; w < kSelWaves; ++w) {
+  for (int w = 1; w < NT / 64; ++w) {
     lo = min(lo, wmin[w]);
     hi = max(hi, wmax[w]);
   }

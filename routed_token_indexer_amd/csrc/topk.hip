@@ -67,14 +67,14 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum) 
   return pre + inc - v;
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(TopkArgs a) {
+// Exact top-k of row t by one 1024-thread workgroup, rows of any length.
+__device__ __forceinline__ void topk_row_general(const TopkArgs& a, int64_t t) {
   __shared__ uint32_t hist[4096];
   __shared__ uint32_t rowk[kRowCap];
   __shared__ uint32_t wsum[kTopkWaves];
   __shared__ uint32_t wgt[kTopkWaves], weq[kTopkWaves];
   __shared__ uint32_t sh_digit, sh_krem;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t = blockIdx.x;
   int64_t n;
   int p;
   row_geometry(a, t, n, p);
@@ -207,23 +207,151 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(TopkArgs a) {
   }
 }
 
-// Register-resident variant for rows of at most kTopkThreads * EPT scores
-// (EPT <= 32): every key stays in the registers of its lane for the whole
-// select, wave w owning the contiguous run [64 * EPT * w, 64 * EPT * (w + 1))
-// with lane l holding elements 64 * j + l of it.
-// The radix levels run on v = key - min(key) over the row's nbits-bit range,
-// 12 bits per level from the top of that range: scores concentrated in a few
-// octaves then spread over the histogram instead of piling into a handful of
-// exponent bins (which serializes the LDS atomics and leaves large threshold
-// bins), and the select usually ends after one or two levels.
-template <int EPT, bool GATHER>
-__global__ __launch_bounds__(kTopkThreads) void topk_row_reg_kernel(TopkArgs a) {
+__global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(TopkArgs a) { topk_row_general(a, blockIdx.x); }
+
+// First output of a row that the register-resident kernel left to the general
+// select (no valid output is below -1).
+constexpr int32_t kFallbackMark = INT32_MIN;
+constexpr int kFallbackRows = 64;   // rows checked per workgroup
+
+// Rows marked by the register-resident kernel, redone by the general select:
+// each workgroup reads the first output of kFallbackRows rows.
+__global__ __launch_bounds__(kTopkThreads) void topk_fallback_kernel(TopkArgs a) {
+  __shared__ uint64_t s_mask;
+  const int64_t t0 = (int64_t)blockIdx.x * kFallbackRows;
+  if (threadIdx.x < 64) {
+    const int64_t t = t0 + threadIdx.x;
+    const bool marked = t < a.T && a.idx[t * (int64_t)a.k] == kFallbackMark;
+    const uint64_t m = __ballot(marked);
+    if (threadIdx.x == 0) s_mask = m;
+  }
+  __syncthreads();
+  uint64_t m = s_mask;
+  while (m) {
+    const int i = __ffsll((unsigned long long)m) - 1;
+    m &= m - 1;
+    topk_row_general(a, t0 + i);
+    __syncthreads();   // LDS of the general select is reused by the next row
+  }
+}
+
+// Exact select over the whole register-resident row (the fast path's fallback):
+// range [lo, hi] of the row's keys, radix levels on v = key - lo from the top of
+// that range, then the ascending-slot output of every v above the prefix and the
+// first krem equal to it. fresh_nvalid / fresh_nvs give the lane's and the
+// wave's count of slots in the row; emit(j, sel, run) writes slot j.
+template <int EPT, int NT, int NH, typename FV, typename FS, typename Emit>
+__device__ __forceinline__ void general_select(const uint32_t (&u)[EPT], FV fresh_nvalid, FS fresh_nvs, int k,
+                                               RadixScratch<NT, NH>& rs, uint32_t* wmin, uint32_t* wmax,
+                                               uint32_t* wgt, uint32_t* weq, Emit emit) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();   // the fast path's list (in the histograms) is no longer read
+  radix_clear(rs);
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  {
+    const int nv = fresh_nvalid(), ns = fresh_nvs();
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      if (j >= ns) continue;
+      lo = min(lo, j < nv ? u[j] : 0xffffffffu);
+      hi = max(hi, j < nv ? u[j] : 0u);
+    }
+  }
+  block_minmax<NT>(lo, hi, wmin, wmax);   // its barrier also orders the clear
+  const int nbits = hi == lo ? 0 : 32 - __clz(hi - lo);
+
+  uint32_t prefix, pmask, krem = (uint32_t)k;
+  bool full;
+  radix_select(
+      [&](auto&& f) {
+        const int nv = fresh_nvalid(), ns = fresh_nvs();
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+          if (j >= ns) continue;
+          if (j < nv) f(u[j] - lo);
+        }
+      },
+      nbits, prefix, pmask, krem, full, rs);
+
+  // ---- ascending-slot output: values above the prefix, then the first krem equal to it
+  auto is_gt = [&](int j, int nv) { return j < nv && ((u[j] - lo) & pmask) > prefix; };
+  auto is_eq = [&](int j, int nv) { return j < nv && ((u[j] - lo) & pmask) == prefix; };
+  uint32_t cgt = 0, ceq = 0;
+  int nv = fresh_nvalid(), ns = fresh_nvs();
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    if (j >= ns) continue;
+    cgt += (uint32_t)__popcll(__ballot(is_gt(j, nv)));
+    ceq += (uint32_t)__popcll(__ballot(is_eq(j, nv)));
+  }
+  if (lane == 0) {
+    wgt[wave] = cgt;
+    weq[wave] = ceq;
+  }
+  __syncthreads();
+  uint32_t eq_run = 0, sel_run = 0;
+  for (int ww = 0; ww < wave; ++ww) {
+    const uint32_t take = eq_run >= krem ? 0u : min(weq[ww], krem - eq_run);
+    sel_run += wgt[ww] + take;
+    eq_run += weq[ww];
+  }
+  const uint64_t lt = (1ull << lane) - 1ull;
+  nv = fresh_nvalid();
+  ns = fresh_nvs();
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    if (j >= ns) continue;
+    const bool gt = is_gt(j, nv);
+    const bool eq = is_eq(j, nv);
+    const uint64_t meq = __ballot(eq);
+    const uint32_t eq_rank = eq_run + (uint32_t)__popcll(meq & lt);
+    emit(j, gt || (eq && eq_rank < krem), sel_run);
+    eq_run += (uint32_t)__popcll(meq);
+  }
+}
+
+// Register-resident variant for rows of at most NT * EPT scores: every key
+// stays in the registers of its lane for the whole select, wave w owning the
+// contiguous run [64 * EPT * w, 64 * EPT * (w + 1)) with lane l holding elements
+// 64 * j + l of it. Slots past the row hold key 0 and are skipped wave by wave.
+//
+// Fast path (a handful of VALU operations per score, the rest is per row):
+//  1. one LDS histogram of 4096 bins over the row's key range [lo, hi], or over
+//     the 2^kWinBits keys below hi when the range is wider (lower keys fall into
+//     bin 0), gives the bin d of the k-th largest key and how many of that bin
+//     are still needed (a threshold in a clamped bin 0 takes a second histogram
+//     of that bin's keys over their own range);
+//  2. keys above bin d are kept (counted per wave with ballots); the keys of bin
+//     d, about a handful for real scores, go to an LDS list with their slots;
+//  3. each listed key gets its exact rank in (key descending, slot ascending)
+//     order; the last kept one gives the threshold key and the slot cutoff among
+//     keys equal to it, and the kept ones add to their wave's count;
+//  4. one pass writes every key > threshold, or == threshold at a slot <=
+//     cutoff, at its ballot position (ascending slot order).
+// The select falls back to an exact multi-level radix over the whole row when
+// bin d holds more than kCandCap keys (heavy ties, e.g. exactly representable
+// grids) or the row holds the padding key itself.
+constexpr int kWinBits = 26;     // window of 2^26 key units: 8 octaves of positive floats
+constexpr int kBinShift = kWinBits - 12;
+constexpr int kCandCap = 512;    // keys of the threshold bin ranked in LDS
+
+template <int EPT, bool GATHER, int NT>
+__global__ __launch_bounds__(NT, 1024 / NT) void topk_row_reg_kernel(TopkArgs a) {
+  constexpr int NW = NT / 64;
+  // the few-rows (1024-thread) variants run the fallback in place; the many-rows
+  // variants mark the row for topk_fallback_kernel and keep their registers for
+  // the fast path (more rows in flight per CU)
+  constexpr bool kInlineFallback = NT == 1024;
   constexpr bool kPrefetchIds = GATHER && EPT <= 16;   // token ids held beside the keys
-  __shared__ RadixScratch rs;
-  __shared__ uint32_t wmin[kSelWaves], wmax[kSelWaves];
-  __shared__ uint32_t wgt[kSelWaves], weq[kSelWaves];
+  __shared__ RadixScratch<NT, NT == 1024 ? 3 : 1> rs;
+  __shared__ uint32_t wmin[NW], wmax[NW];
+  __shared__ uint32_t wgt[NW], weq[NW];
+  __shared__ uint32_t s_m, s_thr, s_cut;
+  static_assert(2 * kCandCap <= kSelBins, "candidate list lives in the first histogram");
+  uint32_t* const c_key = &rs.hist[0][0];          // after the level-1 scan
+  uint32_t* const c_slot = &rs.hist[0][kCandCap];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t = blockIdx.x;
+  const int64_t t = (int64_t)a.T - 1 - blockIdx.x;   // causal batches: longest rows first
   int64_t n;
   int p;
   row_geometry(a, t, n, p);
@@ -234,7 +362,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_reg_kernel(TopkArgs a) 
   const int32_t* imap = a.imap ? a.imap + t * (int64_t)a.kc : nullptr;
 
   if (n <= k) {
-    for (int j = tid; j < k; j += kTopkThreads) {
+    for (int j = tid; j < k; j += NT) {
       if (j < n) {
         int32_t id;
         float sc;
@@ -250,82 +378,115 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_reg_kernel(TopkArgs a) 
   }
 
   // ---- every request at once: the keys and (gather rows) their token ids
-  const int64_t base = (int64_t)wave * 64 * EPT + lane;
-  auto in_row = [&](int j) { return base + 64 * j < n; };
+  const int base = wave * 64 * EPT + lane;   // slot of element j: base + 64 * j (n < 2^31)
+  // elements j < nvalid of this lane lie in the row (one count instead of an index per element)
+  const int nvalid = n > base ? (int)min((int64_t)EPT, (n - base + 63) / 64) : 0;
+  // lane 0 has the most; slots j >= nvs are empty in the whole wave and skipped by a scalar branch
+  const int nvs = __builtin_amdgcn_readfirstlane(nvalid);
+  // each pass takes fresh copies of nvalid / nvs that the compiler cannot see through,
+  // so it recomputes the slot masks (one compare each) instead of keeping up to 64 of
+  // them live in scalar registers across the whole kernel
+  auto fresh_nvalid = [&]() {
+    int x = nvalid;
+    asm volatile("" : "+v"(x));
+    return x;
+  };
+  auto fresh_nvs = [&]() {
+    int x = nvs;
+    asm volatile("" : "+s"(x));
+    return x;
+  };
+  // loads through range-checked views of the row: one 32-bit lane offset and a
+  // uniform per-element offset instead of a 64-bit address per element
   uint32_t u[EPT];
   int32_t ids[kPrefetchIds ? EPT : 1];
+  const auto rview = buffer_view(row, (uint32_t)(n * 4));
+  const auto iview = buffer_view(imap, GATHER ? (uint32_t)(n * 4) : 0u);
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    if (j >= nvs) continue;
+    u[j] = buffer_load_u32(rview, (uint32_t)base * 4u, 256u * j);   // raw bits; keys in place below
+    if constexpr (kPrefetchIds) ids[j] = (int32_t)buffer_load_u32(iview, (uint32_t)base * 4u, 256u * j);
+  }
+  if (tid == 0) s_m = 0u;
+  radix_clear(rs);
+  uint32_t lo = 0xffffffffu, hi = 0u;
   {
-    float v[EPT];
+    const int nv = fresh_nvalid(), ns = fresh_nvs();
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
-      const int64_t e = base + 64 * j;
-      v[j] = row[e < n ? e : 0];
-      if constexpr (kPrefetchIds) ids[j] = imap[e < n ? e : 0];
+      if (j >= ns) continue;
+      const bool in = j < nv;
+      u[j] = in ? score_key(__uint_as_float(u[j])) : 0u;
+      hi = max(hi, u[j]);
+      lo = min(lo, in ? u[j] : 0xffffffffu);
     }
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) u[j] = score_key(v[j]);
   }
-  radix_clear(rs);
-  // ---- key range of the row (element 0 exists, so it stands in for the tail)
-  uint32_t lo = 0xffffffffu, hi = 0u;
-#pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const uint32_t x = in_row(j) ? u[j] : u[0];
-    lo = min(lo, x);
-    hi = max(hi, x);
-  }
-  block_minmax(lo, hi, wmin, wmax);
-  const int nbits = hi == lo ? 0 : 32 - __clz(hi - lo);
-#pragma unroll
-  for (int j = 0; j < EPT; ++j) u[j] -= lo;   // v = key - min; slots past the row are never visited
+  // every load has been consumed: say so to the compiler's wait tracking (an
+  // s_waitcnt it sees), which otherwise cannot match the skipped slots of the passes
+  // below to those of the loads and waits for all memory operations, the earlier
+  // output stores included, before each slot of the output loop
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+  block_minmax<NT>(lo, hi, wmin, wmax);   // its barrier also orders the histogram clear
 
-  uint32_t prefix, pmask, krem = (uint32_t)k;
-  bool full;
-  radix_select(
-      [&](auto&& f) {
+  // ---- 1. level-1 histogram of the keys <= wtop: over the range [lo, wtop] when
+  // it spans at most kWinBits bits (bins of 2^shift keys from lo), else over the
+  // window of 2^kWinBits keys below wtop with every lower key in bin 0. Padding
+  // slots (key 0, the (-n) mod 64 slots after the row's last element) land in
+  // bin 0 and are taken out of it again. A threshold in a clamped bin 0 gives a
+  // second histogram over that bin's keys (wtop = its top), now unclamped.
+  constexpr uint32_t kWin = (1u << kWinBits) - 1u;
+  auto adaptive_shift = [](uint32_t range) { return max(0, (range == 0u ? 0 : 32 - __clz(range)) - 12); };
+  uint32_t wtop = hi;
+  bool clamped = hi - lo > kWin;
+  uint32_t wbase = clamped ? hi - kWin : lo;
+  int shift = clamped ? kBinShift : adaptive_shift(hi - lo);
+  if (tid == 0) atomicSub(&rs.hist[0][0], (uint32_t)(-n & 63));
+  {
+    const int ns = fresh_nvs();
 #pragma unroll
-        for (int j = 0; j < EPT; ++j)
-          if (in_row(j)) f(u[j]);
-      },
-      nbits, prefix, pmask, krem, full, rs);
-
-  // ---- index-ordered compaction: values above the prefix, then the first krem equal to it
-  auto is_gt = [&](int j) { return in_row(j) && (u[j] & pmask) > prefix; };
-  auto is_eq = [&](int j) { return in_row(j) && (u[j] & pmask) == prefix; };
-  uint32_t cgt = 0, ceq = 0;
-#pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    cgt += (uint32_t)__popcll(__ballot(is_gt(j)));
-    ceq += (uint32_t)__popcll(__ballot(is_eq(j)));
-  }
-  if (lane == 0) {
-    wgt[wave] = cgt;
-    weq[wave] = ceq;
+    for (int j = 0; j < EPT; ++j) {
+      if (j >= ns) continue;
+      const uint32_t d = __builtin_elementwise_sub_sat(u[j], wbase) >> shift;
+      atomicAdd(&rs.hist[0][d], 1u);
+    }
   }
   __syncthreads();
-  uint32_t eq_run = 0, sel_run = 0;
-  for (int ww = 0; ww < wave; ++ww) {
-    const uint32_t take = eq_run >= krem ? 0u : min(weq[ww], krem - eq_run);
-    sel_run += wgt[ww] + take;
-    eq_run += weq[ww];
+  find_threshold<NT>(rs.hist[0], kSelBins, (uint32_t)k, rs.wsum[0], rs.out[0]);
+  uint32_t d1 = rs.out[0][0], krem1 = rs.out[0][1];
+  if (d1 == 0u && clamped) {
+    wtop = wbase + ((1u << shift) - 1u);   // <= hi: bin 0 holds keys below it
+    clamped = false;
+    wbase = lo;
+    shift = adaptive_shift(wtop - lo);
+    for (int i = tid; i < kSelBins; i += NT) rs.hist[0][i] = 0u;   // find_threshold has read them
+    __syncthreads();
+    if (tid == 0) atomicSub(&rs.hist[0][0], (uint32_t)(-n & 63));
+    const int ns = fresh_nvs();
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      if (j >= ns) continue;
+      if (u[j] <= wtop) atomicAdd(&rs.hist[0][__builtin_elementwise_sub_sat(u[j], wbase) >> shift], 1u);
+    }
+    __syncthreads();
+    find_threshold<NT>(rs.hist[0], kSelBins, krem1, rs.wsum[1], rs.out[1]);
+    d1 = rs.out[1][0];
+    krem1 = rs.out[1][1];
   }
   const uint64_t lt = (1ull << lane) - 1ull;
-#pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const bool gt = is_gt(j);
-    const bool eq = is_eq(j);
-    const uint64_t meq = __ballot(eq);
-    const uint32_t eq_rank = eq_run + (uint32_t)__popcll(meq & lt);
-    const bool sel = gt || (eq && eq_rank < krem);
+
+  // ---- output of slot j where sel holds: ascending slot order from pos
+  auto emit = [&](int j, bool sel, uint32_t& run) {
     const uint64_t msel = __ballot(sel);
-    const uint32_t pos = sel_run + (uint32_t)__popcll(msel & lt);
+    const uint32_t pos =
+        run + __builtin_amdgcn_mbcnt_hi((uint32_t)(msel >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)msel, 0u));
     if (sel && pos < (uint32_t)k) {
-      int32_t id = (int32_t)(base + 64 * j);
-      float sc = key_score(u[j] + lo);
+      int32_t id = base + 64 * j;
+      float sc = key_score(u[j]);
       if constexpr (GATHER) {
         int32_t v;
         if constexpr (kPrefetchIds) v = ids[j];
-        else v = imap[base + 64 * j];
+        else v = (int32_t)buffer_load_u32(iview, (uint32_t)base * 4u, 256u * j);
         const bool ok = v >= 0 && v < p;
         id = ok ? v : -1;
         sc = ok ? sc : 0.f;
@@ -333,9 +494,76 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_reg_kernel(TopkArgs a) 
       oi[pos] = id;
       if (os) os[pos] = sc;
     }
-    eq_run += (uint32_t)__popcll(meq);
-    sel_run += (uint32_t)__popcll(msel);
+    run += (uint32_t)__popcll(msel);
+  };
+
+  // bin 0 is exact unless it holds clamped keys; a row key equal to the padding
+  // key 0 (float bits 0xffffffff) leaves it to the general select too
+  if (d1 != 0u || (!clamped && lo != 0u)) {
+    // ---- 2. keys above bin d are kept; keys of bin d are listed
+    const uint32_t klo = wbase + (d1 << shift);
+    const uint32_t span = (1u << shift) - 1u;
+    const uint32_t khi = wtop - klo < span ? wtop : klo + span;   // no wrap past 2^32 - 1
+    uint32_t cgt = 0;
+    {
+      const int ns = fresh_nvs();
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) {
+        if (j >= ns) continue;
+        cgt += (uint32_t)__popcll(__ballot(u[j] > khi));
+        const bool c = u[j] - klo <= khi - klo;   // klo <= key <= khi; padding (key 0) is below klo > 0
+        const uint64_t mc = __ballot(c);
+        if (mc) {
+          uint32_t off = 0;
+          if (lane == 0) off = atomicAdd(&s_m, (uint32_t)__popcll(mc));
+          off = (uint32_t)__shfl(off, 0, kWave) + (uint32_t)__popcll(mc & lt);
+          if (c && off < (uint32_t)kCandCap) {
+            c_key[off] = u[j];
+            c_slot[off] = (uint32_t)(base + 64 * j);
+          }
+        }
+      }
+    }
+    if (lane == 0) {
+      wgt[wave] = cgt;
+      weq[wave] = 0u;
+    }
+    __syncthreads();
+    const uint32_t m = s_m;
+    if (m <= (uint32_t)kCandCap) {
+      // ---- 3. exact rank of each listed key; the krem1 first are kept
+      for (uint32_t i = tid; i < m; i += NT) {
+        const uint32_t ki = c_key[i], si = c_slot[i];
+        uint32_t r = 0;
+        for (uint32_t q = 0; q < m; ++q) {
+          const uint32_t kq = c_key[q], sq = c_slot[q];
+          r += (kq > ki || (kq == ki && sq < si)) ? 1u : 0u;
+        }
+        if (r < krem1) atomicAdd(&weq[si / (64u * EPT)], 1u);
+        if (r == krem1 - 1u) {
+          s_thr = ki;
+          s_cut = si;
+        }
+      }
+      __syncthreads();
+      const uint32_t thr = s_thr;
+      const int cut = (int)s_cut - base;   // kept keys equal to thr: 64 * j <= cut
+      uint32_t run = 0;
+      for (int ww = 0; ww < wave; ++ww) run += wgt[ww] + weq[ww];
+      // ---- 4. ascending-slot output
+      const int ns = fresh_nvs();
+#pragma unroll
+      for (int j = 0; j < EPT; ++j) {
+        if (j >= ns) continue;
+        emit(j, (u[j] > thr) | ((u[j] == thr) & (64 * j <= cut)), run);
+      }
+      return;
+    }
   }
+  if constexpr (kInlineFallback)
+    general_select<EPT, NT>(u, fresh_nvalid, fresh_nvs, k, rs, wmin, wmax, wgt, weq, emit);
+  else if (tid == 0)
+    oi[0] = kFallbackMark;
 }
 
 }  // namespace
@@ -355,18 +583,45 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
   if (a.T == 0) return hipSuccess;
   const int64_t max_len = a.imap ? a.kc : a.Lmax;
   const dim3 grid((unsigned)a.T), block(kTopkThreads);
-#define MISA_TOPK_REG(EPT_)                                                     \
-  if (max_len <= (EPT_) * kTopkThreads) {                                       \
-    if (a.imap)                                                                 \
-      hipLaunchKernelGGL((topk_row_reg_kernel<EPT_, true>), grid, block, 0, st, a);  \
-    else                                                                        \
-      hipLaunchKernelGGL((topk_row_reg_kernel<EPT_, false>), grid, block, 0, st, a); \
-    return hipGetLastError();                                                   \
+  // many rows (prefill): 256- and 512-thread workgroups (one histogram), so that
+  // several rows per CU are in flight; few rows: 1024 threads for the shortest
+  // latency per row
+#define MISA_TOPK_REG(EPT_, NT_)                                                          \
+  if (max_len <= (EPT_) * (NT_)) {                                                        \
+    if (a.imap)                                                                           \
+      hipLaunchKernelGGL((topk_row_reg_kernel<EPT_, true, NT_>), grid, dim3(NT_), 0, st, a);  \
+    else                                                                                  \
+      hipLaunchKernelGGL((topk_row_reg_kernel<EPT_, false, NT_>), grid, dim3(NT_), 0, st, a); \
+    return hipGetLastError();                                                             \
   }
-  MISA_TOPK_REG(4)
-  MISA_TOPK_REG(8)
-  MISA_TOPK_REG(16)
-  MISA_TOPK_REG(32)
+  if (a.T >= 256) {
+    // rows the register-resident kernel leaves to the general select are marked
+    // and redone by topk_fallback_kernel (usually none: a launch that only reads)
+    bool done = false;
+#define MISA_TOPK_MANY(EPT_, NT_)                                                        \
+    if (!done && max_len <= (EPT_) * (NT_)) {                                            \
+      if (a.imap)                                                                        \
+        hipLaunchKernelGGL((topk_row_reg_kernel<EPT_, true, NT_>), grid, dim3(NT_), 0, st, a);  \
+      else                                                                               \
+        hipLaunchKernelGGL((topk_row_reg_kernel<EPT_, false, NT_>), grid, dim3(NT_), 0, st, a); \
+      done = true;                                                                       \
+    }
+    MISA_TOPK_MANY(16, 256)
+    MISA_TOPK_MANY(32, 256)
+    MISA_TOPK_MANY(32, 512)
+#undef MISA_TOPK_MANY
+    if (done) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(topk_fallback_kernel, dim3((unsigned)((a.T + kFallbackRows - 1) / kFallbackRows)),
+                         block, 0, st, a);
+      return hipGetLastError();
+    }
+  }
+  MISA_TOPK_REG(4, 1024)
+  MISA_TOPK_REG(8, 1024)
+  MISA_TOPK_REG(16, 1024)
+  MISA_TOPK_REG(32, 1024)
 #undef MISA_TOPK_REG
   hipLaunchKernelGGL(topk_row_kernel, grid, block, 0, st, a);
   return hipGetLastError();

@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void split_filter_kernel(TopkArgs a, Spli
   __shared__ uint32_t wcnt[kWaves], wdef[kWaves], wbase[kWaves];
   __shared__ uint32_t s_last;
   // the last chunk only
-  __shared__ RadixScratch rs;
+  __shared__ RadixScratch<> rs;
   __shared__ uint32_t wmin[kWaves], wmax[kWaves], wsum2[3][kWaves];
   __shared__ uint32_t cgt[kMaxChunks], ceq[kMaxChunks];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;

@@ -293,6 +293,44 @@ def test_mixed_sign_scores_exact(L):
     np.testing.assert_array_equal(rv.cpu().numpy(), ov2.astype(np.float32))
 
 
+@pytest.mark.parametrize("k", [1, 37, 150, 500])
+def test_prefill_mixed_sign_many_rows(k):
+    """Causal batch of 700 rows (the many-rows top-k) with scores of both signs:
+    rows whose k-th score lies far below the row maximum, or inside a bin of
+    many equal scores, go to the general select and must come out identical to
+    the rows the single-histogram path finishes; bit-exact in grid mode."""
+    x = make_inputs("c2", mode="grid", L=700, T=700, topk=k)
+    x.w[:, 1::3] *= -1.0
+    x.w[:, 2::3] *= -2.0
+    dev = upload(x)
+    idx, sc = M.dsa_index_dense(dev["q"], dev["w"], dev["k"], dev["q_seq"], dev["q_len"], k)
+    oi, ov = O.dsa_index_dense(x.q, x.w, x.k, x.q_seq, x.q_len, k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), oi)
+    np.testing.assert_array_equal(sc.cpu().numpy(), ov.astype(np.float32))
+    assert (ov < 0).any() and (ov > 0).any()
+    ho, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h)
+    _, _, ri, rv = run_misa(dev, x.cfg, heads=ho, topk=k)
+    oi2, ov2 = O.score_topk(x.q, x.w, x.k, ho, x.q_seq, x.q_len, k)
+    np.testing.assert_array_equal(ri, oi2)
+    np.testing.assert_array_equal(rv, ov2.astype(np.float32))
+
+
+@pytest.mark.parametrize("k", [1, 100, 699, 700, 900])
+def test_prefill_all_equal_scores(k):
+    """Many rows of equal scores (zero keys): each row keeps its lowest token
+    indices, padded with -1 where the causal prefix is shorter than k."""
+    x = make_inputs("c2", mode="grid", L=700, T=700, topk=k)
+    dev = upload(x)
+    k0 = torch.zeros_like(dev["k"])
+    idx, sc = M.dsa_index_dense(dev["q"], dev["w"], k0, dev["q_seq"], dev["q_len"], k)
+    idx = idx.cpu().numpy()
+    sc = sc.cpu().numpy()
+    for t in range(x.cfg.T):
+        p = min(int(x.q_len[t]), k)
+        assert idx[t][:p].tolist() == list(range(p)), t
+        assert np.all(idx[t][p:] == -1) and np.all(sc[t] == 0), t
+
+
 @pytest.mark.parametrize("d", [32, 64, 256])
 @pytest.mark.parametrize("H,h", [(8, 2), (40, 5), (64, 16)])
 def test_prefill_shapes(d, H, h):
