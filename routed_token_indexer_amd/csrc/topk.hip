@@ -335,15 +335,16 @@ constexpr int kWinBits = 26;     // window of 2^26 key units: 8 octaves of posit
 constexpr int kBinShift = kWinBits - 12;
 constexpr int kCandCap = 512;    // keys of the threshold bin ranked in LDS
 
-template <int EPT, bool GATHER, int NT>
-__global__ __launch_bounds__(NT, 1024 / NT) void topk_row_reg_kernel(TopkArgs a) {
+template <int EPT, bool GATHER, int NT, bool MANY>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MANY ? 8 : NT / 256))) void topk_row_reg_kernel(
+    TopkArgs a) {
   constexpr int NW = NT / 64;
-  // the few-rows (1024-thread) variants run the fallback in place; the many-rows
-  // variants mark the row for topk_fallback_kernel and keep their registers for
-  // the fast path (more rows in flight per CU)
-  constexpr bool kInlineFallback = NT == 1024;
+  // the few-rows variants run the fallback in place; the many-rows (MANY) variants
+  // mark the row for topk_fallback_kernel and keep their registers for the fast
+  // path: at most 64 per lane, so that eight waves per SIMD are resident
+  constexpr bool kInlineFallback = !MANY;
   constexpr bool kPrefetchIds = GATHER && EPT <= 16;   // token ids held beside the keys
-  __shared__ RadixScratch<NT, NT == 1024 ? 3 : 1> rs;
+  __shared__ RadixScratch<NT, (NT == 1024 && !MANY) ? 3 : 1> rs;
   __shared__ uint32_t wmin[NW], wmax[NW];
   __shared__ uint32_t wgt[NW], weq[NW];
   __shared__ uint32_t s_m, s_thr, s_cut;
@@ -473,7 +474,6 @@ __global__ __launch_bounds__(NT, 1024 / NT) void topk_row_reg_kernel(TopkArgs a)
     d1 = rs.out[1][0];
     krem1 = rs.out[1][1];
   }
-  const uint64_t lt = (1ull << lane) - 1ull;
 
   // ---- output of slot j where sel holds: ascending slot order from pos
   auto emit = [&](int j, bool sel, uint32_t& run) {
@@ -516,7 +516,8 @@ __global__ __launch_bounds__(NT, 1024 / NT) void topk_row_reg_kernel(TopkArgs a)
         if (mc) {
           uint32_t off = 0;
           if (lane == 0) off = atomicAdd(&s_m, (uint32_t)__popcll(mc));
-          off = (uint32_t)__shfl(off, 0, kWave) + (uint32_t)__popcll(mc & lt);
+          off = (uint32_t)__shfl(off, 0, kWave) +
+                __builtin_amdgcn_mbcnt_hi((uint32_t)(mc >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mc, 0u));
           if (c && off < (uint32_t)kCandCap) {
             c_key[off] = u[j];
             c_slot[off] = (uint32_t)(base + 64 * j);
@@ -531,18 +532,35 @@ __global__ __launch_bounds__(NT, 1024 / NT) void topk_row_reg_kernel(TopkArgs a)
     __syncthreads();
     const uint32_t m = s_m;
     if (m <= (uint32_t)kCandCap) {
-      // ---- 3. exact rank of each listed key; the krem1 first are kept
-      for (uint32_t i = tid; i < m; i += NT) {
-        const uint32_t ki = c_key[i], si = c_slot[i];
-        uint32_t r = 0;
-        for (uint32_t q = 0; q < m; ++q) {
-          const uint32_t kq = c_key[q], sq = c_slot[q];
-          r += (kq > ki || (kq == ki && sq < si)) ? 1u : 0u;
-        }
+      // ---- 3. exact rank of each listed key; the krem1 first are kept. A few
+      // keys: a thread per key walks the list; more: a wave per key, its lanes
+      // comparing 64 others at a time
+      auto keep = [&](uint32_t r, uint32_t ki, uint32_t si) {
         if (r < krem1) atomicAdd(&weq[si / (64u * EPT)], 1u);
         if (r == krem1 - 1u) {
           s_thr = ki;
           s_cut = si;
+        }
+      };
+      if (m <= 32u) {
+        if ((uint32_t)tid < m) {
+          const uint32_t ki = c_key[tid], si = c_slot[tid];
+          uint32_t r = 0;
+          for (uint32_t q = 0; q < m; ++q)
+            r += (c_key[q] > ki || (c_key[q] == ki && c_slot[q] < si)) ? 1u : 0u;
+          keep(r, ki, si);
+        }
+      } else {
+        for (uint32_t i = wave; i < m; i += NW) {
+          const uint32_t ki = c_key[i], si = c_slot[i];
+          uint32_t r = 0;
+          for (uint32_t q0 = 0; q0 < m; q0 += 64) {
+            const uint32_t q = q0 + lane;
+            bool before = false;
+            if (q < m) before = c_key[q] > ki || (c_key[q] == ki && c_slot[q] < si);
+            r += (uint32_t)__popcll(__ballot(before));
+          }
+          if (lane == 0) keep(r, ki, si);
         }
       }
       __syncthreads();
@@ -589,9 +607,9 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
 #define MISA_TOPK_REG(EPT_, NT_)                                                          \
   if (max_len <= (EPT_) * (NT_)) {                                                        \
     if (a.imap)                                                                           \
-      hipLaunchKernelGGL((topk_row_reg_kernel<EPT_, true, NT_>), grid, dim3(NT_), 0, st, a);  \
+      hipLaunchKernelGGL((topk_row_reg_kernel<EPT_, true, NT_, false>), grid, dim3(NT_), 0, st, a);  \
     else                                                                                  \
-      hipLaunchKernelGGL((topk_row_reg_kernel<EPT_, false, NT_>), grid, dim3(NT_), 0, st, a); \
+      hipLaunchKernelGGL((topk_row_reg_kernel<EPT_, false, NT_, false>), grid, dim3(NT_), 0, st, a); \
     return hipGetLastError();                                                             \
   }
   if (a.T >= 256) {
@@ -601,9 +619,9 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
 #define MISA_TOPK_MANY(EPT_, NT_)                                                        \
     if (!done && max_len <= (EPT_) * (NT_)) {                                            \
       if (a.imap)                                                                        \
-        hipLaunchKernelGGL((topk_row_reg_kernel<EPT_, true, NT_>), grid, dim3(NT_), 0, st, a);  \
+        hipLaunchKernelGGL((topk_row_reg_kernel<EPT_, true, NT_, true>), grid, dim3(NT_), 0, st, a);  \
       else                                                                               \
-        hipLaunchKernelGGL((topk_row_reg_kernel<EPT_, false, NT_>), grid, dim3(NT_), 0, st, a); \
+        hipLaunchKernelGGL((topk_row_reg_kernel<EPT_, false, NT_, true>), grid, dim3(NT_), 0, st, a); \
       done = true;                                                                       \
     }
     MISA_TOPK_MANY(16, 256)
