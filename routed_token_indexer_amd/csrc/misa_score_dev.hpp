@@ -37,6 +37,71 @@ __device__ __forceinline__ void load_key_tiles(const uint16_t* kseq_lane, int ba
   }
 }
 
+// 64-key row blocks of the d = 128 decode stream. Lane l loads 16-byte piece
+// (l & 15) of rows 4 * i + (l >> 4), i < 16, so every load instruction reads four
+// whole 256-byte key rows (non-temporal: each key is read once). Positions past
+// c_end and skipped candidates read row `fallback` (which exists); their scores
+// are masked when the block is scored.
+struct RowBlock128 {
+  u32x4 v[16];
+};
+
+template <typename KeyOf>
+__device__ __forceinline__ void load_row_block128(const uint16_t* kseq, int base, int c_end, int lane, KeyOf key_of,
+                                                  int fallback, RowBlock128& rb) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int s = base + 4 * i + (lane >> 4);
+    const int key = s < c_end ? key_of(s) : -1;
+    const uint16_t* kp = kseq + (int64_t)(key < 0 ? fallback : key) * 128 + (lane & 15) * 8;
+    rb.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp));
+  }
+}
+
+// A staged block in LDS: piece p of block row k at slot k * 16 + (p ^ (k & 15)),
+// so that the row-wise writes and the MFMA-layout reads (16 rows, one piece
+// each) both spread over all banks.
+__device__ __forceinline__ void stage_row_block128(u32x4* s_blk, const RowBlock128& rb, int lane) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int k = 4 * i + (lane >> 4);
+    s_blk[k * 16 + ((lane & 15) ^ (k & 15))] = rb.v[i];
+  }
+}
+
+// score_four_tiles on a staged block: the B fragment of tile kt, step ks is
+// piece 4 * ks + grp of row 16 * kt + col, the same operands in the same order,
+// so the scores are the same bit for bit. valid_bits: bit kt tells whether key
+// 16 * kt + col of the block is valid.
+template <int RT>
+__device__ __forceinline__ float score_four_tiles_staged(const u32x4 (&afrag)[RT][4], const float (&wrow)[RT][4],
+                                                         const u32x4* s_blk, int grp, int col, uint32_t valid_bits) {
+  float mine = 0.f;
+  bool mine_valid = false;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    u32x4 b[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) b[ks] = s_blk[(16 * kt + col) * 16 + ((4 * ks + grp) ^ col)];
+    float part = 0.f;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc = mfma_16x16x32(afrag[r][ks], b[ks], acc);
+      part += wrow[r][0] * relu(acc[0]) + wrow[r][1] * relu(acc[1]) +
+              wrow[r][2] * relu(acc[2]) + wrow[r][3] * relu(acc[3]);
+    }
+    part += __shfl_xor(part, 16, kWave);
+    part += __shfl_xor(part, 32, kWave);
+    if (grp == kt) {
+      mine = part;
+      mine_valid = (valid_bits >> kt) & 1u;
+    }
+  }
+  return mine_valid ? mine + 0.f : -INFINITY;
+}
+
 // A fragments and row weights of one query: row r*16 + i holds head head_of(row)
 // (-1: a zero row with weight 0).
 template <int D, int RT, typename HeadOf>

@@ -337,8 +337,16 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a) {
   constexpr int LDQ = D + 8;      // LDS row stride of the staged query rows (bf16)
   constexpr int QV = D / 8;       // 16-byte pieces per query row
   constexpr int QPT = (64 * QV + 255) / 256;   // staging pieces per thread (H <= 64)
-  __shared__ uint32_t lh[HIST ? 4096 : 1];
-  __shared__ __align__(16) uint16_t s_q[64 * LDQ];
+  // d = 128 over contiguous keys streams row blocks through a swizzled LDS stage
+  // (16 KiB per wave), which also holds the staged query rows before the stream
+  // starts (gathered candidate rows keep the direct MFMA-layout loads)
+  constexpr bool kStage = D == 128 && !GATHER;
+  constexpr int kQBytes = 64 * LDQ * 2;
+  constexpr int kBufBytes = kStage ? (4 * 1024 * 16 > kQBytes ? 4 * 1024 * 16 : kQBytes) : kQBytes;
+  // level-1 histogram: two 16-bit bin counts per word (a chunk has at most 16384 keys)
+  __shared__ uint32_t lh[HIST ? 2048 : 1];
+  __shared__ __align__(16) uint8_t s_buf[kBufBytes];
+  uint16_t* const s_q = reinterpret_cast<uint16_t*>(s_buf);
   __shared__ float s_w[64];
   __shared__ int s_heads[64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -410,9 +418,16 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a) {
   // 3. the first two iterations' key tiles (two in flight per wave)
   constexpr int kStep = 4 * 16 * KT;   // keys per workgroup iteration
   const int base0 = c_begin + wave * 16 * KT;
-  KeyTiles<D, KT> ta, tb;
-  load_key_tiles<D, KT>(kseq, base0, c_end, col, key_of, fallback, ta);
-  load_key_tiles<D, KT>(kseq, base0 + kStep, c_end, col, key_of, fallback, tb);
+  const uint16_t* kseq_rows = a.k + (int64_t)(seq < 0 ? 0 : seq) * a.Lmax * D;
+  KeyTiles<D, kStage ? 1 : KT> ta, tb;
+  RowBlock128 ra, rb;
+  if constexpr (kStage) {
+    load_row_block128(kseq_rows, base0, c_end, lane, key_of, fallback, ra);
+    load_row_block128(kseq_rows, base0 + kStep, c_end, lane, key_of, fallback, rb);
+  } else {
+    load_key_tiles<D, KT>(kseq, base0, c_end, col, key_of, fallback, ta);
+    load_key_tiles<D, KT>(kseq, base0 + kStep, c_end, col, key_of, fallback, tb);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // 4. select the heads while the keys stream in
@@ -432,7 +447,7 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a) {
     }
   }
   if constexpr (HIST) {
-    for (int i = threadIdx.x; i < 4096; i += 256) lh[i] = 0;
+    for (int i = threadIdx.x; i < 2048; i += 256) lh[i] = 0;
   }
   __syncthreads();
   if (c_begin >= n) return;
@@ -462,12 +477,15 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a) {
   // branched around: the loop body stays straight-line and the compiler can
   // count the loads in flight exactly.
   const auto ov = buffer_view(a.out + t * a.out_stride + c_begin, (uint32_t)(c_end - c_begin) * 4u);
-  auto emit = [&](const KeyTiles<D, KT>& tiles, int b) {
-    const float v = score_four_tiles<D, RT>(afrag, wrow, tiles, grp);
+  auto put = [&](float v, int b) {
     const int s = b + lane;
     buffer_store_f32(v, ov, (uint32_t)(s - c_begin) * 4u);
-    if constexpr (HIST) atomicAdd(&lh[score_key(v) >> 20], s < c_end ? 1u : 0u);
+    if constexpr (HIST) {
+      const uint32_t bin = score_key(v) >> 20;
+      atomicAdd(&lh[bin >> 1], (s < c_end ? 1u : 0u) << (16 * (bin & 1u)));
+    }
   };
+  auto emit = [&](const KeyTiles<D, KT>& tiles, int b) { put(score_four_tiles<D, RT>(afrag, wrow, tiles, grp), b); };
   // Two register sets alternate, so no in-flight tile is ever copied (a copy
   // would wait for its load). The iteration count is uniform over the
   // workgroup; each wave masks its own tail through c_end. Inside the loop the
@@ -475,20 +493,60 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a) {
   // in-bounds rows).
   const int nit = (c_end - c_begin + kStep - 1) / kStep;
   int it = 0;
-  for (; it + 2 < nit; it += 2) {
-    const int b = base0 + it * kStep;
-    emit(ta, b);
-    load_key_tiles<D, KT>(kseq, b + 2 * kStep, c_end, col, key_of, fallback, ta);
-    emit(tb, b + kStep);
-    load_key_tiles<D, KT>(kseq, b + 3 * kStep, c_end, col, key_of, fallback, tb);
+  if constexpr (kStage) {
+    // a block goes to this wave's LDS stage, the registers take the block after
+    // next, and the block is scored from LDS (LDS operations of a wave run in
+    // order, so the stage is not rewritten before its reads)
+    __syncthreads();   // every wave has read the staged query rows
+    u32x4* const s_blk = reinterpret_cast<u32x4*>(s_buf) + wave * 1024;
+    auto valid_bits = [&](int b) {
+      uint32_t bits = 0;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const int s = b + 16 * kt + col;
+        bits |= (s < c_end && key_of(s) >= 0) ? 1u << kt : 0u;
+      }
+      return bits;
+    };
+    auto score_staged = [&](int b) {
+      put(score_four_tiles_staged<RT>(afrag, wrow, s_blk, grp, col, valid_bits(b)), b);
+    };
+    for (; it + 2 < nit; it += 2) {
+      const int b = base0 + it * kStep;
+      stage_row_block128(s_blk, ra, lane);
+      load_row_block128(kseq_rows, b + 2 * kStep, c_end, lane, key_of, fallback, ra);
+      score_staged(b);
+      stage_row_block128(s_blk, rb, lane);
+      load_row_block128(kseq_rows, b + 3 * kStep, c_end, lane, key_of, fallback, rb);
+      score_staged(b + kStep);
+    }
+    if (it < nit) {
+      stage_row_block128(s_blk, ra, lane);
+      score_staged(base0 + it * kStep);
+    }
+    if (it + 1 < nit) {
+      stage_row_block128(s_blk, rb, lane);
+      score_staged(base0 + (it + 1) * kStep);
+    }
+  } else {
+    for (; it + 2 < nit; it += 2) {
+      const int b = base0 + it * kStep;
+      emit(ta, b);
+      load_key_tiles<D, KT>(kseq, b + 2 * kStep, c_end, col, key_of, fallback, ta);
+      emit(tb, b + kStep);
+      load_key_tiles<D, KT>(kseq, b + 3 * kStep, c_end, col, key_of, fallback, tb);
+    }
+    if (it < nit) emit(ta, base0 + it * kStep);
+    if (it + 1 < nit) emit(tb, base0 + (it + 1) * kStep);
   }
-  if (it < nit) emit(ta, base0 + it * kStep);
-  if (it + 1 < nit) emit(tb, base0 + (it + 1) * kStep);
   if constexpr (HIST) {
     __syncthreads();
     uint32_t* gh = a.hist + t * 4096;
-    for (int i = threadIdx.x; i < 4096; i += 256)
-      if (lh[i]) atomicAdd(&gh[i], lh[i]);
+    for (int i = threadIdx.x; i < 2048; i += 256) {
+      const uint32_t v = lh[i];
+      if (v & 0xffffu) atomicAdd(&gh[2 * i], v & 0xffffu);
+      if (v >> 16) atomicAdd(&gh[2 * i + 1], v >> 16);
+    }
   }
 }
 
