@@ -22,9 +22,12 @@ __device__ __forceinline__ floatx4 mfma_16x16x32(const u32x4& a, const u32x4& b,
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// max(x, 0) as one instruction (the median of x, 0 and +inf); used by every
-// scoring path so that all of them round identically.
-__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, __builtin_inff()); }
+// max(x, 0) as one integer instruction on the bits: a float with the sign bit
+// set (negative, -0) is a negative int and becomes +0, any other is kept as is.
+// (A float max or median needs the compiler to quiet a possible signalling NaN
+// from the MFMA first: two instructions.) Used by every scoring path so that
+// all of them produce the same bits.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }

@@ -67,7 +67,11 @@ __global__ __launch_bounds__(256, 2) void score_prefill_kernel(ScoreArgs a) {
   constexpr bool GROUPED = NHP <= 16 && RT % M4 == 0;
   constexpr int NOUT = GROUPED ? RT / M4 : (NHP <= 8 ? RT : QW);   // output slots of one lane
   // KB: keys per LDS block
-  constexpr int LDK = D + 8;                  // LDS row stride (bf16): 16-byte pad against bank conflicts
+  // LDS key rows: d = 128 rows are unpadded with 16-byte piece p of row k at slot
+  // p ^ (k & 15) (row-wise writes and MFMA-layout reads both spread over all
+  // banks); other widths use a 16-byte pad per row
+  constexpr bool SWZ = D == 128;
+  constexpr int LDK = SWZ ? D : D + 8;        // LDS row stride (bf16)
   constexpr int PPR = D / 8;                  // 16-byte pieces per key row
   constexpr int LPT = KB * PPR / 256;         // pieces each thread moves per block
   static_assert(QW >= 1 && (16 * RT) % NHP == 0 && LPT >= 1, "tiling");
@@ -243,36 +247,48 @@ __global__ __launch_bounds__(256, 2) void score_prefill_kernel(ScoreArgs a) {
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
         const int pc = tid + 256 * i;
-        *reinterpret_cast<u32x4*>(buf + (pc / PPR) * LDK + (pc % PPR) * 8) = v[i];
+        const int row = pc / PPR, piece = pc % PPR;
+        *reinterpret_cast<u32x4*>(buf + row * LDK + (SWZ ? piece ^ (row & 15) : piece) * 8) = v[i];
       }
     };
+    // Blocks in flight in registers while block b is multiplied: two where the
+    // registers allow (one block of MFMA work is shorter than a key load's latency
+    // under load), else one.
+    constexpr int PF = NHP <= 16 && RT <= 4 ? 2 : 1;
+    u32x4 nv[PF][LPT];
     {
       u32x4 v[LPT];
       load_block(0, v);
+#pragma unroll
+      for (int j = 0; j < PF; ++j) load_block(1 + j < nblk ? 1 + j : 0, nv[(1 + j) % PF]);
       store_block(s_k[0], v);
     }
     __syncthreads();
-    for (int b = 0; b < nblk; ++b) {
-      u32x4 nv[LPT];
-      load_block(b + 1 < nblk ? b + 1 : b, nv);   // the next block, requested before this one is used
+    // one block: cur holds block b + 1 (the register sets are named statically, the
+    // loop below alternates them; an index computed at run time would move them
+    // through indexed register access and wait for every load)
+    auto block_step = [&](int b, u32x4 (&cur)[LPT]) {
       const uint16_t* buf = s_k[b & 1];
       const int base = c_begin + b * KB;
       const bool unmasked = base + KB <= lim_min;
-#pragma unroll
-      for (int kt = 0; kt < KB / 16; ++kt) {
+      // Tiles are software-pipelined: the MFMAs of tile kt + 1 go out next to the
+      // epilogue (ReLU, weights, head sum, stores) of tile kt, which does not depend
+      // on them, so neither waits on the other's latency; within a tile the k-step
+      // is outer, so consecutive MFMAs feed different accumulators.
+      auto mma = [&](int kt, floatx4 (&acc)[RT]) {
         u32x4 bv[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          bv[ks] = *reinterpret_cast<const u32x4*>(buf + (kt * 16 + col) * LDK + grp * 8 + ks * 32);
-        // k-step outer: the RT accumulators are independent, so consecutive MFMAs
-        // never wait on each other's results
-        floatx4 acc[RT];
+          bv[ks] = *reinterpret_cast<const u32x4*>(buf + (kt * 16 + col) * LDK +
+                                                   (SWZ ? (4 * ks + grp) ^ col : 4 * ks + grp) * 8);
 #pragma unroll
         for (int r = 0; r < RT; ++r) acc[r] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
           for (int r = 0; r < RT; ++r) acc[r] = mfma_16x16x32(afrag[r][ks], bv[ks], acc[r]);
+      };
+      auto epi = [&](int kt, const floatx4 (&acc)[RT]) {
         float part[RT];
 #pragma unroll
         for (int r = 0; r < RT; ++r)
@@ -315,9 +331,29 @@ __global__ __launch_bounds__(256, 2) void score_prefill_kernel(ScoreArgs a) {
           for (int i = 0; i < NOUT; ++i)
             buffer_store_f32(val[i] + 0.f, oview, s_out < lim[i] ? voff[i] + (uint32_t)s_out * 4u : 0xfffffff0u);
         }
+      };
+      floatx4 acc0[RT], acc1[RT];
+      mma(0, acc0);
+#pragma unroll
+      for (int kt = 0; kt < KB / 16; kt += 2) {
+        if (kt + 1 < KB / 16) mma(kt + 1, acc1);
+        epi(kt, acc0);
+        if (kt + 2 < KB / 16) mma(kt + 2, acc0);
+        if (kt + 1 < KB / 16) epi(kt + 1, acc1);
       }
-      store_block(s_k[(b + 1) & 1], nv);
+      store_block(s_k[(b + 1) & 1], cur);
+      load_block(b + 1 + PF < nblk ? b + 1 + PF : 0, cur);   // block b + 1 + PF takes the freed registers
       __syncthreads();
+    };
+    int b = 0;
+    if constexpr (PF == 2) {
+      for (; b + 1 < nblk; b += 2) {
+        block_step(b, nv[1]);
+        block_step(b + 1, nv[0]);
+      }
+      if (b < nblk) block_step(b, nv[1]);
+    } else {
+      for (; b < nblk; ++b) block_step(b, nv[0]);
     }
   }
 }

@@ -331,7 +331,7 @@ def test_prefill_all_equal_scores(k):
         assert np.all(idx[t][p:] == -1) and np.all(sc[t] == 0), t
 
 
-@pytest.mark.parametrize("d", [32, 64, 256])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
 @pytest.mark.parametrize("H,h", [(8, 2), (40, 5), (64, 16)])
 def test_prefill_shapes(d, H, h):
     """Causal prefill through the LDS-tiled MFMA kernel for every row tiling (4, 8, 16
@@ -410,7 +410,7 @@ def test_empty_batch_noop():
     assert idx.shape == (0, 8)
 
 
-@pytest.mark.parametrize("d", [32, 64, 256])
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
 @pytest.mark.parametrize("H,h", [(8, 2), (40, 5), (64, 16)])
 def test_shapes_head_dims(d, H, h):
     """Other head dims and head counts (padding rows, 48-row tiles), grid-exact."""
