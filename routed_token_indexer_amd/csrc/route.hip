@@ -57,19 +57,36 @@ __device__ __forceinline__ void split_hi_lo(float x, uint32_t& hi, uint32_t& lo)
   lo = bf16_rne_bits(r);
 }
 
-// Sum of the partial block's keys into s[0..D) (all lanes of one wave).
+// Sum of the partial block's keys into s[0..D) (all lanes of one wave), rows in
+// order. The loads go out 16 rows at a time (a load per row and wait would make
+// the sum one memory round trip per key); only the adds are sequential.
 template <int D>
 __device__ __forceinline__ void wave_tail_sum(const RouteArgs& a, int seq, int start, int n_tail, float* s) {
   const int lane = threadIdx.x & 63;
   constexpr int PER = D / 64 > 0 ? D / 64 : 1;
+  constexpr int RB = 16;
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
   if (n_tail > 0 && lane * PER < D) {
     const uint16_t* kp = a.k + ((int64_t)seq * a.Lmax + start) * D + lane * PER;
-    for (int r = 0; r < n_tail; ++r) {
+    for (int r0 = 0; r0 < n_tail; r0 += RB) {
+      uint16_t v[RB][PER];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] += __uint_as_float((uint32_t)kp[(int64_t)r * D + i] << 16);
+      for (int rr = 0; rr < RB; ++rr) {
+        const int r = min(r0 + rr, n_tail - 1);   // rows past the tail re-read the last one and are not added
+#pragma unroll
+        for (int i = 0; i < PER; ++i) v[rr][i] = kp[(int64_t)r * D + i];
+      }
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) {
+        const bool in = r0 + rr < n_tail;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const float x = __uint_as_float((uint32_t)v[rr][i] << 16);
+          acc[i] = in ? acc[i] + x : acc[i];
+        }
+      }
     }
   }
   if (lane * PER < D) {
@@ -96,9 +113,12 @@ __device__ __forceinline__ float tail_dot(const RouteArgs& a, int64_t t, int lan
   float x = 0.f;
   if (lane < a.H) {
     const u32x4* qrow = reinterpret_cast<const u32x4*>(a.q + (t * a.H + lane) * D);
-#pragma unroll 4
+    u32x4 qv[D / 8];   // the whole row requested at once
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) qv[i] = qrow[i];
+#pragma unroll
     for (int i = 0; i < D / 8; ++i) {
-      const u32x4 v = qrow[i];
+      const u32x4 v = qv[i];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         x = fmaf(bf16_lo(v[e]), s[8 * i + 2 * e], x);
@@ -288,10 +308,209 @@ __global__ __launch_bounds__(256) void route_prefill_kernel(RouteArgs a) {
   route_select(a, t, lane, A, x, n_tail);
 }
 
+// prefill, tiled: grid (ceil(T / (4 * QPW))); a workgroup routes QPW consecutive
+// queries per wave. When they all read one sequence, every 64-block chunk of its
+// pooled keys is split into bf16 hi / lo once and staged in LDS (16-byte piece p
+// of block row j at slot p ^ (j & 15)), and each 16-block tile feeds the MFMAs
+// of every query's head rows; a query adds only its complete blocks. Per query
+// the tiles, their order and the MFMA sequence are those of block_affinity, so
+// the aggregates are the same bit for bit. Workgroups whose queries span several
+// sequences route each query on its own wave as route_prefill_kernel does.
+template <int D, int RTQ, int QPW>
+__global__ __launch_bounds__(256, 2) void route_prefill_tiled_kernel(RouteArgs a) {
+  constexpr int KS = D / 32;
+  constexpr int PPR = D / 8;                 // 16-byte bf16 pieces per pooled row
+  constexpr int SB = 64;                     // pooled blocks per LDS stage
+  constexpr int QT = 4 * QPW;
+  constexpr int SPT = SB * PPR / 256;        // staged pieces per thread
+  static_assert(SPT >= 1 && PPR <= 32, "staging");
+  __shared__ __attribute__((aligned(16))) uint16_t s_hi[SB * D], s_lo[SB * D];
+  __shared__ float red[QT][64];
+  __shared__ float stail[QT][D];
+  __shared__ int s_seq[QT], s_nfull[QT], s_shared_seq, s_nmax;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * QT;
+  if (tid < QT) {
+    int seq, p;
+    query_prefix(a, t0 + tid, seq, p);
+    s_seq[tid] = seq;
+    s_nfull[tid] = p / a.B;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int sq = -2, nmax = 0;
+    for (int i = 0; i < QT; ++i) {
+      if (s_seq[i] < 0) continue;
+      sq = (sq == -2 || sq == s_seq[i]) ? s_seq[i] : -3;
+      nmax = max(nmax, s_nfull[i]);
+    }
+    s_shared_seq = sq;   // -2: no valid query, -3: several sequences
+    s_nmax = nmax;
+  }
+  __syncthreads();
+  const int seq_all = s_shared_seq;
+
+  // per query of this wave: head aggregates in red[], then tail, ranking, routed set
+  auto finish = [&](int i) {
+    const int ql = wave * QPW + i;
+    const int64_t t = t0 + ql;
+    if (t >= a.T) return;
+    int seq, p;
+    query_prefix(a, t, seq, p);
+    const int nfull = p / a.B;
+    const int n_tail = p - nfull * a.B;
+    wave_tail_sum<D>(a, seq, nfull * a.B, n_tail, stail[ql]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const float A = red[ql][lane];
+    const float x = n_tail > 0 ? tail_dot<D>(a, t, lane, stail[ql]) : 0.f;
+    route_select(a, t, lane, A, x, n_tail);
+  };
+  auto put_red = [&](int ql, const float (&rs)[RTQ][4]) {
+    if (col == 0) {
+#pragma unroll
+      for (int r = 0; r < RTQ; ++r)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) red[ql][16 * r + 4 * grp + jj] = rs[r][jj];
+    }
+  };
+
+  if (seq_all == -3) {   // several sequences: each query on its own
+#pragma unroll 1
+    for (int i = 0; i < QPW; ++i) {
+      const int ql = wave * QPW + i;
+      const int64_t t = t0 + ql;
+      if (t >= a.T) break;
+      int seq, p;
+      query_prefix(a, t, seq, p);
+      float rs[RTQ][4];
+      block_affinity<D, RTQ>(a, t, seq, 0, p / a.B, 1, rs);
+      put_red(ql, rs);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      finish(i);
+    }
+    return;
+  }
+
+  // ---- one sequence: the wave's query rows as A fragments (zero rows past H or past T)
+  u32x4 afrag[QPW][RTQ][KS];
+  int nf[QPW];
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) {
+    const int ql = wave * QPW + i;
+    const int64_t t = t0 + ql;
+    const bool tv = t < a.T && s_seq[ql] >= 0;
+    nf[i] = tv ? s_nfull[ql] : 0;
+#pragma unroll
+    for (int r = 0; r < RTQ; ++r) {
+      const int head = 16 * r + col;
+      const bool hv = tv && head < a.H;
+      const uint16_t* qp = a.q + ((hv ? t : 0) * a.H + (hv ? head : 0)) * D + grp * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(qp + ks * 32);
+        afrag[i][r][ks] = hv ? v : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+  float rs[QPW][RTQ][4];
+#pragma unroll
+  for (int i = 0; i < QPW; ++i)
+#pragma unroll
+    for (int r = 0; r < RTQ; ++r)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) rs[i][r][jj] = 0.f;
+  const int nmax = s_nmax;
+  const int64_t nblk_seq = a.Lmax / a.B;
+  const float* kb_seq = a.kbar + (int64_t)(seq_all < 0 ? 0 : seq_all) * nblk_seq * D;
+  for (int c0 = 0; c0 < nmax; c0 += SB) {
+    // stage blocks [c0, c0 + SB) as hi / lo (rows past nmax are zero)
+#pragma unroll
+    for (int s = 0; s < SPT; ++s) {
+      const int pc = tid + 256 * s;
+      const int jr = pc / PPR, piece = pc % PPR;
+      const bool bv = c0 + jr < nmax;
+      const float* kp = kb_seq + (int64_t)(bv ? c0 + jr : 0) * D + piece * 8;
+      floatx4 v0 = *reinterpret_cast<const floatx4*>(kp);
+      floatx4 v1 = *reinterpret_cast<const floatx4*>(kp + 4);
+      uint32_t h[8], l[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        split_hi_lo(bv ? v0[e] : 0.f, h[e], l[e]);
+        split_hi_lo(bv ? v1[e] : 0.f, h[4 + e], l[4 + e]);
+      }
+      u32x4 hv4, lv4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        hv4[e] = h[2 * e] | (h[2 * e + 1] << 16);
+        lv4[e] = l[2 * e] | (l[2 * e + 1] << 16);
+      }
+      const int slot = piece ^ (jr & 15);
+      *reinterpret_cast<u32x4*>(s_hi + jr * D + slot * 8) = hv4;
+      *reinterpret_cast<u32x4*>(s_lo + jr * D + slot * 8) = lv4;
+    }
+    __syncthreads();
+    const int nb = min(SB, nmax - c0);
+    for (int jt = 0; jt < nb; jt += 16) {
+      const int jr = jt + col;
+      u32x4 bhi[KS], blo[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int slot = (4 * ks + grp) ^ (jr & 15);
+        bhi[ks] = *reinterpret_cast<const u32x4*>(s_hi + jr * D + slot * 8);
+        blo[ks] = *reinterpret_cast<const u32x4*>(s_lo + jr * D + slot * 8);
+      }
+#pragma unroll
+      for (int i = 0; i < QPW; ++i) {
+        const bool jv = c0 + jr < nf[i];
+#pragma unroll
+        for (int r = 0; r < RTQ; ++r) {
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            acc = mfma_16x16x32(afrag[i][r][ks], bhi[ks], acc);
+            acc = mfma_16x16x32(afrag[i][r][ks], blo[ks], acc);
+          }
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) rs[i][r][jj] += jv ? relu(acc[jj]) : 0.f;
+        }
+      }
+    }
+    __syncthreads();   // the stage is rewritten next
+  }
+  // sum over the 16 block columns (the xor tree of block_affinity), then per query
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) {
+#pragma unroll
+    for (int r = 0; r < RTQ; ++r)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        float v = rs[i][r][jj];
+        v += __shfl_xor(v, 1, kWave);
+        v += __shfl_xor(v, 2, kWave);
+        v += __shfl_xor(v, 4, kWave);
+        v += __shfl_xor(v, 8, kWave);
+        rs[i][r][jj] = v;
+      }
+    put_red(wave * QPW + i, rs[i]);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll 1
+  for (int i = 0; i < QPW; ++i) finish(i);
+}
+
 template <int D, int RTQ>
 hipError_t launch_rtq(const RouteArgs& a, bool prefill, hipStream_t st) {
   if (prefill && !a.fused) {
-    hipLaunchKernelGGL((route_prefill_kernel<D, RTQ>), dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, st, a);
+    constexpr int QPW = D <= 128 ? 2 : 1;
+    hipLaunchKernelGGL((route_prefill_tiled_kernel<D, RTQ, QPW>), dim3((unsigned)((a.T + 4 * QPW - 1) / (4 * QPW))),
+                       dim3(256), 0, st, a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((route_decode_kernel<D, RTQ>), dim3(a.nchunk, (unsigned)a.T), dim3(256), 0, st, a);
