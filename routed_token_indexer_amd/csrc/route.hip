@@ -501,8 +501,59 @@ __global__ __launch_bounds__(256, 2) void route_prefill_tiled_kernel(RouteArgs a
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll 1
-  for (int i = 0; i < QPW; ++i) finish(i);
+  // per query: the partial-block sum, then the tail dot x_g = q_g . S_tail from the
+  // A fragments already in registers (lane (col, grp) holds k-slots 32 ks + 8 grp
+  // .. + 8 of head 16 r + col; the four groups' parts are added across lanes),
+  // instead of reading the query rows from memory a second time
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) {
+    const int ql = wave * QPW + i;
+    const int64_t t = t0 + ql;
+    if (t >= a.T) break;
+    int seq, p;
+    query_prefix(a, t, seq, p);
+    const int nfull = p / a.B;
+    const int n_tail = p - nfull * a.B;
+    wave_tail_sum<D>(a, seq, nfull * a.B, n_tail, stail[ql]);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float x = 0.f;
+    if (n_tail > 0) {
+      float xr[RTQ];
+#pragma unroll
+      for (int r = 0; r < RTQ; ++r) xr[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const floatx4 s0 = *reinterpret_cast<const floatx4*>(&stail[ql][32 * ks + 8 * grp]);
+        const floatx4 s1 = *reinterpret_cast<const floatx4*>(&stail[ql][32 * ks + 8 * grp + 4]);
+#pragma unroll
+        for (int r = 0; r < RTQ; ++r) {
+          const u32x4 v = afrag[i][r][ks];
+          float acc = xr[r];
+          acc = fmaf(bf16_lo(v[0]), s0[0], acc);
+          acc = fmaf(bf16_hi(v[0]), s0[1], acc);
+          acc = fmaf(bf16_lo(v[1]), s0[2], acc);
+          acc = fmaf(bf16_hi(v[1]), s0[3], acc);
+          acc = fmaf(bf16_lo(v[2]), s1[0], acc);
+          acc = fmaf(bf16_hi(v[2]), s1[1], acc);
+          acc = fmaf(bf16_lo(v[3]), s1[2], acc);
+          acc = fmaf(bf16_hi(v[3]), s1[3], acc);
+          xr[r] = acc;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < RTQ; ++r) {
+        xr[r] += __shfl_xor(xr[r], 16, kWave);
+        xr[r] += __shfl_xor(xr[r], 32, kWave);
+      }
+      // lane g = 16 * grp + col takes head g: row tile grp
+#pragma unroll
+      for (int r = 0; r < RTQ; ++r)
+        if (grp == r) x = xr[r];
+    }
+    route_select(a, t, lane, red[ql][lane], x, n_tail);
+  }
 }
 
 template <int D, int RTQ>
