@@ -22,8 +22,10 @@
 //   decode  (few queries, long prefixes): a workgroup takes one query and a
 //           chunk of blocks, its waves split the blocks; a second small kernel
 //           sums the chunk partials in chunk order and selects the heads.
-//   prefill (many queries): a workgroup takes four queries, one per wave, and
-//           each wave walks all complete blocks of its query and selects.
+//   prefill (many queries): a workgroup takes eight consecutive queries, two
+//           per wave; the pooled keys of their sequence are staged in LDS as
+//           hi / lo tiles once for all of them, and each wave selects its
+//           queries' heads.
 #include "misa_common.hpp"
 #include "misa_internal.hpp"
 #include "misa_score_dev.hpp"
@@ -278,36 +280,6 @@ __global__ __launch_bounds__(64) void route_final_kernel(RouteArgs a) {
   route_select(a, t, lane, A, x, n_tail);
 }
 
-// prefill: grid (ceil(T / 4)); wave w routes query 4 * blockIdx.x + w over all its complete blocks.
-template <int D, int RTQ>
-__global__ __launch_bounds__(256) void route_prefill_kernel(RouteArgs a) {
-  __shared__ float red[4][64];
-  __shared__ float stail[4][D];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
-  if (t >= a.T) return;
-  int seq, p;
-  query_prefix(a, t, seq, p);
-  const int nfull = p / a.B;
-  float rs[RTQ][4];
-  block_affinity<D, RTQ>(a, t, seq, 0, nfull, 1, rs);
-  if ((lane & 15) == 0) {
-#pragma unroll
-    for (int r = 0; r < RTQ; ++r)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) red[wave][16 * r + 4 * (lane >> 4) + jj] = rs[r][jj];
-  }
-  const int n_tail = p - nfull * a.B;
-  wave_tail_sum<D>(a, seq, nfull * a.B, n_tail, stail[wave]);
-  // the wave's own LDS rows: a wave-level barrier orders the writes above with the reads below
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const float A = red[wave][lane];
-  const float x = n_tail > 0 ? tail_dot<D>(a, t, lane, stail[wave]) : 0.f;
-  route_select(a, t, lane, A, x, n_tail);
-}
-
 // prefill, tiled: grid (ceil(T / (4 * QPW))); a workgroup routes QPW consecutive
 // queries per wave. When they all read one sequence, every 64-block chunk of its
 // pooled keys is split into bf16 hi / lo once and staged in LDS (16-byte piece p
@@ -315,7 +287,7 @@ __global__ __launch_bounds__(256) void route_prefill_kernel(RouteArgs a) {
 // of every query's head rows; a query adds only its complete blocks. Per query
 // the tiles, their order and the MFMA sequence are those of block_affinity, so
 // the aggregates are the same bit for bit. Workgroups whose queries span several
-// sequences route each query on its own wave as route_prefill_kernel does.
+// sequences route each query on its own wave (block_affinity over its blocks).
 template <int D, int RTQ, int QPW>
 __global__ __launch_bounds__(256, 2) void route_prefill_tiled_kernel(RouteArgs a) {
   constexpr int KS = D / 32;

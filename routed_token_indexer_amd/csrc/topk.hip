@@ -6,13 +6,14 @@
 // first min(k, n) are kept; the set is written in ascending token index, padded
 // with -1. Scores compare as reals (-0 == +0).
 //
-// One workgroup per row: a three-level radix select over an order-preserving
-// 32-bit key (12 + 12 + 8 bits, LDS histograms) finds the k-th key u* and how
-// many keys equal to u* are kept; then each wave compacts its contiguous
-// segment in index order with ballots, so the lowest indices among equal keys
-// win and the output comes out sorted. A row of at most kRowCap scores is
-// staged once into LDS as keys and every pass runs out of LDS; longer rows are
-// re-read from global memory in each pass.
+// One workgroup per row. Rows of up to 32K scores keep their keys (an
+// order-preserving 32-bit map of the scores) in registers: one LDS histogram
+// finds the bin of the k-th key, the few keys of that bin are ranked exactly,
+// and one ballot pass writes the kept set in index order (topk_row_reg_kernel).
+// Rows of heavy ties, and longer rows, take an exact three-level radix select
+// (12 + 12 + 8 bits) whose index-ordered compaction lets the lowest indices win
+// among equal keys (topk_row_kernel; a row of at most kRowCap scores is staged
+// once into LDS, longer rows are re-read in each pass).
 #include "misa_common.hpp"
 #include "misa_internal.hpp"
 #include "misa_select.hpp"
