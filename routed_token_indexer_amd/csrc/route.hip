@@ -22,10 +22,10 @@
 //   decode  (few queries, long prefixes): a workgroup takes one query and a
 //           chunk of blocks, its waves split the blocks; a second small kernel
 //           sums the chunk partials in chunk order and selects the heads.
-//   prefill (many queries): a workgroup takes eight consecutive queries, two
+//   prefill (many queries): a workgroup takes four consecutive queries, one
 //           per wave; the pooled keys of their sequence are staged in LDS as
 //           hi / lo tiles once for all of them, and each wave selects its
-//           queries' heads.
+//           query's heads.
 #include "misa_common.hpp"
 #include "misa_internal.hpp"
 #include "misa_score_dev.hpp"
@@ -299,7 +299,8 @@ __global__ __launch_bounds__(256, 2) void route_prefill_tiled_kernel(RouteArgs a
   __shared__ __attribute__((aligned(16))) uint16_t s_hi[SB * D], s_lo[SB * D];
   __shared__ float red[QT][64];
   __shared__ float stail[QT][D];
-  __shared__ int s_seq[QT], s_nfull[QT], s_shared_seq, s_nmax;
+  __shared__ int s_seq[QT], s_nfull[QT], s_ntail[QT], s_shared_seq, s_nmax;
+  __shared__ int s_tst[2], s_tlen[2];   // staged partial blocks: first block index, rows
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int64_t t0 = (int64_t)blockIdx.x * QT;
@@ -308,6 +309,7 @@ __global__ __launch_bounds__(256, 2) void route_prefill_tiled_kernel(RouteArgs a
     query_prefix(a, t0 + tid, seq, p);
     s_seq[tid] = seq;
     s_nfull[tid] = p / a.B;
+    s_ntail[tid] = p - (p / a.B) * a.B;
   }
   __syncthreads();
   if (tid == 0) {
@@ -473,6 +475,40 @@ __global__ __launch_bounds__(256, 2) void route_prefill_tiled_kernel(RouteArgs a
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // ---- the partial blocks of the workgroup's queries (usually one or two distinct
+  // ones: consecutive positions) are staged in the freed LDS stage, each with one
+  // round trip for the whole workgroup; a block longer than the stage, or a third
+  // one, is summed from memory by its queries' waves
+  if (tid == 0) {
+    int st0 = -1, st1 = -1, len0 = 0, len1 = 0;
+    for (int q = 0; q < QT; ++q) {
+      if (s_seq[q] < 0 || s_ntail[q] == 0) continue;
+      const int sq = s_nfull[q], nt = s_ntail[q];
+      if (st0 < 0 || st0 == sq) {
+        st0 = sq;
+        len0 = max(len0, nt);
+      } else if (st1 < 0 || st1 == sq) {
+        st1 = sq;
+        len1 = max(len1, nt);
+      }
+    }
+    s_tst[0] = st0;
+    s_tst[1] = st1;
+    s_tlen[0] = len0 <= SB ? len0 : 0;   // 0: not staged
+    s_tlen[1] = len1 <= SB ? len1 : 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int len = s_tlen[j];
+    if (len == 0) continue;
+    uint16_t* rows = j == 0 ? s_hi : s_lo;
+    const uint16_t* src = a.k + ((int64_t)(seq_all < 0 ? 0 : seq_all) * a.Lmax + (int64_t)s_tst[j] * a.B) * D;
+    for (int pc = tid; pc < len * PPR; pc += 256)
+      *reinterpret_cast<u32x4*>(rows + pc * 8) = *reinterpret_cast<const u32x4*>(src + (int64_t)pc * 8);
+  }
+  __syncthreads();
+
   // per query: the partial-block sum, then the tail dot x_g = q_g . S_tail from the
   // A fragments already in registers (lane (col, grp) holds k-slots 32 ks + 8 grp
   // .. + 8 of head 16 r + col; the four groups' parts are added across lanes),
@@ -486,7 +522,25 @@ __global__ __launch_bounds__(256, 2) void route_prefill_tiled_kernel(RouteArgs a
     query_prefix(a, t, seq, p);
     const int nfull = p / a.B;
     const int n_tail = p - nfull * a.B;
-    wave_tail_sum<D>(a, seq, nfull * a.B, n_tail, stail[ql]);
+    const int sj = (s_tlen[0] > 0 && s_tst[0] == nfull) ? 0 : ((s_tlen[1] > 0 && s_tst[1] == nfull) ? 1 : -1);
+    if (sj >= 0 && n_tail > 0) {
+      // rows in order from the staged block (the adds of wave_tail_sum)
+      constexpr int PER = D / 64 > 0 ? D / 64 : 1;
+      const uint16_t* rows = sj == 0 ? s_hi : s_lo;
+      if (lane * PER < D) {
+        float acc[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+        for (int r = 0; r < n_tail; ++r)
+#pragma unroll
+          for (int e = 0; e < PER; ++e)
+            acc[e] += __uint_as_float((uint32_t)rows[r * D + lane * PER + e] << 16);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) stail[ql][lane * PER + e] = acc[e];
+      }
+    } else {
+      wave_tail_sum<D>(a, seq, nfull * a.B, n_tail, stail[ql]);
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -531,7 +585,9 @@ __global__ __launch_bounds__(256, 2) void route_prefill_tiled_kernel(RouteArgs a
 template <int D, int RTQ>
 hipError_t launch_rtq(const RouteArgs& a, bool prefill, hipStream_t st) {
   if (prefill && !a.fused) {
-    constexpr int QPW = D <= 128 ? 2 : 1;
+    // one query per wave: 155 registers at d = 128, three workgroups per CU (two
+    // queries per wave share more staging but leave two)
+    constexpr int QPW = 1;
     hipLaunchKernelGGL((route_prefill_tiled_kernel<D, RTQ, QPW>), dim3((unsigned)((a.T + 4 * QPW - 1) / (4 * QPW))),
                        dim3(256), 0, st, a);
     return hipGetLastError();

@@ -601,8 +601,9 @@ hipError_t launch_timed(int kid, K kernel, dim3 grid, dim3 block, hipStream_t st
 template <int D, int RT, bool GATHER>
 hipError_t launch_decode(ScoreArgs a, int64_t max_len, hipStream_t st) {
   if (a.chunk <= 0) {
-    // about 512 workgroups (two per CU), at least 256 keys each
-    int64_t c = 256;
+    // about 512 workgroups (two per CU), at least 512 keys (two iterations) each: a
+    // workgroup of one iteration spends most of its time before its first keys arrive
+    int64_t c = 512;
     while (c < 16384 && c * 512 < max_len * a.T) c *= 2;
     a.chunk = (int)c;
   }
