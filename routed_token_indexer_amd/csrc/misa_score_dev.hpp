@@ -198,13 +198,23 @@ __device__ __forceinline__ bool route_rank(int H, int h, int lane, float w, floa
   }
   rho += 0.f;   // -0 -> +0
   r += 0.f;
-  // j is uniform, so each comparison value is read with v_readlane (no LDS
-  // round trip per head)
+  // rank = heads ahead of this one: larger rho, or equal rho and a lower id.
+  // As one 64-bit key (order-preserving bits of rho, then 63 - id) that is a
+  // single unsigned compare per head; j is uniform, so each head's key bits
+  // are read with v_readlane (no LDS round trip), fully unrolled for H = 64
+  const uint32_t rb = __float_as_uint(rho);
+  const uint32_t kh = (rb & 0x80000000u) ? ~rb : (rb | 0x80000000u);
+  const uint64_t mine = ((uint64_t)kh << 32) | (uint32_t)(63 - lane);
+  auto ahead = [&](int j) {
+    const uint32_t oh = (uint32_t)__builtin_amdgcn_readlane((int)kh, j);
+    return (((uint64_t)oh << 32) | (uint32_t)(63 - j)) > mine ? 1 : 0;
+  };
   int rank = 0;
-  const int rho_bits = __float_as_int(rho);
-  for (int j = 0; j < H; ++j) {
-    const float o = __int_as_float(__builtin_amdgcn_readlane(rho_bits, j));
-    rank += (o > rho || (o == rho && j < lane)) ? 1 : 0;
+  if (H == 64) {
+#pragma unroll
+    for (int j = 0; j < 64; ++j) rank += ahead(j);
+  } else {
+    for (int j = 0; j < H; ++j) rank += ahead(j);
   }
   const bool sel = active && rank < h;
   const uint64_t m = __ballot(sel);

@@ -99,14 +99,17 @@ __device__ __forceinline__ void wave_tail_sum(const RouteArgs& a, int seq, int s
 
 // Rank heads by rho (ties: lower id) and write the routed set. Runs in one
 // wave; lane g < H holds head g's complete-block aggregate A and partial-block dot x.
-__device__ __forceinline__ void route_select(const RouteArgs& a, int64_t t, int lane, float A, float x,
-                                             int n_tail) {
-  const float w = lane < a.H ? a.w[t * a.H + lane] : 0.f;
+__device__ __forceinline__ void route_select_w(const RouteArgs& a, int64_t t, int lane, float w, float A, float x,
+                                               int n_tail) {
   int pos;
   float r;
   const bool sel = route_rank(a.H, a.h, lane, w, A, x, n_tail, pos, r);
   if (sel) a.heads[t * a.h + pos] = lane;
   if (lane < a.H && a.router_key) a.router_key[t * a.H + lane] = r;
+}
+__device__ __forceinline__ void route_select(const RouteArgs& a, int64_t t, int lane, float A, float x,
+                                             int n_tail) {
+  route_select_w(a, t, lane, lane < a.H ? a.w[t * a.H + lane] : 0.f, A, x, n_tail);
 }
 
 // Tail dot x_g = q_g . S_tail for lane g < H (q read from global, S_tail in LDS).
@@ -283,11 +286,13 @@ __global__ __launch_bounds__(64) void route_final_kernel(RouteArgs a) {
 // prefill, tiled: grid (ceil(T / (4 * QPW))); a workgroup routes QPW consecutive
 // queries per wave. When they all read one sequence, every 64-block chunk of its
 // pooled keys is split into bf16 hi / lo once and staged in LDS (16-byte piece p
-// of block row j at slot p ^ (j & 15)), and each 16-block tile feeds the MFMAs
-// of every query's head rows; a query adds only its complete blocks. Per query
-// the tiles, their order and the MFMA sequence are those of block_affinity, so
-// the aggregates are the same bit for bit. Workgroups whose queries span several
-// sequences route each query on its own wave (block_affinity over its blocks).
+// of block row j at slot p ^ (j & SWM): an XOR swizzle that stays inside the
+// row), and each 16-block tile feeds the MFMAs of every query's head rows; a
+// query adds only its complete blocks. Per query the tiles, their order and the
+// MFMA sequence are those of block_affinity, so the aggregates are the same bit
+// for bit; the partial block is staged and summed while the query rows load.
+// Workgroups whose queries span several sequences route each query on its own
+// wave (block_affinity over its blocks).
 template <int D, int RTQ, int QPW>
 __global__ __launch_bounds__(256, 2) void route_prefill_tiled_kernel(RouteArgs a) {
   constexpr int KS = D / 32;
@@ -295,12 +300,14 @@ __global__ __launch_bounds__(256, 2) void route_prefill_tiled_kernel(RouteArgs a
   constexpr int SB = 64;                     // pooled blocks per LDS stage
   constexpr int QT = 4 * QPW;
   constexpr int SPT = SB * PPR / 256;        // staged pieces per thread
+  constexpr int SWM = (PPR < 16 ? PPR : 16) - 1;   // XOR swizzle within the row
   static_assert(SPT >= 1 && PPR <= 32, "staging");
   __shared__ __attribute__((aligned(16))) uint16_t s_hi[SB * D], s_lo[SB * D];
   __shared__ float red[QT][64];
   __shared__ float stail[QT][D];
   __shared__ int s_seq[QT], s_nfull[QT], s_ntail[QT], s_shared_seq, s_nmax;
-  __shared__ int s_tst[2], s_tlen[2];   // staged partial blocks: first block index, rows
+  __shared__ __attribute__((aligned(16))) uint16_t s_tail[SB * D];   // rows of the staged partial block
+  __shared__ int s_tst, s_tlen;   // staged partial block: first block index, rows (0: none)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int64_t t0 = (int64_t)blockIdx.x * QT;
@@ -370,7 +377,44 @@ __global__ __launch_bounds__(256, 2) void route_prefill_tiled_kernel(RouteArgs a
     return;
   }
 
-  // ---- one sequence: the wave's query rows as A fragments (zero rows past H or past T)
+  // ---- one sequence. The rows of the queries' partial block (consecutive
+  // positions share it, except across a block boundary) are requested first,
+  // then the head weights and the query rows; staging the partial block and
+  // summing it per query then overlap the wait for the query rows, since loads
+  // complete in order
+  if (tid == 0) {
+    int st = -1, len = 0;
+    for (int q = 0; q < QT; ++q) {
+      if (s_seq[q] < 0 || s_ntail[q] == 0) continue;
+      if (st < 0 || st == s_nfull[q]) {
+        st = s_nfull[q];
+        len = max(len, s_ntail[q]);
+      }
+    }
+    s_tst = st;
+    s_tlen = len <= SB ? len : 0;
+  }
+  __syncthreads();
+  const int tst = s_tst, tlen = s_tlen;
+  u32x4 tr[SPT];
+  {
+    const uint16_t* src = a.k + ((int64_t)(seq_all < 0 ? 0 : seq_all) * a.Lmax + (int64_t)(tst < 0 ? 0 : tst) * a.B) * D;
+#pragma unroll
+    for (int s = 0; s < SPT; ++s) {
+      const int pc = tid + 256 * s;
+      if (pc < tlen * PPR) tr[s] = *reinterpret_cast<const u32x4*>(src + (int64_t)pc * 8);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // (a volatile load from a clamped index: issued here, not moved next to its use)
+  float wq[QPW];
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) {
+    const int64_t t = t0 + wave * QPW + i;
+    const bool ok = t < a.T && lane < a.H;
+    const float v = *reinterpret_cast<const volatile float*>(a.w + (ok ? t * a.H + lane : 0));
+    wq[i] = ok ? v : 0.f;
+  }
   u32x4 afrag[QPW][RTQ][KS];
   int nf[QPW];
 #pragma unroll
@@ -391,31 +435,31 @@ __global__ __launch_bounds__(256, 2) void route_prefill_tiled_kernel(RouteArgs a
       }
     }
   }
-  float rs[QPW][RTQ][4];
-#pragma unroll
-  for (int i = 0; i < QPW; ++i)
-#pragma unroll
-    for (int r = 0; r < RTQ; ++r)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) rs[i][r][jj] = 0.f;
   const int nmax = s_nmax;
   const int64_t nblk_seq = a.Lmax / a.B;
   const float* kb_seq = a.kbar + (int64_t)(seq_all < 0 ? 0 : seq_all) * nblk_seq * D;
-  for (int c0 = 0; c0 < nmax; c0 += SB) {
-    // stage blocks [c0, c0 + SB) as hi / lo (rows past nmax are zero)
+  floatx4 sv[SPT][2];
+  auto stage_load = [&](int c0) {   // pooled rows [c0, c0 + SB) (rows past nmax read row 0)
+#pragma unroll
+    for (int s = 0; s < SPT; ++s) {
+      const int pc = tid + 256 * s;
+      const int jr = pc / PPR, piece = pc % PPR;
+      const float* kp = kb_seq + (int64_t)(c0 + jr < nmax ? c0 + jr : 0) * D + piece * 8;
+      sv[s][0] = *reinterpret_cast<const floatx4*>(kp);
+      sv[s][1] = *reinterpret_cast<const floatx4*>(kp + 4);
+    }
+  };
+  auto stage_store = [&](int c0) {   // as hi / lo (rows past nmax are zero)
 #pragma unroll
     for (int s = 0; s < SPT; ++s) {
       const int pc = tid + 256 * s;
       const int jr = pc / PPR, piece = pc % PPR;
       const bool bv = c0 + jr < nmax;
-      const float* kp = kb_seq + (int64_t)(bv ? c0 + jr : 0) * D + piece * 8;
-      floatx4 v0 = *reinterpret_cast<const floatx4*>(kp);
-      floatx4 v1 = *reinterpret_cast<const floatx4*>(kp + 4);
       uint32_t h[8], l[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        split_hi_lo(bv ? v0[e] : 0.f, h[e], l[e]);
-        split_hi_lo(bv ? v1[e] : 0.f, h[4 + e], l[4 + e]);
+        split_hi_lo(bv ? sv[s][0][e] : 0.f, h[e], l[e]);
+        split_hi_lo(bv ? sv[s][1][e] : 0.f, h[4 + e], l[4 + e]);
       }
       u32x4 hv4, lv4;
 #pragma unroll
@@ -423,18 +467,84 @@ __global__ __launch_bounds__(256, 2) void route_prefill_tiled_kernel(RouteArgs a
         hv4[e] = h[2 * e] | (h[2 * e + 1] << 16);
         lv4[e] = l[2 * e] | (l[2 * e + 1] << 16);
       }
-      const int slot = piece ^ (jr & 15);
+      const int slot = piece ^ (jr & SWM);
       *reinterpret_cast<u32x4*>(s_hi + jr * D + slot * 8) = hv4;
       *reinterpret_cast<u32x4*>(s_lo + jr * D + slot * 8) = lv4;
     }
-    __syncthreads();
+  };
+  // the first stage is requested with the rest, so that every load of the
+  // prologue is in flight at once
+  if (nmax > 0) stage_load(0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 0; s < SPT; ++s) {
+    const int pc = tid + 256 * s;
+    if (pc < tlen * PPR) *reinterpret_cast<u32x4*>(s_tail + pc * 8) = tr[s];
+  }
+  if (nmax > 0) stage_store(0);
+  __syncthreads();
+  // per query: the partial-block sum S_tail, rows in order (the adds of
+  // wave_tail_sum), from the staged rows 16 at a time so that the LDS reads
+  // overlap; a second distinct partial block is summed from memory
+#pragma unroll
+  for (int i = 0; i < QPW; ++i) {
+    const int ql = wave * QPW + i;
+    const int seq = s_seq[ql];
+    const int nfull = seq < 0 ? 0 : s_nfull[ql];
+    const int n_tail = seq < 0 || t0 + ql >= a.T ? 0 : s_ntail[ql];
+    if (n_tail == 0) continue;
+    if (tlen > 0 && tst == nfull) {
+      constexpr int PER = D / 64 > 0 ? D / 64 : 1;
+      constexpr int RB = 16;
+      if (lane * PER < D) {
+        float acc[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+        for (int r0 = 0; r0 < n_tail; r0 += RB) {
+          uint16_t v[RB][PER];
+#pragma unroll
+          for (int rr = 0; rr < RB; ++rr) {
+            const int r = min(r0 + rr, n_tail - 1);   // rows past the tail re-read the last one, not added
+#pragma unroll
+            for (int e = 0; e < PER; ++e) v[rr][e] = s_tail[r * D + lane * PER + e];
+          }
+#pragma unroll
+          for (int rr = 0; rr < RB; ++rr) {
+            const bool in = r0 + rr < n_tail;
+#pragma unroll
+            for (int e = 0; e < PER; ++e) {
+              const float x = __uint_as_float((uint32_t)v[rr][e] << 16);
+              acc[e] = in ? acc[e] + x : acc[e];
+            }
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < PER; ++e) stail[ql][lane * PER + e] = acc[e];
+      }
+    } else {
+      wave_tail_sum<D>(a, seq, nfull * a.B, n_tail, stail[ql]);
+    }
+  }
+  float rs[QPW][RTQ][4];
+#pragma unroll
+  for (int i = 0; i < QPW; ++i)
+#pragma unroll
+    for (int r = 0; r < RTQ; ++r)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) rs[i][r][jj] = 0.f;
+  for (int c0 = 0; c0 < nmax; c0 += SB) {
+    if (c0 > 0) {
+      stage_load(c0);
+      stage_store(c0);
+      __syncthreads();
+    }
     const int nb = min(SB, nmax - c0);
     for (int jt = 0; jt < nb; jt += 16) {
       const int jr = jt + col;
       u32x4 bhi[KS], blo[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int slot = (4 * ks + grp) ^ (jr & 15);
+        const int slot = (4 * ks + grp) ^ (jr & SWM);
         bhi[ks] = *reinterpret_cast<const u32x4*>(s_hi + jr * D + slot * 8);
         blo[ks] = *reinterpret_cast<const u32x4*>(s_lo + jr * D + slot * 8);
       }
@@ -456,7 +566,12 @@ __global__ __launch_bounds__(256, 2) void route_prefill_tiled_kernel(RouteArgs a
     }
     __syncthreads();   // the stage is rewritten next
   }
-  // sum over the 16 block columns (the xor tree of block_affinity), then per query
+  // sum over the 16 block columns: the pairs of block_affinity's xor tree, as
+  // DPP moves inside each 16-lane row. After the steps over lane ^ 1 and
+  // lane ^ 2 every lane of a quad holds the same value, so its mirror partner
+  // in the other quad (and then in the other half row) gives the same sum as
+  // the lane ^ 4 (lane ^ 8) partner, bit for bit
+#define MISA_DPP_ADD(v, ctrl) ((v) + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), (ctrl), 0xf, 0xf, false)))
 #pragma unroll
   for (int i = 0; i < QPW; ++i) {
 #pragma unroll
@@ -464,86 +579,28 @@ __global__ __launch_bounds__(256, 2) void route_prefill_tiled_kernel(RouteArgs a
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         float v = rs[i][r][jj];
-        v += __shfl_xor(v, 1, kWave);
-        v += __shfl_xor(v, 2, kWave);
-        v += __shfl_xor(v, 4, kWave);
-        v += __shfl_xor(v, 8, kWave);
+        v = MISA_DPP_ADD(v, 0xb1);    // quad_perm [1, 0, 3, 2]: lane ^ 1
+        v = MISA_DPP_ADD(v, 0x4e);    // quad_perm [2, 3, 0, 1]: lane ^ 2
+        v = MISA_DPP_ADD(v, 0x141);   // row_half_mirror
+        v = MISA_DPP_ADD(v, 0x140);   // row_mirror
         rs[i][r][jj] = v;
       }
     put_red(wave * QPW + i, rs[i]);
   }
+#undef MISA_DPP_ADD
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // ---- the partial blocks of the workgroup's queries (usually one or two distinct
-  // ones: consecutive positions) are staged in the freed LDS stage, each with one
-  // round trip for the whole workgroup; a block longer than the stage, or a third
-  // one, is summed from memory by its queries' waves
-  if (tid == 0) {
-    int st0 = -1, st1 = -1, len0 = 0, len1 = 0;
-    for (int q = 0; q < QT; ++q) {
-      if (s_seq[q] < 0 || s_ntail[q] == 0) continue;
-      const int sq = s_nfull[q], nt = s_ntail[q];
-      if (st0 < 0 || st0 == sq) {
-        st0 = sq;
-        len0 = max(len0, nt);
-      } else if (st1 < 0 || st1 == sq) {
-        st1 = sq;
-        len1 = max(len1, nt);
-      }
-    }
-    s_tst[0] = st0;
-    s_tst[1] = st1;
-    s_tlen[0] = len0 <= SB ? len0 : 0;   // 0: not staged
-    s_tlen[1] = len1 <= SB ? len1 : 0;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int len = s_tlen[j];
-    if (len == 0) continue;
-    uint16_t* rows = j == 0 ? s_hi : s_lo;
-    const uint16_t* src = a.k + ((int64_t)(seq_all < 0 ? 0 : seq_all) * a.Lmax + (int64_t)s_tst[j] * a.B) * D;
-    for (int pc = tid; pc < len * PPR; pc += 256)
-      *reinterpret_cast<u32x4*>(rows + pc * 8) = *reinterpret_cast<const u32x4*>(src + (int64_t)pc * 8);
-  }
-  __syncthreads();
-
-  // per query: the partial-block sum, then the tail dot x_g = q_g . S_tail from the
-  // A fragments already in registers (lane (col, grp) holds k-slots 32 ks + 8 grp
-  // .. + 8 of head 16 r + col; the four groups' parts are added across lanes),
-  // instead of reading the query rows from memory a second time
+  // per query: the tail dot x_g = q_g . S_tail from the A fragments already in
+  // registers (lane (col, grp) holds k-slots 32 ks + 8 grp .. + 8 of head
+  // 16 r + col; the four groups' parts are added across lanes), instead of
+  // reading the query rows from memory a second time
 #pragma unroll
   for (int i = 0; i < QPW; ++i) {
     const int ql = wave * QPW + i;
     const int64_t t = t0 + ql;
     if (t >= a.T) break;
-    int seq, p;
-    query_prefix(a, t, seq, p);
-    const int nfull = p / a.B;
-    const int n_tail = p - nfull * a.B;
-    const int sj = (s_tlen[0] > 0 && s_tst[0] == nfull) ? 0 : ((s_tlen[1] > 0 && s_tst[1] == nfull) ? 1 : -1);
-    if (sj >= 0 && n_tail > 0) {
-      // rows in order from the staged block (the adds of wave_tail_sum)
-      constexpr int PER = D / 64 > 0 ? D / 64 : 1;
-      const uint16_t* rows = sj == 0 ? s_hi : s_lo;
-      if (lane * PER < D) {
-        float acc[PER];
-#pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-        for (int r = 0; r < n_tail; ++r)
-#pragma unroll
-          for (int e = 0; e < PER; ++e)
-            acc[e] += __uint_as_float((uint32_t)rows[r * D + lane * PER + e] << 16);
-#pragma unroll
-        for (int e = 0; e < PER; ++e) stail[ql][lane * PER + e] = acc[e];
-      }
-    } else {
-      wave_tail_sum<D>(a, seq, nfull * a.B, n_tail, stail[ql]);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int n_tail = s_seq[ql] < 0 ? 0 : s_ntail[ql];
     float x = 0.f;
     if (n_tail > 0) {
       float xr[RTQ];
@@ -578,7 +635,7 @@ __global__ __launch_bounds__(256, 2) void route_prefill_tiled_kernel(RouteArgs a
       for (int r = 0; r < RTQ; ++r)
         if (grp == r) x = xr[r];
     }
-    route_select(a, t, lane, red[ql][lane], x, n_tail);
+    route_select_w(a, t, lane, wq[i], red[ql][lane], x, n_tail);
   }
 }
 

@@ -425,6 +425,22 @@ def test_shapes_head_dims(d, H, h):
     np.testing.assert_array_equal(di.cpu().numpy(), od)
 
 
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
+@pytest.mark.parametrize("H,h", [(8, 2), (32, 8), (40, 5), (64, 16)])
+def test_prefill_route_shapes(d, H, h):
+    """The prefill router (pooled-key tiles staged in LDS, 32-head MFMA tiles) for
+    every head dim (staged rows of 4..32 sixteen-byte pieces), head counts that
+    leave zero rows in a tile, ragged partial blocks: grid-exact head sets, and
+    Gaussian head sets equal up to near-ties."""
+    for mode in ("grid", "gauss"):
+        x = make_inputs("c2", mode=mode, L=300, T=300, H=H, d=d, h=h, B=32, topk=50)
+        dev = upload(x)
+        kbar = M.pool_keys(dev["k"], x.cfg.B)
+        heads = M.route(dev["q"], dev["w"], dev["k"], kbar, dev["q_seq"], dev["q_len"], x.cfg.B, h).cpu().numpy()
+        qs = list(range(0, 300, 7)) + [31, 32, 33, 63, 64, 65, 299]
+        check_router(x, heads[qs], qs, h, exact=mode == "grid")
+
+
 def test_non_power_of_two_block():
     x = make_inputs("c1", mode="gauss", L=2000, T=4, nseq=4, B=48, topk=200)
     dev = upload(x)
