@@ -332,6 +332,7 @@ __device__ __forceinline__ void general_select(const uint32_t (&u)[EPT], FV fres
 // The select falls back to an exact multi-level radix over the whole row when
 // bin d holds more than kCandCap keys (heavy ties, e.g. exactly representable
 // grids) or the row holds the padding key itself.
+constexpr int kNonTemporal = 2;   // buffer cache policy bit: streaming access
 constexpr int kWinBits = 26;     // window of 2^26 key units: 8 octaves of positive floats
 constexpr int kBinShift = kWinBits - 12;
 constexpr int kCandCap = 512;    // keys of the threshold bin ranked in LDS
@@ -407,7 +408,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MANY ? 8 : N
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
     if (j >= nvs) continue;
-    u[j] = buffer_load_u32(rview, (uint32_t)base * 4u, 256u * j);   // raw bits; keys in place below
+    // raw bits (keys in place below); non-temporal: every score is read once
+    u[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rview, (int)((uint32_t)base * 4u), (int)(256u * j),
+                                                          kNonTemporal);
     if constexpr (kPrefetchIds) ids[j] = (int32_t)buffer_load_u32(iview, (uint32_t)base * 4u, 256u * j);
   }
   if (tid == 0) s_m = 0u;
