@@ -98,6 +98,7 @@ int64_t topk_row_reg_max();
 // global memory (level-1 histogram, candidate list, per-chunk offsets).
 struct SplitTopkWs {
   uint32_t* hist;      // [T][4096] level-1 histogram (zero on entry)
+  uint32_t* hist2;     // [T][4096] key bits 8..19 of the level-1 threshold bin's keys (zero on entry)
   uint32_t* state;     // [T][8] threshold key and how many keys equal to it are kept
   uint32_t* counter;   // [T][4] candidate-list cursor, arrivals of the filter (zero on entry)
   uint32_t* ndef;      // [T][nchunk] keys above the level-1 threshold bin in each chunk

@@ -9,11 +9,13 @@
 //               the row's global histogram (atomics; the decode scoring kernel
 //               usually builds it instead).
 //   2. filter   each chunk reads the finished histogram, finds the threshold
-//               bin b1, counts its keys above b1 and appends the keys of bin b1
-//               (key, index) to the row's candidate list. The last chunk of the
-//               row to finish resolves the exact threshold key among the
-//               candidates and turns the per-chunk counts into per-chunk output
-//               offsets.
+//               bin b1, counts its keys above b1, appends the keys of bin b1
+//               (key, index) to the row's candidate list and counts their next
+//               12 key bits into the row's level-2 histogram. The last chunk of
+//               the row to finish resolves the exact threshold key from the
+//               level-2 histogram (and, when its threshold bin is not kept
+//               whole, the low 8 bits of that bin's few candidates) and turns
+//               the per-chunk counts into per-chunk output offsets.
 //   3. compact  each chunk writes its kept indices in index order from its
 //               offset (ballots inside waves, counts across waves).
 // Within a launch, chunks hand data to the last one through device-coherent
@@ -124,12 +126,14 @@ __global__ __launch_bounds__(kThreads) void split_hist_kernel(TopkArgs a, SplitT
 
 // Every chunk finds the row's threshold bin b1 from the finished histogram,
 // counts its keys above b1 and appends the keys of bin b1 (key, index) to the
-// row's candidate list (one cursor reservation per workgroup). The last chunk
-// of the row to arrive then
-//   - resolves the threshold key thr among the candidates: a radix select on
-//     the candidates' low 20 bits, relative to their minimum (all of them share
-//     the top 12 bits b1), and how many keys equal to thr are kept (krem; all
-//     of them when the select ended on a bin kept whole);
+// row's candidate list (one cursor reservation per workgroup), and counts key
+// bits 8..19 of those keys into the row's level-2 histogram. The last chunk of
+// the row to arrive then
+//   - resolves the threshold key thr: the level-2 threshold bin b2 (all the
+//     candidates share the top 12 bits b1); when b2 is not kept whole, a
+//     256-bin histogram of the low 8 bits of its keys (usually one or two)
+//     gives the rest, and how many keys equal to thr are kept (krem; all of
+//     them when b2 is kept whole);
 //   - counts the kept candidates of every chunk, and writes each chunk's output
 //     offset (keys kept in the chunks before it) and the number of keys equal
 //     to thr in front of it, for the compaction launch.
@@ -141,8 +145,8 @@ __global__ __launch_bounds__(kThreads) void split_filter_kernel(TopkArgs a, Spli
   __shared__ uint32_t wcnt[kWaves], wdef[kWaves], wbase[kWaves];
   __shared__ uint32_t s_last;
   // the last chunk only
-  __shared__ RadixScratch<> rs;
-  __shared__ uint32_t wmin[kWaves], wmax[kWaves], wsum2[3][kWaves];
+  __shared__ uint32_t s_p[kCandReg];   // level-3 histogram, then the list prefix
+  __shared__ uint32_t wsum2[3][kWaves], sh2[4], sh3[4];
   __shared__ uint32_t cgt[kMaxChunks], ceq[kMaxChunks];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t = blockIdx.y;
@@ -154,8 +158,14 @@ __global__ __launch_bounds__(kThreads) void split_filter_kernel(TopkArgs a, Spli
   uint32_t u[EPT];
   bool in[EPT];
   load_chunk<EPT>(a.scores + t * a.stride, e0, n, u, in);
+  // the row's histogram: all words requested before the first wait (a strided
+  // copy loop would wait for each load in turn)
   const uint32_t* gh = w.hist + t * kBins;
-  for (int i = tid; i < kBins; i += kThreads) lh[i] = gh[i];
+  uint32_t hv[kBins / kThreads];
+#pragma unroll
+  for (int k = 0; k < kBins / kThreads; ++k) hv[k] = gh[tid + k * kThreads];
+#pragma unroll
+  for (int k = 0; k < kBins / kThreads; ++k) lh[tid + k * kThreads] = hv[k];
   __syncthreads();
   find_threshold(lh, kBins, (uint32_t)a.k, wsum, sh);
   const uint32_t b1 = sh[0], krem1 = sh[1], m_all = lh[b1];
@@ -168,6 +178,12 @@ __global__ __launch_bounds__(kThreads) void split_filter_kernel(TopkArgs a, Spli
     mk[j] = __ballot(in[j] && bin == b1);
     ncand += (uint32_t)__popcll(mk[j]);
   }
+  // level 2: bits 8..19 of the keys of bin b1 (device-scope atomics, complete
+  // before this chunk's arrival below)
+  uint32_t* h2 = w.hist2 + t * kBins;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j)
+    if ((mk[j] >> lane) & 1ull) atomicAdd(&h2[(u[j] >> 8) & 0xfffu], 1u);
   ndef = wave_sum(ndef);
   if (lane == 0) {
     wdef[wave] = ndef;
@@ -219,17 +235,22 @@ __global__ __launch_bounds__(kThreads) void split_filter_kernel(TopkArgs a, Spli
   const uint32_t m = m_all < (uint32_t)w.cap ? m_all : (uint32_t)w.cap;
   const bool inreg = m <= (uint32_t)kCandReg;
   uint64_t cv[8];
+  // unconditional loads from a clamped index (m >= 1: bin b1 holds the krem1-th
+  // key), so that all of them go out before the first wait
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const uint32_t i = (uint32_t)(8 * tid + j);
-    cv[j] = (inreg && i < m) ? load_coherent(cand + i) : 0ull;
+    const uint64_t x = load_coherent(cand + (i < m ? i : m - 1u));
+    cv[j] = (inreg && i < m) ? x : 0ull;
   }
-  uint32_t nd_c = 0;
-  uint64_t sg = 0;
-  if (tid < nact) {
-    nd_c = load_coherent(w.ndef + t * w.nchunk + tid);
-    sg = load_coherent(reinterpret_cast<const uint64_t*>(w.seg) + t * w.nchunk + tid);
-  }
+  const int tc = tid < nact ? tid : 0;
+  const uint32_t nd_l = load_coherent(w.ndef + t * w.nchunk + tc);
+  const uint64_t sg_l = load_coherent(reinterpret_cast<const uint64_t*>(w.seg) + t * w.nchunk + tc);
+  // the level-2 histogram, requested with the list (one round trip for all)
+  constexpr int H2PT = kBins / kThreads;
+  uint32_t h2v[H2PT];
+#pragma unroll
+  for (int k = 0; k < H2PT; ++k) h2v[k] = load_coherent(w.hist2 + t * kBins + tid + k * kThreads);
   // visit(f): f(key, index) for each of this thread's candidates
   auto visit = [&](auto&& f) {
     if (inreg) {
@@ -243,32 +264,42 @@ __global__ __launch_bounds__(kThreads) void split_filter_kernel(TopkArgs a, Spli
       }
     }
   };
-  radix_clear(rs);
   if (!inreg)
     for (int i = tid; i < kMaxChunks; i += kThreads) {
       cgt[i] = 0;
       ceq[i] = 0;
     }
-  uint32_t lo = 0xfffffu, hi = 0u;
-  visit([&](uint32_t key, uint32_t) {
-    lo = min(lo, key & 0xfffffu);
-    hi = max(hi, key & 0xfffffu);
-  });
-  block_minmax(lo, hi, wmin, wmax);
-  const int nbits = hi <= lo ? 0 : 32 - __clz(hi - lo);
-  uint32_t prefix, pmask, krem = krem1;
-  bool full;
-  radix_select([&](auto&& f) { visit([&](uint32_t key, uint32_t) { f((key & 0xfffffu) - lo); }); }, nbits, prefix,
-               pmask, krem, full, rs);
-  // kept: keys > thr, and krem keys == thr (all of them when the bin was kept whole)
-  const uint32_t thr = (b1 << 20) | (lo + prefix);
-  const uint32_t krem_eq = full ? krem : 0xffffffffu;
+  // level 2: the threshold sub-bin b2 of bits 8..19 among the m keys of bin b1
+  uint32_t* const h3 = s_p;   // level 3: 256 bins of the low 8 bits
+  const uint32_t nd_c = tid < nact ? nd_l : 0u;
+  const uint64_t sg = tid < nact ? sg_l : 0ull;
+#pragma unroll
+  for (int k = 0; k < H2PT; ++k) lh[tid + k * kThreads] = h2v[k];
+  if (tid < 256) h3[tid] = 0u;
+  __syncthreads();
+  find_threshold(lh, kBins, krem1, wsum2[0], sh2);
+  const uint32_t b2 = sh2[0], krem2 = sh2[1];
+  uint32_t thr, krem_eq;
+  if (sh2[2]) {
+    // the sub-bin is kept whole: every key from its lowest value up
+    thr = (b1 << 20) | (b2 << 8);
+    krem_eq = 0xffffffffu;
+  } else {
+    // level 3: the low 8 bits of the (usually few) keys of sub-bin b2
+    visit([&](uint32_t key, uint32_t) {
+      if (((key >> 8) & 0xfffu) == b2) atomicAdd(&h3[key & 0xffu], 1u);
+    });
+    __syncthreads();
+    find_threshold(h3, 256, krem2, wsum2[1], sh3);
+    thr = (b1 << 20) | (b2 << 8) | sh3[0];
+    krem_eq = sh3[1];   // all 32 bits resolved: the first krem_eq keys equal to thr
+  }
   // ---- kept candidates of every chunk (keys above thr, keys equal to thr)
   uint32_t gt_c = 0, eq_c = 0;
   if (inreg) {
     // prefix over the list of (above << 16 | equal), m <= 8192 keeps both
-    // halves below 2^16; the radix histograms are free again and hold it
-    uint32_t* P = &rs.hist[0][0];
+    // halves below 2^16; the level-3 histogram is free again
+    uint32_t* P = s_p;
     uint32_t loc[8], run = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -360,23 +391,41 @@ __global__ __launch_bounds__(kThreads) void split_compact_kernel(TopkArgs a, Spl
   constexpr int CH = kThreads * EPT;
   const int64_t e0 = (int64_t)c * CH;
 
-  // dense query rows (all heads) staged in LDS for the re-scoring; requested
-  // first so that the loads overlap the selection
+  // dense query rows (all heads) for the re-scoring: requested first, held in
+  // registers while the selection runs, and staged in LDS (stage_q) only before
+  // the barrier that precedes the re-scoring, so that no wait for them comes
+  // earlier
   const uint16_t* kseq = nullptr;
+  constexpr int PIECES = 16 * RT * D / 8;   // 16-byte pieces of the padded row block
+  constexpr int QPT = RESCORE ? (PIECES + kThreads - 1) / kThreads : 1;
+  // (loads from clamped addresses; rows past H are zeroed only when staged)
+  u32x4 qv[QPT];
+  float wq = 0.f;
   if constexpr (RESCORE) {
     const int seq = a.q_seq[t];
     kseq = r.k + (int64_t)((seq >= 0 && seq < a.nseq) ? seq : 0) * a.Lmax * D + grp * 8;
-    constexpr int PIECES = 16 * RT * D / 8;   // 16-byte pieces of the padded row block
-    for (int i = tid; i < PIECES; i += kThreads) {
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+      const int i = tid + k * kThreads;
       const int rr = i / (D / 8), cc = (i % (D / 8)) * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (rr < r.H) v = *reinterpret_cast<const u32x4*>(r.q + (t * r.H + rr) * D + cc);
-      *reinterpret_cast<u32x4*>(s_q + rr * LDQ + cc) = v;
+      const bool ok = i < PIECES && rr < r.H;
+      qv[k] = *reinterpret_cast<const u32x4*>(r.q + (t * r.H + (ok ? rr : 0)) * D + (ok ? cc : 0));
     }
-    if (tid < 16 * RT) s_w[tid] = tid < r.H ? r.w[t * r.H + tid] : 0.f;
+    wq = r.w[t * r.H + (tid < r.H ? tid : 0)];
     if (r.hist)
       for (int i = tid; i < kBins; i += kThreads) lh[i] = 0;
   }
+  auto stage_q = [&]() {
+    if constexpr (RESCORE) {
+#pragma unroll
+      for (int k = 0; k < QPT; ++k) {
+        const int i = tid + k * kThreads;
+        const int rr = i / (D / 8), cc = (i % (D / 8)) * 8;
+        if (i < PIECES) *reinterpret_cast<u32x4*>(s_q + rr * LDQ + cc) = rr < r.H ? qv[k] : u32x4{0u, 0u, 0u, 0u};
+      }
+      if (tid < 16 * RT) s_w[tid] = tid < r.H ? wq : 0.f;
+    }
+  };
   uint32_t off = 0, nsel = 0;
 
   if (n <= a.k) {
@@ -392,6 +441,7 @@ __global__ __launch_bounds__(kThreads) void split_compact_kernel(TopkArgs a, Spl
     if constexpr (RESCORE) {
       off = (uint32_t)e0;
       nsel = e1 > e0 ? (uint32_t)(e1 - e0) : 0u;
+      stage_q();
       __syncthreads();
     }
     // padding [n, k), spread over the row's chunks
@@ -455,6 +505,7 @@ __global__ __launch_bounds__(kThreads) void split_compact_kernel(TopkArgs a, Spl
       sel_run += (uint32_t)__popcll(msel);
     }
     if constexpr (!RESCORE) return;
+    stage_q();
     if (lane == 0) wend[wave] = sel_run;
     __syncthreads();
     off = sel_before;
@@ -496,14 +547,14 @@ bool use_split_topk(int64_t T, int64_t max_len) {
   return T <= 4096 && max_len > topk_row_reg_max() && max_len <= (int64_t)kMaxChunks * kThreads * 4;
 }
 
-int64_t split_topk_zero_words(int64_t T) { return (int64_t)(al((size_t)T * (kBins + 4) * 4) / 4); }
+int64_t split_topk_zero_words(int64_t T) { return (int64_t)(al((size_t)T * (2 * kBins + 4) * 4) / 4); }
 
 inline int64_t cand_cap(int64_t max_len) { return max_len; }
 
 size_t split_topk_ws_bytes(int64_t T, int64_t max_len) {
   const int chunk = split_chunk(max_len);
   const int64_t nchunk = (max_len + chunk - 1) / chunk;
-  return al((size_t)T * (kBins + 4) * 4) + al((size_t)T * 8 * 4) + 3 * al((size_t)T * nchunk * 4) +
+  return al((size_t)T * (2 * kBins + 4) * 4) + al((size_t)T * 8 * 4) + 3 * al((size_t)T * nchunk * 4) +
          al((size_t)T * nchunk * 8) + al((size_t)T * cand_cap(max_len) * 8);
 }
 
@@ -513,10 +564,11 @@ SplitTopkWs split_topk_carve(void* base, int64_t T, int64_t max_len) {
   w.nchunk = (int)((max_len + w.chunk - 1) / w.chunk);
   w.cap = cand_cap(max_len);
   char* p = static_cast<char*>(base);
-  // zeroed region first: histogram and counters
+  // zeroed region first: histograms and counters
   w.hist = reinterpret_cast<uint32_t*>(p);
-  w.counter = w.hist + T * kBins;
-  p += al((size_t)T * (kBins + 4) * 4);
+  w.hist2 = w.hist + T * kBins;
+  w.counter = w.hist2 + T * kBins;
+  p += al((size_t)T * (2 * kBins + 4) * 4);
   w.state = reinterpret_cast<uint32_t*>(p);
   p += al((size_t)T * 8 * 4);
   w.ndef = reinterpret_cast<uint32_t*>(p);
