@@ -365,16 +365,41 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MANY ? 8 : N
   const int32_t* imap = a.imap ? a.imap + t * (int64_t)a.kc : nullptr;
 
   if (n <= k) {
-    for (int j = tid; j < k; j += NT) {
-      if (j < n) {
-        int32_t id;
-        float sc;
-        out_entry(a, imap, p, j, score_key(row[j]), id, sc);
+    // the whole row, then -1 padding: four slots per thread requested at once
+    // (clamped reads), so that the copy takes one memory round trip per 4 * NT
+    // slots instead of one per slot
+    constexpr int U = 4;
+    const int nl = (int)n;
+    for (int j0 = 0; j0 < k; j0 += U * NT) {
+      float v[U];
+      int32_t m[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u * NT + tid;
+        const int jc = j < nl ? j : 0;
+        v[u] = nl > 0 ? row[jc] : 0.f;
+        m[u] = (imap && nl > 0) ? imap[jc] : 0;
+      }
+      // all of them consumed from here on (an s_waitcnt the compiler sees: it
+      // would otherwise also wait for the stores below before each use)
+      __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u * NT + tid;
+        if (j >= k) continue;
+        int32_t id = -1;
+        float sc = 0.f;
+        if (j < nl) {
+          sc = key_score(score_key(v[u]));
+          id = j;
+          if (imap) {
+            const bool ok = m[u] >= 0 && m[u] < p;
+            id = ok ? m[u] : -1;
+            sc = ok ? sc : 0.f;
+          }
+        }
         oi[j] = id;
         if (os) os[j] = sc;
-      } else {
-        oi[j] = -1;
-        if (os) os[j] = 0.f;
       }
     }
     return;
