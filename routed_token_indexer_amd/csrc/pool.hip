@@ -7,8 +7,9 @@
 // router itself.
 //
 // One wave per (sequence, block): each lane reads 16 contiguous bytes of a key
-// row per load, so a wave instruction covers 1 KiB of consecutive key rows; the
-// per-lane fp32 sums are combined with a fixed xor tree (deterministic order).
+// row per load, so a wave instruction covers 1 KiB of consecutive key rows, and
+// eight such loads per lane are in flight at once; the per-lane fp32 sums (rows
+// in order) are combined with a fixed xor tree (deterministic order).
 #include "misa_common.hpp"
 #include "misa_internal.hpp"
 
@@ -29,12 +30,24 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ 
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int r = sub; r < B; r += RPI) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(base + (int64_t)r * D);
+  // RB rows per lane in flight (clamped reads), then added in row order: one
+  // memory round trip per RB * RPI rows instead of one per RPI rows
+  constexpr int RB = 8;
+  for (int r0 = sub; r0 < B; r0 += RB * RPI) {
+    u32x4 v[RB];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[2 * e] += bf16_lo(v[e]);
-      acc[2 * e + 1] += bf16_hi(v[e]);
+    for (int u = 0; u < RB; ++u) {
+      const int r = r0 + u * RPI;
+      v[u] = *reinterpret_cast<const u32x4*>(base + (int64_t)(r < B ? r : sub) * D);
+    }
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      if (r0 + u * RPI >= B) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += bf16_lo(v[u][e]);
+        acc[2 * e + 1] += bf16_hi(v[u][e]);
+      }
     }
   }
 #pragma unroll
