@@ -252,7 +252,8 @@ def test_short_prefix_takes_all():
 
 
 @pytest.mark.parametrize("case,topk", [("c1r", 1), ("c1r", 2), ("c1r", 3000), ("c1r", 3001), ("c1r", 5000),
-                                        ("c1s", 1), ("c1s", 7), ("c1s", 20000), ("c1s", 20001), ("c1s", 30000)])
+                                        ("c1s", 1), ("c1s", 7), ("c1s", 20000), ("c1s", 20001), ("c1s", 30000),
+                                        ("c1x", 1), ("c1x", 7), ("c1x", 40000), ("c1x", 40001), ("c1x", 50000)])
 def test_topk_extremes(case, topk):
     x, dev = get(case, "grid")
     ho, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h)
@@ -261,9 +262,10 @@ def test_topk_extremes(case, topk):
     np.testing.assert_array_equal(idx, oi)
 
 
-@pytest.mark.parametrize("case", ["c1r", "c1s"])
+@pytest.mark.parametrize("case", ["c1r", "c1s", "c1x"])
 def test_all_equal_scores_tie_break(case):
-    """Every score equal (zero keys): the lowest token indices win."""
+    """Every score equal (zero keys): the lowest token indices win (c1x: the split
+    path, whose threshold bin then holds the whole row down to the last level)."""
     x, dev = get(case, "grid")
     k0 = torch.zeros_like(dev["k"])
     idx, sc = M.dsa_index_dense(dev["q"], dev["w"], k0, dev["q_seq"], dev["q_len"], 100)
