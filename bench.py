@@ -276,6 +276,14 @@ def main():
         rows = {}
         n = max(10, args.steps // 2)
         rows["pool_us"] = timed(lambda i: M.pool_keys(ks[i % ncopy], B, kbar=kbar_pf), n, 3) * 1e3
+        if not prefill:
+            # incremental pooling of a decode step: one token appended to every
+            # sequence, each append closing a block (the most work a step can need)
+            nseq_k = ks[0].shape[0]
+            new_len = torch.full((nseq_k,), (L // B) * B, dtype=torch.int32, device="cuda")
+            prev_len = new_len - 1
+            rows["pool_update_us"] = timed(lambda i: M.pool_update(ks[i % ncopy], B, prev_len, new_len, 1, kbar_pf),
+                                           n, 3) * 1e3
         rows["route_us"] = timed(lambda i: M.route(q, w, ks[i % ncopy], kbars[i % ncopy], q_seq, q_len, B, h,
                                                    heads=heads, ws=ws_route), n, 3) * 1e3
         kk_sel = kc or topk

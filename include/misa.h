@@ -110,6 +110,29 @@ MISA_API int32_t misa_pool_keys(const void* k, int64_t nseq, int64_t Lmax, int32
                        void* stream);
 
 /*
+ * Incremental pooling for a decode loop. The router's O(H * M) cost
+ * ("Methodologie: MISA") presumes that the pooled keys already exist; this call
+ * keeps them current after tokens were appended to the key cache, by pooling
+ * only the blocks that the append completed.
+ *   k         bf16 [nseq][Lmax][d]    in, already holding the appended keys
+ *   prev_len  int32 [nseq]            in: tokens of each sequence before the append
+ *   new_len   int32 [nseq]            in: tokens after it
+ *   max_new   bound on new_len[n] - prev_len[n] over the batch (0 .. Lmax)
+ *   kbar      fp32 [nseq][Lmax/B][d]  in/out: kbar[n][j] is rewritten for every
+ *             block j with prev_len[n] < (j + 1) B <= new_len[n]; every other
+ *             block keeps its value
+ * The written means are bit-identical to what misa_pool_keys writes for the
+ * same blocks. A sequence whose pair is not an append (prev_len < 0,
+ * new_len < prev_len or new_len > Lmax) is left alone; blocks completed
+ * beyond max_new new tokens are not pooled (max_new must bound the append).
+ * Errors: MISA_ERR_ARG (sizes, max_new outside [0, Lmax], null pointers),
+ * MISA_ERR_ALIGN (k, kbar not 16-byte or the lengths not 4-byte aligned).
+ */
+MISA_API int32_t misa_pool_update(const void* k, int64_t nseq, int64_t Lmax, int32_t d, int32_t B,
+                                  const int32_t* prev_len, const int32_t* new_len, int32_t max_new, float* kbar,
+                                  void* stream);
+
+/*
  * Block-pooled MoE router (MISA abstract; "Methodologie: MISA": per-head
  * affinities with pooled keys over M = ceil(p/B) blocks, aggregated into one
  * importance per head, top-h heads kept; cost O(H * M)).

@@ -47,6 +47,7 @@ _SIGNATURES = {
     "misa_last_error": (ctypes.c_char_p, []),
     "misa_workspace_bytes": (_SZ, [_I32, _I64, _I32, _I64, _I32, _I32, _I32]),
     "misa_pool_keys": (_I32, [_P, _I64, _I64, _I32, _I32, _P, _P]),
+    "misa_pool_update": (_I32, [_P, _I64, _I64, _I32, _I32, _P, _P, _I32, _P, _P]),
     "misa_route": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I64, _I64, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "misa_score_topk": (_I32, [_P, _P, _P, _P, _I32, _P, _P, _I64, _I32, _I32, _I64, _I64, _I32, _P, _P, _P, _SZ,
                                _P]),
@@ -128,6 +129,17 @@ def pool_keys(k: torch.Tensor, B: int, kbar: Optional[torch.Tensor] = None, stre
     if kbar is None:
         kbar = torch.empty((nseq, L // B, d), dtype=torch.float32, device=k.device)
     _check("misa_pool_keys", lib().misa_pool_keys(_ptr(k), nseq, L, d, B, _ptr(kbar), _stream(stream)))
+    return kbar
+
+
+def pool_update(k: torch.Tensor, B: int, prev_len: torch.Tensor, new_len: torch.Tensor, max_new: int,
+                kbar: torch.Tensor, stream=None) -> torch.Tensor:
+    """Pools, in place in ``kbar``, the blocks that growing each sequence from
+    ``prev_len`` to ``new_len`` tokens completed (at most ``max_new`` new tokens)."""
+    _req(k, torch.bfloat16, "k", 3)
+    nseq, L, d = k.shape
+    _check("misa_pool_update", lib().misa_pool_update(_ptr(k), nseq, L, d, B, _ptr(prev_len), _ptr(new_len), max_new,
+                                                      _ptr(kbar), _stream(stream)))
     return kbar
 
 

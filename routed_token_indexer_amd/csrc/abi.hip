@@ -205,6 +205,26 @@ int32_t misa_pool_keys(const void* k, int64_t nseq, int64_t Lmax, int32_t d, int
   return hip_status(e, fn);
 }
 
+int32_t misa_pool_update(const void* k, int64_t nseq, int64_t Lmax, int32_t d, int32_t B, const int32_t* prev_len,
+                         const int32_t* new_len, int32_t max_new, float* kbar, void* stream) {
+  const char* fn = "misa_pool_update";
+  if (!(d == 32 || d == 64 || d == 128 || d == 256)) return fail(MISA_ERR_ARG, "%s: d = %d not in {32, 64, 128, 256}", fn, d);
+  if (nseq < 0) return fail(MISA_ERR_ARG, "%s: nseq < 0", fn);
+  if (Lmax < 1 || Lmax >= (int64_t(1) << 31)) return fail(MISA_ERR_ARG, "%s: Lmax out of range", fn);
+  if (B < 1 || B > Lmax) return fail(MISA_ERR_ARG, "%s: B = %d not in [1, Lmax]", fn, B);
+  if (max_new < 0 || max_new > Lmax) return fail(MISA_ERR_ARG, "%s: max_new = %d not in [0, Lmax]", fn, max_new);
+  if (nseq == 0) return ok();
+  if (!k || !kbar || !prev_len || !new_len) return fail(MISA_ERR_ARG, "%s: null pointer", fn);
+  if (!aligned(k, 16) || !aligned(kbar, 16)) return fail(MISA_ERR_ALIGN, "%s: k and kbar must be 16-byte aligned", fn);
+  if (!aligned(prev_len, 4) || !aligned(new_len, 4))
+    return fail(MISA_ERR_ALIGN, "%s: prev_len/new_len must be 4-byte aligned", fn);
+  if (nseq * (int64_t)(max_new / B + 1) >= (int64_t(1) << 33)) return fail(MISA_ERR_ARG, "%s: grid too large", fn);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = misa::launch_pool_update(static_cast<const uint16_t*>(k), nseq, Lmax, d, B, prev_len, new_len,
+                                          max_new, kbar, st);
+  return hip_status(e, fn);
+}
+
 int32_t misa_route(const void* q, const float* w, const void* k, const float* kbar, const int32_t* q_seq,
                    const int32_t* q_len, int64_t T, int32_t H, int32_t d, int64_t nseq, int64_t Lmax, int32_t B,
                    int32_t h, int32_t* heads, float* router_key, void* ws, size_t ws_bytes, void* stream) {

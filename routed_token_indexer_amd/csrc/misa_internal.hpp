@@ -41,6 +41,8 @@ hipError_t launch_score(const ScoreArgs& a, int d, bool gather, bool wide, int64
 
 hipError_t launch_pool(const uint16_t* k, int64_t nseq, int64_t Lmax, int d, int B, float* kbar,
                        hipStream_t st);
+hipError_t launch_pool_update(const uint16_t* k, int64_t nseq, int64_t Lmax, int d, int B, const int32_t* prev_len,
+                              const int32_t* new_len, int max_new, float* kbar, hipStream_t st);
 
 struct RouteArgs {
   const uint16_t* q;        // bf16 [T][H][d]

@@ -136,6 +136,15 @@ def test_pool_checks(L):
     assert L.misa_pool_keys(FAKE, 0, 4096, 128, 64, FAKE, None) == 0      # nothing to do
 
 
+def test_pool_update_checks(L):
+    assert L.misa_pool_update(FAKE, 4, 4096, 100, 64, FAKE, FAKE, 1, FAKE, None) == -1     # d
+    assert L.misa_pool_update(FAKE, 4, 4096, 128, 64, FAKE, FAKE, -1, FAKE, None) == -1    # max_new < 0
+    assert L.misa_pool_update(FAKE, 4, 4096, 128, 64, FAKE, FAKE, 4097, FAKE, None) == -1  # max_new > Lmax
+    assert L.misa_pool_update(FAKE, 4, 4096, 128, 64, None, FAKE, 1, FAKE, None) == -1     # null lengths
+    assert L.misa_pool_update(FAKE, 4, 4096, 128, 0, FAKE, FAKE, 1, FAKE, None) == -1      # B
+    assert L.misa_pool_update(FAKE, 0, 4096, 128, 64, FAKE, FAKE, 1, FAKE, None) == 0      # nothing to do
+
+
 def test_empty_batch_is_a_noop(L):
     # T = 0: valid, nothing enqueued, no pointer touched
     assert L.misa_score_topk(None, None, None, None, 8, None, None, 0, 64, 128, 4, 4096, 64, None, None, None, 0,

@@ -65,6 +65,53 @@ def test_pool(case, mode):
 
 
 @pytest.mark.parametrize("mode", MODES)
+def test_pool_update_rewrites_exactly_the_completed_blocks(mode):
+    """Incremental pooling: every block that an append completes gets the bits of
+    the full pooling (and the oracle's mean), every other block keeps its value,
+    and a pair that is not an append changes nothing."""
+    x, dev = get("c1r", mode)                     # 4 sequences of 3001 keys, B = 64: 46 blocks each
+    B = x.cfg.B
+    full = M.pool_keys(dev["k"], B)
+    sentinel = 1234.5
+    kb = torch.full_like(full, sentinel)
+    prev = [0, 100, 1500, 2990]
+    new = [3001, 164, 1600, 2980]                  # the last pair shrinks: not an append
+    M.pool_update(dev["k"], B, torch.tensor(prev, dtype=torch.int32, device="cuda"),
+                  torch.tensor(new, dtype=torch.int32, device="cuda"), 3001, kb)
+    kb, full = kb.cpu().numpy(), full.cpu().numpy()
+    ref = O.pool_keys(x.k, B)
+    for n in range(4):
+        for j in range(kb.shape[1]):
+            done = new[n] >= prev[n] and prev[n] < (j + 1) * B <= new[n]
+            if done:
+                np.testing.assert_array_equal(kb[n, j], full[n, j])
+                if mode == "grid":
+                    np.testing.assert_array_equal(kb[n, j], ref[n, j].astype(np.float32))
+                else:
+                    np.testing.assert_allclose(kb[n, j], ref[n, j], rtol=1e-5, atol=1e-6)
+            else:
+                assert np.all(kb[n, j] == sentinel), (n, j)
+
+
+def test_pool_update_decode_loop():
+    """A decode loop that appends 1..40 tokens per sequence per step (a different
+    count per sequence) and updates the pooled keys each step ends with exactly
+    the pooled keys of one full pooling."""
+    x, dev = get("c1r", "gauss")
+    B = x.cfg.B
+    full = M.pool_keys(dev["k"], B).cpu().numpy()
+    kb = torch.zeros((4, x.cfg.L // B, x.cfg.d), dtype=torch.float32, device="cuda")
+    rng = np.random.default_rng(5)
+    lens = np.zeros(4, dtype=np.int32)
+    while lens.min() < x.cfg.L:
+        step = rng.integers(1, 41, size=4).astype(np.int32)
+        nxt = np.minimum(lens + step, x.cfg.L).astype(np.int32)
+        M.pool_update(dev["k"], B, torch.from_numpy(lens).cuda(), torch.from_numpy(nxt).cuda(), 40, kb)
+        lens = nxt
+    np.testing.assert_array_equal(kb.cpu().numpy(), full)
+
+
+@pytest.mark.parametrize("mode", MODES)
 @pytest.mark.parametrize("case", list(CASES))
 def test_route(case, mode):
     x, dev = get(case, mode)
