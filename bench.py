@@ -88,8 +88,8 @@ def recorded_traffic(config_name):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the indexer path has no "
-              f"multi-GPU mode. Run with --gpus 1.", file=sys.stderr)
+        print(f"bench.py: the indexer runs on one GPU (got --gpus {args.gpus}); it has no multi-GPU mode. "
+              f"Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
