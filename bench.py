@@ -39,9 +39,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4"],
+    ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c1m"],
                     help="c4 (default): MISA† 128K decode; c1: DeepSeek-V3.2-like decode; "
-                         "c3: GLM-5-like decode; c2: causal prefill 16K")
+                         "c3: GLM-5-like decode; c2: causal prefill 16K; c1m: c1 with 4 consecutive "
+                         "decode positions per sequence (multi-token prediction)")
     ap.add_argument("--warm-cache", action="store_true", help="no key-cache rotation")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="skip the per-row timings")
@@ -229,8 +230,10 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
     else:
-        # keys of the visible prefixes read once + gathered routed query rows + head weights
-        kernel_bytes = tokens * d * 2 + T * h * d * 2 + T * h * 4
+        # keys of the visible prefixes read once (per sequence: the longest prefix among
+        # its queries) + gathered routed query rows + head weights
+        key_tokens = sum(int(x.q_len[x.q_seq == n].max()) for n in np.unique(x.q_seq))
+        kernel_bytes = key_tokens * d * 2 + T * h * d * 2 + T * h * 4
         achieved = kernel_bytes / (per_launch_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(c.name),

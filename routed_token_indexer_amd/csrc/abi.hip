@@ -62,6 +62,9 @@ int32_t check_ws(const char* fn, void* ws, size_t ws_bytes, size_t need) {
 }
 
 bool wide_tiles(int64_t T, int64_t nseq) { return T >= 64 && T >= 8 * nseq; }
+// several queries per sequence on average, too few for wide tiles: a decode step
+// over consecutive positions (multi-token prediction) shares each key pass
+bool few_tiles(int64_t T, int64_t nseq) { return !wide_tiles(T, nseq) && T >= 2 * nseq; }
 
 // Workspace of scoring + selection over rows of at most max_len: the fp32 score
 // rows, then (for few long rows) the split top-k's state.
@@ -292,6 +295,7 @@ int32_t score_and_select(const char* fn, const void* q, const float* w, const vo
   const bool gather = cand != nullptr;
   const int64_t max_len = gather ? kc : Lmax;
   const bool wide = !gather && wide_tiles(T, nseq);
+  const bool few = !gather && few_tiles(T, nseq);
   const bool split = idx && misa::use_split_topk(T, max_len);
   misa::SplitTopkWs sw{};
   hipError_t e = hipSuccess;
@@ -300,9 +304,9 @@ int32_t score_and_select(const char* fn, const void* q, const float* w, const vo
     sw = misa::split_topk_carve(base, T, max_len);
     e = misa::launch_zero(sw.hist, misa::split_topk_zero_words(T), st);
     if (e != hipSuccess) return hip_status(e, fn);
-    if (!wide) a.hist = sw.hist;   // the decode scoring kernel builds the level-1 histogram
+    if (!wide && !few) a.hist = sw.hist;   // the decode scoring kernel builds the level-1 histogram
   }
-  e = misa::launch_score(a, d, gather, wide, max_len, st);   // timed by the launch itself
+  e = misa::launch_score(a, d, gather, wide, max_len, st, few);   // timed by the launch itself
   if (e != hipSuccess) return hip_status(e, fn);
   if (!idx) return ok();
   misa::TopkArgs b{};
@@ -411,7 +415,7 @@ int32_t run_indexer(const char* fn, bool hier, const void* q, const float* w, co
   rc = check_ws(fn, ws, ws_bytes, misa_workspace_bytes(op, T, H, Lmax, B, topk, hier ? kc : 0));
   if (rc) return rc;
 
-  const bool fused = !wide_tiles(T, nseq) && misa::split_topk_always_ok(Lmax) &&
+  const bool fused = !wide_tiles(T, nseq) && !few_tiles(T, nseq) && misa::split_topk_always_ok(Lmax) &&
                      (!hier || misa::split_topk_always_ok(kc));
   if (!fused) {
     char* p = static_cast<char*>(ws);

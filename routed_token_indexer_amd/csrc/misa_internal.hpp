@@ -36,8 +36,10 @@ struct ScoreArgs {
 };
 
 int score_rows_per_query(int hh);
-// gather: keys come from cand; wide: many queries of one sequence per tile (prefill)
-hipError_t launch_score(const ScoreArgs& a, int d, bool gather, bool wide, int64_t max_len, hipStream_t st);
+// gather: keys come from cand; wide: many queries of one sequence per tile (prefill);
+// few: several queries per sequence over long prefixes (small tiles, short key chunks)
+hipError_t launch_score(const ScoreArgs& a, int d, bool gather, bool wide, int64_t max_len, hipStream_t st,
+                        bool few = false);
 
 hipError_t launch_pool(const uint16_t* k, int64_t nseq, int64_t Lmax, int d, int B, float* kbar,
                        hipStream_t st);

@@ -633,9 +633,17 @@ hipError_t launch_decode_d(const ScoreArgs& a, bool gather, int64_t max_len, hip
 }
 
 template <int D, int NHP, int RT, int KB>
-hipError_t launch_prefill_cfg(ScoreArgs a, int64_t max_len, hipStream_t st) {
+hipError_t launch_prefill_cfg(ScoreArgs a, int64_t max_len, hipStream_t st, bool few = false) {
   constexpr int QT = 4 * (16 * RT) / NHP;
   if ((uint64_t)QT * (uint64_t)a.out_stride * 4u >= (1ull << 32) - 16) return hipErrorInvalidValue;   // view offsets
+  if (a.chunk <= 0 && few) {
+    // few tiles over long prefixes: key chunks for about 512 workgroups, at least
+    // 256 keys (four blocks) each
+    const int64_t ntiles = (a.T + QT - 1) / QT;
+    int64_t c = 256;
+    while (c < 2048 && ntiles * ((max_len + c - 1) / c) > 512) c *= 2;
+    a.chunk = (int)c;
+  }
   if (a.chunk <= 0) a.chunk = 2048;
   const dim3 grid((unsigned)((a.T + QT - 1) / QT), (unsigned)((max_len + a.chunk - 1) / a.chunk));
   return launch_timed(KID_SCORE, score_prefill_kernel<D, NHP, RT, KB>, grid, dim3(256), st, a);
@@ -663,6 +671,25 @@ hipError_t launch_prefill(const ScoreArgs& a, int nhp, int64_t max_len, hipStrea
   return hipErrorInvalidValue;
 }
 
+// Few queries per sequence (a decode step that scores several consecutive
+// positions of each sequence): one query per wave, four per workgroup, so that a
+// tile usually covers a single sequence, which then streams its keys once for
+// all of its queries. Up to 16 routed heads take one row tile (padding rows
+// cost matrix-core time only, which this memory-bound case has to spare).
+template <int D>
+hipError_t launch_prefill_few(const ScoreArgs& a, int nhp, int64_t max_len, hipStream_t st) {
+  constexpr int KB = D == 256 ? 32 : 64;
+  switch (nhp) {
+    case 4:
+    case 8:
+    case 16: return launch_prefill_cfg<D, 16, 1, KB>(a, max_len, st, true);
+    case 32: return launch_prefill_cfg<D, 32, 2, KB>(a, max_len, st, true);
+    case 48: return launch_prefill_cfg<D, 48, 3, KB>(a, max_len, st, true);
+    case 64: return launch_prefill_cfg<D, 64, 4, KB>(a, max_len, st, true);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 int score_rows_per_query(int hh) {
@@ -671,8 +698,19 @@ int score_rows_per_query(int hh) {
   return 16 * ((hh + 15) / 16);
 }
 
-hipError_t launch_score(const ScoreArgs& a, int d, bool gather, bool wide, int64_t max_len, hipStream_t st) {
+hipError_t launch_score(const ScoreArgs& a, int d, bool gather, bool wide, int64_t max_len, hipStream_t st,
+                        bool few) {
   if (a.T == 0) return hipSuccess;
+  if (!gather && few) {
+    const int nhp = score_rows_per_query(a.hh);
+    switch (d) {
+      case 32: return launch_prefill_few<32>(a, nhp, max_len, st);
+      case 64: return launch_prefill_few<64>(a, nhp, max_len, st);
+      case 128: return launch_prefill_few<128>(a, nhp, max_len, st);
+      case 256: return launch_prefill_few<256>(a, nhp, max_len, st);
+    }
+    return hipErrorInvalidValue;
+  }
   if (gather || !wide) {
     switch (d) {
       case 32: return launch_decode_d<32>(a, gather, max_len, st);

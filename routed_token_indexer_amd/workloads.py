@@ -50,7 +50,7 @@ class Config:
     kc: Optional[int]    # candidate count of the hierarchical coarse pass (None: not used)
     needles: int         # planted needle keys per sequence (gauss mode only)
     ar1: bool            # AR(1) keys (True) or i.i.d. keys (False)
-    phase: str           # "decode" or "prefill"
+    phase: str           # "decode", "mtp" (several consecutive decode positions per sequence) or "prefill"
     q_len0: int = 0      # decode: first query's visible prefix when queries share one sequence
     description: str = ""
 
@@ -82,6 +82,12 @@ CONFIGS = {
                  needles=64, ar1=True, phase="decode",
                  description="hierarchical MISA at 128K: 4 sequences x 1 query, L=131072, H=64, "
                              "d=128, B=128, h=8, k'=8192, k=2048"),
+    # not one of the five shapes: a multi-token-prediction decode step on c1's
+    # sequences (4 consecutive positions of each), for the shared key pass
+    "c1m": Config("c1m", 5, nseq=4, L=32768, T=16, H=64, d=128, B=64, h=8, topk=2048, kc=None,
+                  needles=32, ar1=True, phase="mtp",
+                  description="multi-token decode: 4 sequences x 4 consecutive queries, L=32768, H=64, "
+                              "d=128, B=64, h=8, k=2048"),
 }
 
 
@@ -113,6 +119,12 @@ def query_layout(cfg: Config):
         # every position is a query; a query sees itself, so p = t + 1
         q_seq = np.zeros(T, np.int32)
         q_len = np.arange(1, T + 1, dtype=np.int32)
+    elif cfg.phase == "mtp":
+        # m = T / nseq consecutive positions per sequence, queries of a sequence
+        # adjacent: query i of sequence n sees L - m + 1 + i tokens
+        m = T // cfg.nseq
+        q_seq = np.repeat(np.arange(cfg.nseq, dtype=np.int32), m)
+        q_len = np.tile(cfg.L - m + 1 + np.arange(m, dtype=np.int32), cfg.nseq).astype(np.int32)
     elif cfg.nseq == 1 and T > 1:
         # several decode queries on one sequence at consecutive prefixes
         q_seq = np.zeros(T, np.int32)
@@ -173,6 +185,8 @@ def make_inputs(cfg, mode: str = "gauss", seed: Optional[int] = None, **override
         raise ValueError("prefill: every position is a query (T == L)")
     if cfg.phase == "decode" and cfg.nseq > 1 and cfg.T != cfg.nseq:
         raise ValueError("decode over several sequences: one query per sequence (T == nseq)")
+    if cfg.phase == "mtp" and (cfg.T % cfg.nseq or cfg.T // cfg.nseq > cfg.L):
+        raise ValueError("multi-token decode: the same number (at most L) of queries per sequence")
     if cfg.nseq == 1 and cfg.phase == "decode" and cfg.q_len0 + cfg.T - 1 > cfg.L:
         raise ValueError("decode prefixes exceed the stored length")
     if seed is None:

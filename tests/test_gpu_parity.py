@@ -26,6 +26,10 @@ CASES = {
     # rows above 32K scores: the multi-workgroup (split) top-k
     "c1x": ("c1", dict(L=40001, T=4, nseq=4, topk=1000)),
     "c4s": ("c4", dict(L=40000, T=4, nseq=4, kc=4096, topk=512)),
+    # several consecutive decode positions per sequence: the shared key pass
+    "c1m": ("c1m", dict(L=3001, topk=256)),
+    # ... over rows of the split top-k
+    "c1mx": ("c1m", dict(L=40001, T=8, topk=1000)),
 }
 MODES = ["gauss", "grid"]
 
@@ -251,6 +255,27 @@ def test_hier_full_candidates_is_dense_bitwise(case, mode):
     hi, hs = M.hier_rerank(dev["q"], dev["w"], dev["k"], cand, dev["q_seq"], dev["q_len"], x.cfg.topk)
     di, ds = M.dsa_index_dense(dev["q"], dev["w"], dev["k"], dev["q_seq"], dev["q_len"], x.cfg.topk)
     assert torch.equal(hi, di) and torch.equal(hs, ds)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_mtp_rows_equal_decode_calls(mode):
+    """A decode step with four consecutive positions per sequence scores each
+    sequence's keys once for all four queries; every query's selection and scores
+    are bit-identical to a decode call for that query alone."""
+    x, dev = get("c1m", mode)
+    ho, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h)
+    hd = torch.from_numpy(ho).cuda()
+    bi, bs = M.score_topk(dev["q"], dev["w"], dev["k"], hd, dev["q_seq"], dev["q_len"], x.cfg.topk)
+    di_all, ds_all = M.dsa_index_dense(dev["q"], dev["w"], dev["k"], dev["q_seq"], dev["q_len"], x.cfg.topk)
+    for t in range(x.cfg.T):
+        sl = slice(t, t + 1)
+        one = lambda v: v[sl].contiguous()
+        di, ds = M.score_topk(one(dev["q"]), one(dev["w"]), dev["k"], one(hd), one(dev["q_seq"]), one(dev["q_len"]),
+                              x.cfg.topk)
+        assert torch.equal(bi[t], di[0]) and torch.equal(bs[t], ds[0]), t
+        ei, es = M.dsa_index_dense(one(dev["q"]), one(dev["w"]), dev["k"], one(dev["q_seq"]), one(dev["q_len"]),
+                                   x.cfg.topk)
+        assert torch.equal(di_all[t], ei[0]) and torch.equal(ds_all[t], es[0]), t
 
 
 def test_prefill_row_equals_decode_call():
