@@ -346,7 +346,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MANY ? 8 : N
   // path: at most 64 per lane, so that eight waves per SIMD are resident
   constexpr bool kInlineFallback = !MANY;
   constexpr bool kPrefetchIds = GATHER && EPT <= 16;   // token ids held beside the keys
-  __shared__ RadixScratch<NT, (NT == 1024 && !MANY) ? 3 : 1> rs;
+  __shared__ __attribute__((aligned(16))) RadixScratch<NT, (NT == 1024 && !MANY) ? 3 : 1> rs;
   __shared__ uint32_t wmin[NW], wmax[NW];
   __shared__ uint32_t wgt[NW], weq[NW];
   __shared__ uint32_t s_m, s_thr, s_cut;
@@ -575,8 +575,22 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MANY ? 8 : N
         if ((uint32_t)tid < m) {
           const uint32_t ki = c_key[tid], si = c_slot[tid];
           uint32_t r = 0;
-          for (uint32_t q = 0; q < m; ++q)
-            r += (c_key[q] > ki || (c_key[q] == ki && c_slot[q] < si)) ? 1u : 0u;
+          if constexpr (!MANY) {
+            // the list read 4 slots at a time (16-byte broadcast reads; slots
+            // past m are in the list's storage and masked); the many-row
+            // variants lack the registers to hold these loads in flight
+#pragma unroll
+            for (int g = 0; g < 8; ++g) {
+              const u32x4 kk = *reinterpret_cast<const u32x4*>(c_key + 4 * g);
+              const u32x4 ss = *reinterpret_cast<const u32x4*>(c_slot + 4 * g);
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                r += ((uint32_t)(4 * g + e) < m && (kk[e] > ki || (kk[e] == ki && ss[e] < si))) ? 1u : 0u;
+            }
+          } else {
+            for (uint32_t q = 0; q < m; ++q)
+              r += (c_key[q] > ki || (c_key[q] == ki && c_slot[q] < si)) ? 1u : 0u;
+          }
           keep(r, ki, si);
         }
       } else {
