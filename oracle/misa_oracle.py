@@ -21,8 +21,9 @@ Notation (pages' notation where they have one):
 
 Status of each function's pin (see tests/test_oracle_*.py):
   pool_keys, route, routed_scores, select_topk, score_topk, dsa_index_dense,
-  hier_rerank, misa_indexer, misa_hier_indexer: pinned (brute force, closed
-  forms, invariants). The router's aggregation rule is a reading of the pages;
+  hier_rerank, misa_indexer, misa_hier_indexer, block_filter,
+  score_topk_in_blocks, block_indexer: pinned (brute force, closed forms,
+  invariants). The router's aggregation rule is a reading of the pages;
   agreement with the authors' own (unpublished) router is "parity unpinned".
 """
 from __future__ import annotations
@@ -34,6 +35,7 @@ import numpy as np
 __all__ = [
     "pool_keys", "router_values", "route", "routed_scores", "select_topk", "score_topk",
     "dsa_index_dense", "hier_rerank", "misa_indexer", "misa_hier_indexer", "mac_count",
+    "block_scores", "block_filter", "block_candidates", "score_topk_in_blocks", "block_indexer",
 ]
 
 
@@ -247,6 +249,91 @@ def misa_hier_indexer(q, w, k, q_seq, q_len, B: int, h: int, kc: int, topk: int,
     cand, _ = score_topk(q, w, k, heads, q_seq, q_len, kc, queries=queries)
     idx, val = hier_rerank(q, w, k, cand, q_seq, q_len, topk, queries=queries)
     return heads, cand, idx, val
+
+
+# ------------------------------------------------------------------ block filter + routed heads
+# The token axis composed with the head axis. HISA (thelatestinai.com paper
+# cards, the HISA abstract) replaces the flat token scan of the indexer by two
+# stages: a coarse stage scores pooled block representations and discards the
+# weak blocks, then the indexer runs only on the tokens of the retained blocks.
+# The gist.science MISA summary places HISA on the token axis
+# ("Probleemstelling") and presents head routing as combinable with such
+# schemes ("Betekenis en Claims"). Here both stages use the routed heads.
+#
+# Readings taken (the pages give no formula for the coarse stage):
+#  - a block's pooled representation is the mean of its keys (the same pooled
+#    keys the router reads), and its score is the routed indexer formula applied
+#    to that mean: b_j = sum_{g in R, ascending g} w_g * max(q_g . Kbar_j, 0);
+#  - only complete blocks j < floor(p / B) are ranked; the query's partial last
+#    block (tokens floor(p / B) * B .. p - 1) is always retained, like the most
+#    recent tokens of a local window;
+#  - the m best complete blocks are kept, ties to the lower block id; all of
+#    them when there are at most m;
+#  - the fine stage is the routed top-k over the retained tokens, with the
+#    usual rule (score descending, token id ascending), ids ascending, -1 padded.
+
+
+def block_scores(q_t, w_t, keys_seq, heads_t, p: int, B: int) -> np.ndarray:
+    """Coarse score b_j of each complete visible block j < floor(p / B)."""
+    q_t = _f64(q_t)
+    w_t = _f64(w_t)
+    nb = p // B
+    d = q_t.shape[1]
+    kbar = _f64(keys_seq)[:nb * B].reshape(nb, B, d).sum(axis=1) / B
+    b = np.zeros(nb)
+    for g in sorted(int(x) for x in heads_t):
+        b = b + w_t[g] * np.maximum(kbar @ q_t[g], 0.0)
+    return b
+
+
+def block_filter(q, w, k, heads, q_seq, q_len, B: int, m: int, queries=None):
+    """Retained complete blocks of each query: [nq, m] ascending ids, -1 padded.
+
+    heads: [nq, h] routed heads (row i <-> query queries[i]).
+    """
+    T = np.asarray(q).shape[0]
+    qs = range(T) if queries is None else list(queries)
+    blocks = np.full((len(qs), m), -1, np.int64)
+    for i, t in enumerate(qs):
+        b = block_scores(q[t], w[t], k[q_seq[t]], heads[i], int(q_len[t]), B)
+        nb = b.shape[0]
+        keep = np.sort(np.lexsort((np.arange(nb), -b))[:min(m, nb)])
+        blocks[i, :keep.shape[0]] = keep
+    return blocks
+
+
+def block_candidates(blocks_t, p: int, B: int) -> np.ndarray:
+    """Token ids (ascending) of a query's retained blocks and of its partial block."""
+    c = [np.arange(int(j) * B, int(j) * B + B) for j in blocks_t if j >= 0]
+    c.append(np.arange((p // B) * B, p))
+    return np.concatenate(c).astype(np.int64)
+
+
+def score_topk_in_blocks(q, w, k, heads, blocks, q_seq, q_len, B: int, topk: int, queries=None):
+    """Fine stage: routed scores of the retained tokens only, then the top-k."""
+    q = _f64(q)
+    T = q.shape[0]
+    qs = range(T) if queries is None else list(queries)
+    idx = np.full((len(qs), topk), -1, np.int64)
+    val = np.zeros((len(qs), topk))
+    for i, t in enumerate(qs):
+        p = int(q_len[t])
+        c = block_candidates(blocks[i], p, B)
+        S = routed_scores(q[t], w[t], k[q_seq[t]], heads[i], p)[c]
+        n = min(topk, c.shape[0])
+        sel = np.sort(np.lexsort((c, -S))[:n])      # c ascending => slot order is token order
+        idx[i, :n] = c[sel]
+        val[i, :n] = S[sel]
+    return idx, val
+
+
+def block_indexer(q, w, k, q_seq, q_len, B: int, h: int, m: int, topk: int, queries=None):
+    """Route (top-h heads), keep the m best complete blocks plus the partial one,
+    and take the routed top-k among their tokens."""
+    heads, r = route(q, w, k, q_seq, q_len, B, h, queries=queries)
+    blocks = block_filter(q, w, k, heads, q_seq, q_len, B, m, queries=queries)
+    idx, val = score_topk_in_blocks(q, w, k, heads, blocks, q_seq, q_len, B, topk, queries=queries)
+    return heads, blocks, idx, val
 
 
 def mac_count(q_len, H: int, h: int, d: int, B: int) -> int:

@@ -378,3 +378,127 @@ def test_mac_count_formula():
     # O(h L + H M) per query: d * (h * p + H * ceil(p / B))
     assert O.mac_count([5], 3, 1, 2, 2) == 2 * (1 * 5 + 3 * 3)
     assert O.mac_count([32768] * 4, 64, 8, 128, 64) == 4 * 128 * (8 * 32768 + 64 * 512)
+
+
+# ------------------------------------------------------------------ block filter + routed heads
+def test_hand_block_filter(hand):
+    g, keys, q, w, q_seq, q_len = hand
+    B = int(g["B"])
+    np.testing.assert_array_equal(O.block_scores(q[0], w[0], keys[0], [0], 5, B), g["A.block_scores_R0"])
+    np.testing.assert_array_equal(O.block_scores(q[0], w[0], keys[0], [0, 1], 5, B), g["A.block_scores_R01"])
+    np.testing.assert_array_equal(O.block_scores(q[1], w[1], keys[0], [1], 4, B), g["B.block_scores_R1"])
+    bl = O.block_filter(q, w, keys, np.array([[0]]), q_seq, q_len, B, 1, queries=[0])
+    assert bl[0].tolist() == [int(g["A.blocks_R0_m1"])]
+    idx, _ = O.score_topk_in_blocks(q, w, keys, np.array([[0]]), bl, q_seq, q_len, B, 3, queries=[0])
+    assert idx[0].tolist() == g["A.block_top3_R0_m1"].astype(int).tolist()
+    # the whole composed call routes to head 0 (h = 1) and gives the same
+    heads, blocks, idx2, _ = O.block_indexer(q, w, keys, q_seq, q_len, B, 1, 1, 3, queries=[0])
+    assert heads[0].tolist() == [0] and blocks[0].tolist() == [0]
+    np.testing.assert_array_equal(idx2, idx)
+    h01 = np.array([[0, 1]])
+    bl = O.block_filter(q, w, keys, h01, q_seq, q_len, B, 1, queries=[0])
+    idx, _ = O.score_topk_in_blocks(q, w, keys, h01, bl, q_seq, q_len, B, 2, queries=[0])
+    assert idx[0].tolist() == g["A.block_top2_R01_m1"].astype(int).tolist()
+    bl = O.block_filter(q, w, keys, np.array([[1]]), q_seq, q_len, B, 1, queries=[1])   # exact tie
+    assert bl[0].tolist() == [int(g["B.blocks_R1_m1"])]
+    idx, _ = O.score_topk_in_blocks(q, w, keys, np.array([[1]]), bl, q_seq, q_len, B, 1, queries=[1])
+    assert idx[0].tolist() == [int(g["B.block_top1_R1_m1"])]
+
+
+def test_block_filter_B1_reduces_to_routed_topk():
+    """With one token per block the coarse score of block j is the routed score
+    of token j, so keeping m >= k blocks and taking the top-k reproduces MISA's
+    routed top-k with the same heads."""
+    for mode in ("gauss", "grid"):
+        x = make_inputs("c0", mode=mode)
+        heads, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h)
+        for t in (0, 7, 15):
+            p = int(x.q_len[t])
+            np.testing.assert_array_equal(O.block_scores(x.q[t], x.w[t], x.k[0], heads[t], p, 1),
+                                          O.routed_scores(x.q[t], x.w[t], x.k[0], heads[t], p))
+        ref, rv = O.score_topk(x.q, x.w, x.k, heads, x.q_seq, x.q_len, x.cfg.topk)
+        for m in (x.cfg.topk, x.cfg.topk + 37):
+            bl = O.block_filter(x.q, x.w, x.k, heads, x.q_seq, x.q_len, 1, m)
+            idx, val = O.score_topk_in_blocks(x.q, x.w, x.k, heads, bl, x.q_seq, x.q_len, 1, x.cfg.topk)
+            np.testing.assert_array_equal(idx, ref)
+            np.testing.assert_array_equal(val, rv)
+
+
+def test_block_filter_all_blocks_is_misa():
+    for mode in ("gauss", "grid"):
+        x = make_inputs("c0", mode=mode)
+        m = int(x.q_len.max()) // x.cfg.B
+        heads, _, mi, mv = O.misa_indexer(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h, x.cfg.topk)
+        h2, blocks, idx, val = O.block_indexer(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h, m, x.cfg.topk)
+        np.testing.assert_array_equal(h2, heads)
+        for t in range(x.cfg.T):
+            assert blocks[t].tolist() == list(range(int(x.q_len[t]) // x.cfg.B)) + [-1] * (m - int(x.q_len[t]) // x.cfg.B)
+        np.testing.assert_array_equal(idx, mi)
+        np.testing.assert_array_equal(val, mv)
+
+
+def test_block_filter_rank_count_bruteforce():
+    """Exact rational block scores from the keys themselves; block j is kept iff
+    fewer than m blocks beat it (higher score, or equal score and lower id).
+    Grid inputs make exact ties frequent."""
+    x = make_inputs("c0", mode="grid", L=256, T=4, B=8, q_len0=243)
+    heads, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h)
+    m = 9
+    blocks = O.block_filter(x.q, x.w, x.k, heads, x.q_seq, x.q_len, x.cfg.B, m)
+    saw_tie = False
+    for t in range(4):
+        p, B = int(x.q_len[t]), x.cfg.B
+        nb = p // B
+        b = []
+        for j in range(nb):
+            tot = Fraction(0)
+            for g in sorted(heads[t].tolist()):
+                a = sum((Fraction(float(x.q[t, g, c])) * Fraction(float(x.k[0, s, c]))
+                         for s in range(j * B, j * B + B) for c in range(x.cfg.d)), Fraction(0)) / B
+                tot += Fraction(float(x.w[t, g])) * max(a, Fraction(0))
+            b.append(tot)
+        keep = [j for j in range(nb) if sum(1 for i in range(nb) if b[i] > b[j] or (b[i] == b[j] and i < j)) < m]
+        saw_tie |= len(set(b)) < nb
+        assert blocks[t].tolist() == keep + [-1] * (m - len(keep))
+    assert saw_tie
+
+
+def test_block_filter_drops_tokens_of_weak_blocks():
+    """A key that scores highest but sits in a block whose mean cancels is lost
+    when its block is not retained, and found when it is; the partial block is
+    always searched."""
+    d, B = 2, 2
+    keys = np.array([[[3, 0], [-3, 0], [1, 0], [1, 0], [0, 0], [2.5, 0], [0.5, 0]]], np.float64)
+    q = np.array([[[1.0, 0.0]]])
+    w = np.array([[1.0]])
+    q_seq, q_len = np.array([0]), np.array([7])
+    heads = np.array([[0]])
+    # complete blocks: {0,1} mean 0, {2,3} mean 1, {4,5} mean 1.25; partial {6}
+    np.testing.assert_array_equal(O.block_scores(q[0], w[0], keys[0], [0], 7, B), [0.0, 1.0, 1.25])
+    bl = O.block_filter(q, w, keys, heads, q_seq, q_len, B, 1)
+    assert bl[0].tolist() == [2]
+    idx, val = O.score_topk_in_blocks(q, w, keys, heads, bl, q_seq, q_len, B, 2)
+    assert idx[0].tolist() == [5, 6] and val[0].tolist() == [2.5, 0.5]      # token 0 (score 3) is lost
+    bl = O.block_filter(q, w, keys, heads, q_seq, q_len, B, 3)
+    idx, _ = O.score_topk_in_blocks(q, w, keys, heads, bl, q_seq, q_len, B, 2)
+    assert idx[0].tolist() == [0, 5]
+    # fewer retained tokens than k: all of them, then -1 padding
+    bl = O.block_filter(q, w, keys, heads, q_seq, q_len, B, 1)
+    idx, _ = O.score_topk_in_blocks(q, w, keys, heads, bl, q_seq, q_len, B, 5)
+    assert idx[0].tolist() == [4, 5, 6, -1, -1]
+
+
+def test_block_filter_nested_in_m():
+    """The retained block sets grow with m (one fixed order), so the k-th best
+    retained routed score never falls as m grows."""
+    x = make_inputs("c0")
+    heads, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h)
+    prev_b, prev_v = None, None
+    for m in (2, 4, 8, 16):
+        bl = O.block_filter(x.q, x.w, x.k, heads, x.q_seq, x.q_len, x.cfg.B, m)
+        _, val = O.score_topk_in_blocks(x.q, x.w, x.k, heads, bl, x.q_seq, x.q_len, x.cfg.B, x.cfg.topk)
+        if prev_b is not None:
+            for t in range(x.cfg.T):
+                assert set(prev_b[t]) - {-1} <= set(bl[t]) - {-1}
+            assert np.all(val.min(axis=1) >= prev_v.min(axis=1))
+        prev_b, prev_v = bl, val
