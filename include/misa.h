@@ -79,6 +79,8 @@ extern "C" {
 #define MISA_OP_DSA_DENSE 4
 #define MISA_OP_INDEXER 5
 #define MISA_OP_HIER_INDEXER 6
+#define MISA_OP_BLOCK_FILTER 7     /* kc argument = m, the complete blocks kept */
+#define MISA_OP_BLOCK_INDEXER 8    /* kc argument = m */
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 MISA_API int32_t misa_version(void);
@@ -91,8 +93,9 @@ MISA_API const char* misa_last_error(void);
 
 /*
  * Workspace bytes needed by one call of `op` (MISA_OP_*) with these sizes.
- * Arguments that an op does not use are ignored (kc only matters for
- * MISA_OP_HIER_RERANK, B only for MISA_OP_ROUTE). Returns 0 if none is needed.
+ * Arguments that an op does not use are ignored (kc matters for the MISA†
+ * ops, and stands for m, the blocks kept, in the block ops; B for the ops that
+ * route or pool). Returns 0 if none is needed.
  */
 MISA_API size_t misa_workspace_bytes(int32_t op, int64_t T, int32_t H, int64_t Lmax, int32_t B, int32_t topk,
                             int32_t kc);
@@ -227,6 +230,49 @@ MISA_API int32_t misa_hier_indexer(const void* q, const float* w, const void* k,
                                    int64_t nseq, int64_t Lmax, int32_t B, int32_t h, int32_t kc, int32_t topk,
                                    int32_t* heads, int32_t* cand, int32_t* idx, float* score, void* ws,
                                    size_t ws_bytes, void* stream);
+
+/*
+ * Block filter on the pooled keys, composed with head routing: the coarse stage
+ * of a two-stage (block, then token) search. HISA (thelatestinai.com paper
+ * cards, the HISA abstract) scores pooled block representations, drops the
+ * weak blocks and runs the indexer only inside the retained ones; the
+ * gist.science MISA summary presents head routing as combinable with such
+ * token-axis schemes ("Betekenis en Claims"). The pages give no formula for the
+ * coarse score; this library takes the routed indexer formula on the block's
+ * mean key, b_j = sum over the routed heads g of w[t][g] * max(q[t][g] . kbar[j], 0),
+ * for the complete visible blocks j < q_len[t] / B, keeps the m best (ties to
+ * the lower block id; all of them when there are at most m) and always keeps
+ * the partial last block.
+ *   kbar    fp32 [nseq][Lmax/B][d]  from misa_pool_keys
+ *   heads   int32 [T][h]            routed heads (an id outside [0, H) contributes nothing)
+ *   m       complete blocks kept per query, 1 .. Lmax / B
+ *   blocks  int32 [T][m] out: kept complete block ids, ascending, -1 padded
+ *   cand    int32 [T][(m + 1) * B] out, may be NULL: the token ids of the kept
+ *           blocks, then those of the partial block, ascending, -1 padded (the
+ *           candidate list of misa_hier_rerank's form, for the fine stage)
+ *   ws: misa_workspace_bytes(MISA_OP_BLOCK_FILTER, T, H, Lmax, B, 0, m)
+ * Errors: as misa_route, and MISA_ERR_ARG for m outside [1, Lmax / B].
+ */
+MISA_API int32_t misa_block_filter(const void* q, const float* w, const float* kbar, const int32_t* heads,
+                                   int32_t h, const int32_t* q_seq, const int32_t* q_len, int64_t T, int32_t H,
+                                   int32_t d, int64_t nseq, int64_t Lmax, int32_t B, int32_t m, int32_t* blocks,
+                                   int32_t* cand, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Routed indexer restricted to the retained blocks: misa_route, then
+ * misa_block_filter, then the routed scores of the candidate tokens and their
+ * top-k (score descending, token id ascending; ids ascending, -1 padded). With
+ * m = Lmax / B every visible token is a candidate and the result equals
+ * misa_indexer's. Each query reads the keys of at most (m + 1) * B tokens.
+ *   heads   int32 [T][h] out, may be NULL;  blocks  int32 [T][m] out, may be NULL
+ *   idx / score as misa_score_topk (score: routed scores)
+ *   ws: misa_workspace_bytes(MISA_OP_BLOCK_INDEXER, T, H, Lmax, B, topk, m)
+ */
+MISA_API int32_t misa_block_indexer(const void* q, const float* w, const void* k, const float* kbar,
+                                    const int32_t* q_seq, const int32_t* q_len, int64_t T, int32_t H, int32_t d,
+                                    int64_t nseq, int64_t Lmax, int32_t B, int32_t h, int32_t m, int32_t topk,
+                                    int32_t* heads, int32_t* blocks, int32_t* idx, float* score, void* ws,
+                                    size_t ws_bytes, void* stream);
 
 /*
  * Full score rows of the routed scoring step (a diagnostic of step 3 above):

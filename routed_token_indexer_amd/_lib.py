@@ -27,6 +27,8 @@ OP_HIER_RERANK = 3
 OP_DSA_DENSE = 4
 OP_INDEXER = 5
 OP_HIER_INDEXER = 6
+OP_BLOCK_FILTER = 7
+OP_BLOCK_INDEXER = 8
 
 KERNEL_SCORE = 1
 KERNEL_TOPK = 2
@@ -59,6 +61,10 @@ _SIGNATURES = {
                             _SZ, _P]),
     "misa_hier_indexer": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I64, _I64, _I32, _I32, _I32, _I32, _P, _P,
                                  _P, _P, _P, _SZ, _P]),
+    "misa_block_filter": (_I32, [_P, _P, _P, _P, _I32, _P, _P, _I64, _I32, _I32, _I64, _I64, _I32, _I32, _P, _P,
+                                 _P, _SZ, _P]),
+    "misa_block_indexer": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I64, _I64, _I32, _I32, _I32, _I32, _P,
+                                  _P, _P, _P, _P, _SZ, _P]),
     "misa_timing_begin": (_I32, [_I32, _I32]),
     "misa_timing_end": (_I32, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)]),
 }
@@ -236,6 +242,43 @@ def hier_indexer(q, w, k, kbar, q_seq, q_len, B: int, h: int, kc: int, topk: int
                                                         _ptr(q_len), T, H, d, nseq, L, B, h, kc, topk, _ptr(heads),
                                                         _ptr(cand), _ptr(idx), _ptr(score), _ptr(ws), ws.numel(),
                                                         _stream(stream)))
+    return idx, score
+
+
+def block_filter(q, w, kbar, heads, q_seq, q_len, Lmax: int, B: int, m: int, blocks=None, cand=None,
+                 want_cand=True, ws=None, stream=None):
+    """Coarse stage: the m best complete blocks of each query by the routed
+    formula on the pooled keys (blocks [T, m], ascending, -1 padded) and the
+    candidate token list cand [T, (m + 1) * B] (kept blocks, then the partial one)."""
+    _req(q, torch.bfloat16, "q", 3)
+    _req(heads, torch.int32, "heads", 2)
+    _req(kbar, torch.float32, "kbar", 3)
+    T, H, d = q.shape
+    nseq = kbar.shape[0]
+    if blocks is None:
+        blocks = torch.empty((T, m), dtype=torch.int32, device=q.device)
+    if cand is None and want_cand:
+        cand = torch.empty((T, (m + 1) * B), dtype=torch.int32, device=q.device)
+    ws = _workspace(ws, workspace_bytes(OP_BLOCK_FILTER, T, H, Lmax, B, 0, m), q.device)
+    _check("misa_block_filter", lib().misa_block_filter(_ptr(q), _ptr(w), _ptr(kbar), _ptr(heads), heads.shape[1],
+                                                        _ptr(q_seq), _ptr(q_len), T, H, d, nseq, Lmax, B, m,
+                                                        _ptr(blocks), _ptr(cand), _ptr(ws), ws.numel(),
+                                                        _stream(stream)))
+    return blocks, cand
+
+
+def block_indexer(q, w, k, kbar, q_seq, q_len, B: int, h: int, m: int, topk: int, heads=None, blocks=None, idx=None,
+                  score=None, want_score=True, ws=None, stream=None):
+    """Route, keep the m best complete blocks (+ the partial one), routed top-k among their tokens."""
+    _req(q, torch.bfloat16, "q", 3)
+    T, H, d = q.shape
+    nseq, L, _ = k.shape
+    idx, score = _outs(T, topk, q.device, idx, score, want_score)
+    ws = _workspace(ws, workspace_bytes(OP_BLOCK_INDEXER, T, H, L, B, topk, m), q.device)
+    _check("misa_block_indexer", lib().misa_block_indexer(_ptr(q), _ptr(w), _ptr(k), _ptr(kbar), _ptr(q_seq),
+                                                          _ptr(q_len), T, H, d, nseq, L, B, h, m, topk, _ptr(heads),
+                                                          _ptr(blocks), _ptr(idx), _ptr(score), _ptr(ws), ws.numel(),
+                                                          _stream(stream)))
     return idx, score
 
 

@@ -66,6 +66,11 @@ bool wide_tiles(int64_t T, int64_t nseq) { return T >= 64 && T >= 8 * nseq; }
 // over consecutive positions (multi-token prediction) shares each key pass
 bool few_tiles(int64_t T, int64_t nseq) { return !wide_tiles(T, nseq) && T >= 2 * nseq; }
 
+// Workspace of the block filter: the block score rows and the block counts.
+size_t block_filter_ws_bytes(int64_t T, int64_t Lmax, int32_t B) {
+  return round_up((size_t)T * (size_t)(Lmax / B) * sizeof(float)) + round_up((size_t)T * sizeof(int32_t));
+}
+
 // Workspace of scoring + selection over rows of at most max_len: the fp32 score
 // rows, then (for few long rows) the split top-k's state.
 size_t select_ws_bytes(int64_t T, int64_t max_len) {
@@ -177,6 +182,16 @@ size_t misa_workspace_bytes(int32_t op, int64_t T, int32_t H, int64_t Lmax, int3
       return select_ws_bytes(T, Lmax);
     case MISA_OP_HIER_RERANK:
       return select_ws_bytes(T, kc > 0 ? kc : 0);
+    case MISA_OP_BLOCK_FILTER:
+      if (B < 1) return 0;
+      return block_filter_ws_bytes(T, Lmax, B);
+    case MISA_OP_BLOCK_INDEXER: {
+      if (B < 1 || H < 1 || kc < 1) return 0;
+      const int64_t nc = ((int64_t)kc + 1) * B;
+      const size_t fs = block_filter_ws_bytes(T, Lmax, B), ss = select_ws_bytes(T, nc);
+      return misa_workspace_bytes(MISA_OP_ROUTE, T, H, Lmax, B, 0, 0) + round_up((size_t)T * H * 4) +
+             round_up((size_t)T * (size_t)kc * 4) + round_up((size_t)T * (size_t)nc * 4) + (fs > ss ? fs : ss);
+    }
     case MISA_OP_INDEXER:
     case MISA_OP_HIER_INDEXER: {
       if (B < 1 || H < 1) return 0;
@@ -558,6 +573,120 @@ int32_t misa_hier_indexer(const void* q, const float* w, const void* k, const fl
                           float* score, void* ws, size_t ws_bytes, void* stream) {
   return run_indexer("misa_hier_indexer", true, q, w, k, kbar, q_seq, q_len, T, H, d, nseq, Lmax, B, h, kc, topk,
                      heads, cand, idx, score, ws, ws_bytes, (hipStream_t)stream);
+}
+
+namespace {
+
+// Checks of the block filter's own arguments (q, w, kbar, q_seq, q_len checked before).
+int32_t check_block(const char* fn, int64_t T, int32_t H, int64_t Lmax, int32_t B, int32_t h, int32_t m) {
+  if (B < 1 || B > Lmax) return fail(MISA_ERR_ARG, "%s: B = %d not in [1, Lmax]", fn, B);
+  if (h < 1 || h > H) return fail(MISA_ERR_ARG, "%s: h = %d not in [1, H = %d]", fn, h, H);
+  if (m < 1 || m > Lmax / B) return fail(MISA_ERR_ARG, "%s: m = %d not in [1, Lmax / B = %lld]", fn, m, (long long)(Lmax / B));
+  const int64_t kc = ((int64_t)m + 1) * B;
+  if (kc >= (int64_t(1) << 30)) return fail(MISA_ERR_ARG, "%s: (m + 1) * B too large", fn);
+  const int64_t nchunk = (Lmax / B + 63) / 64;
+  if (T * nchunk >= (int64_t(1) << 32) || T * ((kc + 255) / 256) >= (int64_t(1) << 32))
+    return fail(MISA_ERR_ARG, "%s: grid too large", fn);
+  return MISA_OK;
+}
+
+// Block scores, the top-m complete blocks (ordinary top-k over the score rows)
+// and, if cand is given, the candidate token list.
+int32_t block_filter_run(const char* fn, const void* q, const float* w, const float* kbar, const int32_t* heads,
+                         int32_t h, const int32_t* q_seq, const int32_t* q_len, int64_t T, int32_t H, int32_t d,
+                         int64_t nseq, int64_t Lmax, int32_t B, int32_t m, int32_t* blocks, int32_t* cand, void* ws,
+                         hipStream_t st) {
+  misa::BlockArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.w = w;
+  a.kbar = kbar;
+  a.heads = heads;
+  a.h = h;
+  a.q_seq = q_seq;
+  a.q_len = q_len;
+  a.T = T;
+  a.H = H;
+  a.nseq = nseq;
+  a.Lmax = Lmax;
+  a.B = B;
+  a.nblk = Lmax / B;
+  a.bscore = static_cast<float*>(ws);
+  a.blen = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + round_up((size_t)T * (size_t)a.nblk * sizeof(float)));
+  hipError_t e = misa::launch_block_score(a, d, st);
+  if (e != hipSuccess) return hip_status(e, fn);
+  misa::TopkArgs b{};
+  b.scores = a.bscore;
+  b.stride = a.nblk;
+  b.q_seq = q_seq;
+  b.q_len = a.blen;
+  b.nseq = nseq;
+  b.Lmax = a.nblk;
+  b.imap = nullptr;
+  b.kc = 0;
+  b.T = T;
+  b.k = m;
+  b.idx = blocks;
+  b.score = nullptr;
+  e = misa::launch_topk(b, st);
+  if (e != hipSuccess) return hip_status(e, fn);
+  if (cand) e = misa::launch_block_expand(a, blocks, m, cand, (m + 1) * B, st);
+  return hip_status(e, fn);
+}
+
+}  // namespace
+
+int32_t misa_block_filter(const void* q, const float* w, const float* kbar, const int32_t* heads, int32_t h,
+                          const int32_t* q_seq, const int32_t* q_len, int64_t T, int32_t H, int32_t d, int64_t nseq,
+                          int64_t Lmax, int32_t B, int32_t m, int32_t* blocks, int32_t* cand, void* ws,
+                          size_t ws_bytes, void* stream) {
+  const char* fn = "misa_block_filter";
+  int32_t rc = check_common(fn, q, w, kbar, q_seq, q_len, T, H, d, nseq, Lmax);   // kbar in the place of k
+  if (rc) return rc;
+  rc = check_block(fn, T, H, Lmax, B, h, m);
+  if (rc) return rc;
+  if (T == 0) return ok();
+  if (!heads || !blocks) return fail(MISA_ERR_ARG, "%s: null heads/blocks", fn);
+  if (!aligned(heads, 4) || !aligned(blocks, 4) || !aligned(cand, 4))
+    return fail(MISA_ERR_ALIGN, "%s: heads/blocks/cand must be 4-byte aligned", fn);
+  rc = check_ws(fn, ws, ws_bytes, misa_workspace_bytes(MISA_OP_BLOCK_FILTER, T, H, Lmax, B, 0, m));
+  if (rc) return rc;
+  return block_filter_run(fn, q, w, kbar, heads, h, q_seq, q_len, T, H, d, nseq, Lmax, B, m, blocks, cand, ws,
+                          (hipStream_t)stream);
+}
+
+int32_t misa_block_indexer(const void* q, const float* w, const void* k, const float* kbar, const int32_t* q_seq,
+                           const int32_t* q_len, int64_t T, int32_t H, int32_t d, int64_t nseq, int64_t Lmax,
+                           int32_t B, int32_t h, int32_t m, int32_t topk, int32_t* heads, int32_t* blocks,
+                           int32_t* idx, float* score, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "misa_block_indexer";
+  int32_t rc = check_common(fn, q, w, k, q_seq, q_len, T, H, d, nseq, Lmax);
+  if (rc) return rc;
+  rc = check_block(fn, T, H, Lmax, B, h, m);
+  if (rc) return rc;
+  if (topk < 1) return fail(MISA_ERR_ARG, "%s: topk = %d < 1", fn, topk);
+  if (T == 0) return ok();
+  if (!kbar || !aligned(kbar, 16)) return fail(MISA_ERR_ARG, "%s: kbar must be a 16-byte aligned pointer", fn);
+  rc = check_outputs(fn, topk, idx, score);
+  if (rc) return rc;
+  if (!aligned(heads, 4) || !aligned(blocks, 4)) return fail(MISA_ERR_ALIGN, "%s: heads/blocks must be 4-byte aligned", fn);
+  rc = check_ws(fn, ws, ws_bytes, misa_workspace_bytes(MISA_OP_BLOCK_INDEXER, T, H, Lmax, B, topk, m));
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  const int32_t kc = (m + 1) * B;
+  char* p = static_cast<char*>(ws);
+  const size_t rws = misa_workspace_bytes(MISA_OP_ROUTE, T, H, Lmax, B, 0, 0);
+  int32_t* hd = heads ? heads : reinterpret_cast<int32_t*>(p + rws);
+  p += rws + round_up((size_t)T * H * 4);
+  int32_t* bl = blocks ? blocks : reinterpret_cast<int32_t*>(p);
+  p += round_up((size_t)T * (size_t)m * 4);
+  int32_t* cd = reinterpret_cast<int32_t*>(p);
+  p += round_up((size_t)T * (size_t)kc * 4);
+  rc = misa_route(q, w, k, kbar, q_seq, q_len, T, H, d, nseq, Lmax, B, h, hd, nullptr, ws, rws, st);
+  if (rc) return rc;
+  rc = block_filter_run(fn, q, w, kbar, hd, h, q_seq, q_len, T, H, d, nseq, Lmax, B, m, bl, cd, p, st);
+  if (rc) return rc;
+  return score_and_select(fn, q, w, k, hd, h, cd, kc, q_seq, q_len, T, H, d, nseq, Lmax, topk, idx, score,
+                          reinterpret_cast<float*>(p), kc, st);
 }
 
 int32_t misa_debug_scores(const void* q, const float* w, const void* k, const int32_t* heads, int32_t h,

@@ -141,6 +141,31 @@ struct RescoreArgs {
 hipError_t launch_topk_split_rescore(const TopkArgs& a, const SplitTopkWs& w, const RescoreArgs& r, hipStream_t st);
 
 
+// Coarse stage of the block filter: the routed indexer formula on the pooled
+// keys of each query's complete blocks.
+struct BlockArgs {
+  const uint16_t* q;        // bf16 [T][H][d]
+  const float* w;           // fp32 [T][H]
+  const float* kbar;        // fp32 [nseq][nblk][d]
+  const int32_t* heads;     // [T][h] (an id outside [0, H) contributes nothing)
+  int h;
+  const int32_t* q_seq;
+  const int32_t* q_len;
+  int64_t T;
+  int H;
+  int64_t nseq;
+  int64_t Lmax;
+  int B;
+  int64_t nblk;             // Lmax / B pooled blocks per sequence
+  float* bscore;            // [T][nblk] block scores (complete visible blocks)
+  int32_t* blen;            // [T] complete visible blocks of each query
+};
+hipError_t launch_block_score(const BlockArgs& a, int d, hipStream_t st);
+// cand [T][kc]: the tokens of the m retained blocks (blocks [T][m], ascending,
+// -1 padded), then the partial block's tokens, then -1
+hipError_t launch_block_expand(const BlockArgs& a, const int32_t* blocks, int m, int32_t* cand, int kc,
+                               hipStream_t st);
+
 // Event timing of one internal kernel class (measurement aid).
 enum KernelId { KID_NONE = 0, KID_SCORE = 1, KID_TOPK = 2, KID_ROUTE = 3, KID_POOL = 4, KID_GATHER_SCORE = 5 };
 void timing_before(int kid, hipStream_t st);

@@ -145,6 +145,32 @@ def test_pool_update_checks(L):
     assert L.misa_pool_update(FAKE, 0, 4096, 128, 64, FAKE, FAKE, 1, FAKE, None) == 0      # nothing to do
 
 
+def test_block_filter_checks(L):
+    from routed_token_indexer_amd import _lib as B
+    args = lambda **o: [o.get("q", FAKE), FAKE, FAKE, FAKE, o.get("h", 8), FAKE, FAKE, o.get("T", 4), 64, o.get("d", 128),
+                        4, o.get("Lmax", 4096), o.get("B", 64), o.get("m", 16), o.get("blocks", FAKE), None, FAKE,
+                        1 << 30, None]
+    assert L.misa_block_filter(*args(m=0)) == -1
+    assert "m = 0" in _err(L)
+    assert L.misa_block_filter(*args(m=65)) == -1                     # > Lmax / B
+    assert L.misa_block_filter(*args(B=0)) == -1
+    assert L.misa_block_filter(*args(h=65)) == -1
+    assert L.misa_block_filter(*args(d=96)) == -1
+    assert L.misa_block_filter(*args(blocks=None)) == -1
+    assert L.misa_block_filter(*args(q=ctypes.c_void_p((1 << 20) + 8))) == -2
+    assert L.misa_block_filter(*args(T=0)) == 0
+    small = args()
+    small[-2] = 16
+    assert L.misa_block_filter(*small) == -3
+    # block scores (fp32 per block) and block counts
+    assert B.workspace_bytes(B.OP_BLOCK_FILTER, 4, 64, 131072, 128, 0, 64) == 4 * 1024 * 4 + 256
+    assert B.workspace_bytes(B.OP_BLOCK_INDEXER, 4, 64, 131072, 128, 2048, 64) > 4 * 65 * 128 * 4 * 2
+    assert L.misa_block_indexer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 128, 4, 4096, 64, 8, 16, 0, None, None,
+                                FAKE, None, FAKE, 1 << 30, None) == -1     # topk
+    assert L.misa_block_indexer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, 128, 4, 4096, 64, 8, 0, 64, None, None,
+                                FAKE, None, FAKE, 1 << 30, None) == -1     # m
+
+
 def test_empty_batch_is_a_noop(L):
     # T = 0: valid, nothing enqueued, no pointer touched
     assert L.misa_score_topk(None, None, None, None, 8, None, None, 0, 64, 128, 4, 4096, 64, None, None, None, 0,
