@@ -300,6 +300,15 @@ def main():
         rows["all_rows_us"] = timed(lambda i: (M.pool_keys(ks[i % ncopy], B, kbar=kbar_pf), step(i),
                                                M.dsa_index_dense(q, w, ks[i % ncopy], q_seq, q_len, topk, idx=didx,
                                                                  score=dsc, ws=ws_dense)), n, 3) * 1e3
+        if not prefill:
+            # the block filter composed with routing: m complete blocks kept per
+            # query (about 4 * topk candidate tokens), routed top-k among them
+            m_blk = max(1, min(L // B, (4 * topk) // B))
+            bidx = torch.empty_like(idx)
+            ws_blk = ws(M.OP_BLOCK_INDEXER, B=B, topk=topk, kc=m_blk)
+            rows["block_indexer_us"] = timed(lambda i: M.block_indexer(q, w, ks[i % ncopy], kbars[i % ncopy], q_seq,
+                                                                       q_len, B, h, m_blk, topk, idx=bidx,
+                                                                       want_score=False, ws=ws_blk), n, 3) * 1e3
         out["rows"] = {kk: round(v, 2) for kk, v in rows.items()}
         # recall of the routed selections against the dense indexer on the same inputs (no target)
         if not prefill:
@@ -313,6 +322,10 @@ def main():
             out["recall_vs_dense"] = {"misa": round(rec(ro), 4)}
             if hier:
                 out["recall_vs_dense"]["misa_hier"] = round(rec(fi), 4)
+            M.block_indexer(q, w, ks[0], kbars[0], q_seq, q_len, B, h, m_blk, topk, idx=bidx, want_score=False,
+                            ws=ws_blk)
+            torch.cuda.synchronize()
+            out["recall_vs_dense"][f"block_filter_m{m_blk}"] = round(rec(bidx.cpu().numpy()), 4)
 
     # ---- the CPU oracle on the host cores, on a bounded sample of the same workload
     if not args.no_cpu_baseline:

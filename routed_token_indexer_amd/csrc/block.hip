@@ -14,12 +14,13 @@
 // blocks followed by those of its partial block, ascending, -1 padded; the
 // routed scoring and top-k of the fine stage run over that list in gather mode.
 //
-// block_score_kernel: one wave per (64 blocks, query). Lane j owns block j:
-// its pooled key row is read with 16-byte loads (the row stays in the lane's
-// registers four values at a time) and multiplied by the routed query rows,
-// which sit in LDS as bf16 and are read as broadcasts. Eight heads are summed
-// per pass over the row. The cost is a few µs of latency: 1024 pooled rows of
-// d = 128 are 512 KiB per query.
+// block_score_kernel: one workgroup of four waves per (64 blocks, query). The
+// 64 pooled key rows (contiguous in memory) are read once, coalesced, into an
+// LDS tile (16-byte pieces XOR-swizzled by row, so that the row reads below are
+// conflict-free; d = 256 in four quarters). Lane j of every wave then takes row j
+// into registers, and wave w multiplies it by the routed query rows w, w + 4,
+// ... (bf16 in LDS, read as broadcasts). The per-head dots meet in LDS, where
+// wave 0 applies the ReLU and the weights in head order.
 #include "misa_common.hpp"
 #include "misa_internal.hpp"
 
@@ -30,68 +31,99 @@ extern __shared__ __attribute__((aligned(16))) uint16_t block_q_lds[];
 
 namespace {
 
-constexpr int kBlockWave = 64;   // blocks per workgroup (one wave)
-constexpr int kHeadGroup = 8;    // heads summed per pass over a pooled row
+constexpr int kBlockWave = 64;   // blocks per workgroup
+constexpr int kBlockWaves = 4;   // waves per workgroup (heads split among them)
 
 template <int D>
-__global__ __launch_bounds__(kBlockWave) void block_score_kernel(BlockArgs a) {
-  uint16_t* const s_q = block_q_lds;
+__global__ __launch_bounds__(64 * kBlockWaves) void block_score_kernel(BlockArgs a) {
+  // row floats staged at once: with h = 64 routed rows the tile, the query
+  // rows and the dots fill at most 64 KiB of LDS
+  constexpr int HALF = D == 256 ? 64 : D;
+  constexpr int NV = HALF / 4;              // 16-byte pieces of a staged row
+  constexpr int NT = 64 * kBlockWaves;
+  __shared__ floatx4 s_k[kBlockWave * NV];  // [64 rows][NV pieces], piece u of row r at u ^ (r & 7)
+  uint16_t* const s_q = block_q_lds;                                     // [h][D] bf16
+  float* const s_dot = reinterpret_cast<float*>(block_q_lds + a.h * D);  // [h][64] fp32
   // 1-D grid: query t, chunk of 64 of its blocks
   const int64_t nchunk = a.nblk > 0 ? (a.nblk + kBlockWave - 1) / kBlockWave : 1;
   const int64_t t = blockIdx.x / nchunk;
   const int64_t chunk = blockIdx.x % nchunk;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int p = query_prefix_len(a.q_seq, a.q_len, a.nseq, a.Lmax, t);
   const int nb = p < 0 ? 0 : p / a.B;
-  if (chunk == 0 && lane == 0) a.blen[t] = nb;
+  if (chunk == 0 && tid == 0) a.blen[t] = nb;
   const int64_t j0 = chunk * kBlockWave;
   if (j0 >= nb) return;
   const int64_t seq = a.q_seq[t];
   const int h = a.h;
   const int32_t* hrow = a.heads + t * h;
+  const float* kseq = a.kbar + seq * a.nblk * D;
+  // tile loads: piece i of the tile is row i / NV (clamped to the last visible
+  // block), piece i % NV
+  constexpr int PPT = kBlockWave * NV / NT;   // pieces per thread
+  auto load_tile = [&](int c0, floatx4* v) {
+#pragma unroll
+    for (int r = 0; r < PPT; ++r) {
+      const int i = tid + NT * r;
+      const int64_t row = j0 + i / NV < nb ? j0 + i / NV : nb - 1;
+      v[r] = *reinterpret_cast<const floatx4*>(kseq + row * D + c0 + 4 * (i % NV));
+    }
+  };
+  auto store_tile = [&](const floatx4* v) {
+#pragma unroll
+    for (int r = 0; r < PPT; ++r) {
+      const int i = tid + NT * r;
+      const int row = i / NV, u = i % NV;
+      s_k[row * NV + (u ^ (row & 7))] = v[r];
+    }
+  };
+  floatx4 tv[PPT];
+  load_tile(0, tv);
   // stage the routed rows, 8 bf16 per 16-byte piece (an id outside [0, H)
   // stages zeros and contributes nothing)
   constexpr int PPR = D / 8;
-  for (int i = lane; i < h * PPR; i += kBlockWave) {
+  for (int i = tid; i < h * PPR; i += NT) {
     const int g = hrow[i / PPR];
     u32x4 v = {0u, 0u, 0u, 0u};
     if (g >= 0 && g < a.H) v = *reinterpret_cast<const u32x4*>(a.q + (t * a.H + g) * D + (i % PPR) * 8);
     *reinterpret_cast<u32x4*>(s_q + (i / PPR) * D + (i % PPR) * 8) = v;
   }
-  __syncthreads();
-  const int64_t j = j0 + lane;
-  const bool ok = j < nb;
-  const float* krow = a.kbar + (seq * a.nblk + (ok ? j : j0)) * D;
-  float b = 0.f;
-  for (int g0 = 0; g0 < h; g0 += kHeadGroup) {
-    float acc[kHeadGroup];
 #pragma unroll
-    for (int e = 0; e < kHeadGroup; ++e) acc[e] = 0.f;
-#pragma unroll 8
-    for (int c = 0; c < D; c += 4) {
-      const floatx4 kv = *reinterpret_cast<const floatx4*>(krow + c);
-#pragma unroll
-      for (int e = 0; e < kHeadGroup; ++e) {
-        if (g0 + e < h) {
-          const uint2 qq = *reinterpret_cast<const uint2*>(s_q + (g0 + e) * D + c);
-          float x = acc[e];
-          x = fmaf(bf16_lo(qq.x), kv[0], x);
-          x = fmaf(bf16_hi(qq.x), kv[1], x);
-          x = fmaf(bf16_lo(qq.y), kv[2], x);
-          x = fmaf(bf16_hi(qq.y), kv[3], x);
-          acc[e] = x;
-        }
-      }
+  for (int c0 = 0; c0 < D; c0 += HALF) {
+    if (c0 > 0) {
+      load_tile(c0, tv);
+      __syncthreads();   // every wave has read the previous half from the tile
     }
+    store_tile(tv);
+    __syncthreads();
+    floatx4 kv[NV];
 #pragma unroll
-    for (int e = 0; e < kHeadGroup; ++e) {
-      if (g0 + e < h) {
-        const int g = hrow[g0 + e];
-        if (g >= 0 && g < a.H) b += a.w[t * a.H + g] * relu(acc[e]);
+    for (int u = 0; u < NV; ++u) kv[u] = s_k[lane * NV + (u ^ (lane & 7))];
+    for (int g = wave; g < h; g += kBlockWaves) {
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < NV; ++u) {
+        const uint2 qq = *reinterpret_cast<const uint2*>(s_q + g * D + c0 + 4 * u);
+        float x = acc[u & 3];
+        x = fmaf(bf16_lo(qq.x), kv[u][0], x);
+        x = fmaf(bf16_hi(qq.x), kv[u][1], x);
+        x = fmaf(bf16_lo(qq.y), kv[u][2], x);
+        x = fmaf(bf16_hi(qq.y), kv[u][3], x);
+        acc[u & 3] = x;
       }
+      const float dot = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      s_dot[g * 64 + lane] = c0 == 0 ? dot : s_dot[g * 64 + lane] + dot;   // only this wave owns head g
     }
   }
-  if (ok) a.bscore[t * a.nblk + j] = b;
+  __syncthreads();
+  if (wave != 0) return;
+  const int64_t j = j0 + lane;
+  float b = 0.f;
+  for (int g = 0; g < h; ++g) {
+    const int hg = hrow[g];
+    if (hg >= 0 && hg < a.H) b += a.w[t * a.H + hg] * relu(s_dot[g * 64 + lane]);
+  }
+  if (j < nb) a.bscore[t * a.nblk + j] = b;
 }
 
 // cand[t][i]: token i of the retained blocks (in block order), then the
@@ -121,13 +153,13 @@ hipError_t launch_block_score(const BlockArgs& a, int d, hipStream_t st) {
   if (a.T == 0) return hipSuccess;
   // at least one workgroup per query: it writes the query's block count
   const int64_t nchunk = a.nblk > 0 ? (a.nblk + kBlockWave - 1) / kBlockWave : 1;
-  const dim3 grid((unsigned)(nchunk * a.T));
-  const size_t lds = (size_t)a.h * d * sizeof(uint16_t);
+  const dim3 grid((unsigned)(nchunk * a.T)), block(64 * kBlockWaves);
+  const size_t lds = (size_t)a.h * d * sizeof(uint16_t) + (size_t)a.h * 64 * sizeof(float);
   switch (d) {
-    case 32: hipLaunchKernelGGL(block_score_kernel<32>, grid, dim3(kBlockWave), lds, st, a); break;
-    case 64: hipLaunchKernelGGL(block_score_kernel<64>, grid, dim3(kBlockWave), lds, st, a); break;
-    case 128: hipLaunchKernelGGL(block_score_kernel<128>, grid, dim3(kBlockWave), lds, st, a); break;
-    case 256: hipLaunchKernelGGL(block_score_kernel<256>, grid, dim3(kBlockWave), lds, st, a); break;
+    case 32: hipLaunchKernelGGL(block_score_kernel<32>, grid, block, lds, st, a); break;
+    case 64: hipLaunchKernelGGL(block_score_kernel<64>, grid, block, lds, st, a); break;
+    case 128: hipLaunchKernelGGL(block_score_kernel<128>, grid, block, lds, st, a); break;
+    case 256: hipLaunchKernelGGL(block_score_kernel<256>, grid, block, lds, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
