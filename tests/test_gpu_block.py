@@ -220,3 +220,45 @@ def test_empty_batch_is_a_noop():
     q0 = dev["q"][:0]
     idx, _ = M.block_indexer(q0, dev["w"][:0], dev["k"], kbar, dev["q_seq"][:0], dev["q_len"][:0], x.cfg.B, 8, 4, 64)
     assert idx.shape == (0, 64)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
+@pytest.mark.parametrize("H,h", [(8, 2), (40, 5), (64, 16), (64, 64)])
+def test_block_shapes(d, H, h):
+    """Every head dim (d = 256 staged in four quarters), head counts that leave
+    waves without a head or give one wave many, and a ragged last chunk of
+    blocks: grid-exact blocks, candidate lists and selections."""
+    x = make_inputs("c1", mode="grid", L=2500, T=3, nseq=3, H=H, d=d, h=h, B=32, topk=100)
+    x.q_len[:] = np.array([2500, 2077, 95], np.int32)
+    dev = upload(x)
+    B, m = x.cfg.B, 9
+    ho, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, B, h)
+    kbar = M.pool_keys(dev["k"], B)
+    blocks, cand = M.block_filter(dev["q"], dev["w"], kbar, torch.from_numpy(ho).cuda(), dev["q_seq"],
+                                  dev["q_len"], x.cfg.L, B, m)
+    ob = O.block_filter(x.q, x.w, x.k, ho, x.q_seq, x.q_len, B, m)
+    np.testing.assert_array_equal(blocks.cpu().numpy(), ob)
+    for t in range(3):
+        np.testing.assert_array_equal(cand.cpu().numpy()[t], expected_cand(ob[t], int(x.q_len[t]), B, m))
+    idx, sc = M.block_indexer(dev["q"], dev["w"], dev["k"], kbar, dev["q_seq"], dev["q_len"], B, h, m, 100)
+    _, _, oi, ov = O.block_indexer(x.q, x.w, x.k, x.q_seq, x.q_len, B, h, m, 100)
+    np.testing.assert_array_equal(idx.cpu().numpy(), oi)
+    np.testing.assert_array_equal(sc.cpu().numpy(), ov.astype(np.float32))
+
+
+def test_block_non_power_of_two_block_and_negative_weights():
+    """B = 48 (inexact means: Gaussian tolerance rules) and weights of both signs
+    (a head may lower a block's score)."""
+    x = make_inputs("c1", mode="gauss", L=2000, T=4, nseq=4, B=48, topk=200)
+    rng = np.random.default_rng(3)
+    x.w[:] = (x.w * np.where(rng.random(x.w.shape) < 0.3, -1.0, 1.0)).astype(np.float32)
+    dev = upload(x)
+    B, m = x.cfg.B, 10
+    ho, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, B, x.cfg.h)
+    kbar = M.pool_keys(dev["k"], B)
+    blocks, cand = M.block_filter(dev["q"], dev["w"], kbar, torch.from_numpy(ho).cuda(), dev["q_seq"],
+                                  dev["q_len"], x.cfg.L, B, m)
+    blocks, cand = blocks.cpu().numpy(), cand.cpu().numpy()
+    for t in range(4):
+        g = check_blocks(x, ho[t], t, blocks[t], m, False, f"t={t}")
+        np.testing.assert_array_equal(cand[t], expected_cand(g, int(x.q_len[t]), B, m))
