@@ -614,6 +614,8 @@ int32_t block_filter_run(const char* fn, const void* q, const float* w, const fl
   a.blen = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + round_up((size_t)T * (size_t)a.nblk * sizeof(float)));
   hipError_t e = misa::launch_block_score(a, d, st);
   if (e != hipSuccess) return hip_status(e, fn);
+  if (cand && misa::block_select_fused(a))   // selection and candidate list in one launch
+    return hip_status(misa::launch_block_select(a, m, blocks, cand, (m + 1) * B, st), fn);
   misa::TopkArgs b{};
   b.scores = a.bscore;
   b.stride = a.nblk;

@@ -23,6 +23,7 @@
 // wave 0 applies the ReLU and the weights in head order.
 #include "misa_common.hpp"
 #include "misa_internal.hpp"
+#include "misa_select.hpp"
 
 namespace misa {
 
@@ -147,7 +148,100 @@ __global__ __launch_bounds__(256) void block_expand_kernel(BlockArgs a, const in
   cand[t * (int64_t)kc + i] = v;
 }
 
+// The m best complete blocks of one query and its candidate list, in one
+// workgroup of 1024 threads (rows of at most kSelMaxBlocks block scores).
+// Thread i holds blocks 4i .. 4i + 3, so thread order is block order. A radix
+// select over the order-preserving keys finds the threshold; the kept blocks
+// (keys above it, then the lowest-id ones equal to it) get their output slots
+// from two prefix sums in thread order, so the list comes out ascending. The
+// candidate list is then written from the kept list in LDS, coalesced.
+constexpr int kSelEPT = 4;
+constexpr int kSelMaxBlocks = kSelEPT * kSelThreads;
+
+__global__ __launch_bounds__(kSelThreads) void block_select_kernel(BlockArgs a, int m, int32_t* __restrict__ blocks,
+                                                                  int32_t* __restrict__ cand, int kc) {
+  __shared__ RadixScratch<kSelThreads, 1> rs;
+  __shared__ __attribute__((aligned(16))) uint32_t wsum2[2 * kSelWaves];
+  __shared__ int32_t s_blk[kSelMaxBlocks];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int p = query_prefix_len(a.q_seq, a.q_len, a.nseq, a.Lmax, t);
+  const int nb = p < 0 ? 0 : p / a.B;
+  const int ntail = p < 0 ? 0 : p - nb * a.B;
+  const int nk = nb < m ? nb : m;
+  uint32_t u[kSelEPT];
+#pragma unroll
+  for (int r = 0; r < kSelEPT; ++r) {
+    const int j = kSelEPT * tid + r;
+    u[r] = j < nb ? score_key(a.bscore[t * a.nblk + j]) : 0u;
+  }
+  const bool all = nb <= m;
+  uint32_t prefix = 0, pmask = 0, krem = (uint32_t)nk;
+  if (!all) {
+    radix_clear(rs);
+    __syncthreads();
+    bool full;
+    radix_select<kSelThreads, 1>(
+        [&](auto f) {
+#pragma unroll
+          for (int r = 0; r < kSelEPT; ++r)
+            if (kSelEPT * tid + r < nb) f(u[r]);
+        },
+        32, prefix, pmask, krem, full, rs);
+  }
+  // 2 = above the threshold (kept), 1 = equal to it (kept if among the first krem), 0 = below
+  auto cls = [&](int r) -> int {
+    if (kSelEPT * tid + r >= nb) return 0;
+    if (all || (u[r] & pmask) > prefix) return 2;
+    return (u[r] & pmask) == prefix ? 1 : 0;
+  };
+  uint32_t ngt = 0, neq = 0;
+#pragma unroll
+  for (int r = 0; r < kSelEPT; ++r) {
+    const int c = cls(r);
+    ngt += c == 2 ? 1u : 0u;
+    neq += c == 1 ? 1u : 0u;
+  }
+  uint32_t eq_before;
+  const uint32_t gt_before = block_excl_scan2(ngt, neq, wsum2, eq_before);
+  uint32_t pos = gt_before + (eq_before < krem ? eq_before : krem);
+  uint32_t er = eq_before;
+#pragma unroll
+  for (int r = 0; r < kSelEPT; ++r) {
+    const int c = cls(r);
+    bool keep = c == 2;
+    if (c == 1) keep = er++ < krem;
+    if (keep) {
+      const int j = kSelEPT * tid + r;
+      s_blk[pos] = j;
+      blocks[t * m + pos] = j;
+      ++pos;
+    }
+  }
+  for (int i = nk + tid; i < m; i += kSelThreads) blocks[t * m + i] = -1;
+  __syncthreads();
+  const int nfull = nk * a.B;
+  int32_t* crow = cand + t * (int64_t)kc;
+  for (int i = tid; i < kc; i += kSelThreads) {
+    int32_t v = -1;
+    if (i < nfull)
+      v = s_blk[i / a.B] * a.B + i % a.B;
+    else if (i < nfull + ntail)
+      v = nb * a.B + (i - nfull);
+    crow[i] = v;
+  }
+}
+
 }  // namespace
+
+bool block_select_fused(const BlockArgs& a) { return a.nblk <= kSelMaxBlocks; }
+
+hipError_t launch_block_select(const BlockArgs& a, int m, int32_t* blocks, int32_t* cand, int kc, hipStream_t st) {
+  if (a.T == 0) return hipSuccess;
+  if (!block_select_fused(a)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(block_select_kernel, dim3((unsigned)a.T), dim3(kSelThreads), 0, st, a, m, blocks, cand, kc);
+  return hipGetLastError();
+}
 
 hipError_t launch_block_score(const BlockArgs& a, int d, hipStream_t st) {
   if (a.T == 0) return hipSuccess;

@@ -165,6 +165,9 @@ hipError_t launch_block_score(const BlockArgs& a, int d, hipStream_t st);
 // -1 padded), then the partial block's tokens, then -1
 hipError_t launch_block_expand(const BlockArgs& a, const int32_t* blocks, int m, int32_t* cand, int kc,
                                hipStream_t st);
+// Both in one launch (rows of up to 4096 complete blocks: block_select_fused).
+bool block_select_fused(const BlockArgs& a);
+hipError_t launch_block_select(const BlockArgs& a, int m, int32_t* blocks, int32_t* cand, int kc, hipStream_t st);
 
 // Event timing of one internal kernel class (measurement aid).
 enum KernelId { KID_NONE = 0, KID_SCORE = 1, KID_TOPK = 2, KID_ROUTE = 3, KID_POOL = 4, KID_GATHER_SCORE = 5 };

@@ -262,3 +262,26 @@ def test_block_non_power_of_two_block_and_negative_weights():
     for t in range(4):
         g = check_blocks(x, ho[t], t, blocks[t], m, False, f"t={t}")
         np.testing.assert_array_equal(cand[t], expected_cand(g, int(x.q_len[t]), B, m))
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_block_selection_paths_agree(mode):
+    """The one-launch selection (rows of up to 4096 blocks), the ordinary top-k
+    over the block rows (no candidate list asked for) and rows of more than 4096
+    blocks (B = 8 over 40001 keys) all give the oracle's blocks."""
+    for B, m in ((64, 100), (8, 300)):
+        x = make_inputs("c1", mode=mode, L=40001, T=4, nseq=4, B=B, topk=1000)
+        x.q_len[:] = np.array([40001, 39000, 4100, 7], np.int32)
+        dev = upload(x)
+        ho, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, B, x.cfg.h)
+        hd = torch.from_numpy(ho).cuda()
+        kbar = M.pool_keys(dev["k"], B)
+        b1, cand = M.block_filter(dev["q"], dev["w"], kbar, hd, dev["q_seq"], dev["q_len"], x.cfg.L, B, m)
+        b2, none = M.block_filter(dev["q"], dev["w"], kbar, hd, dev["q_seq"], dev["q_len"], x.cfg.L, B, m,
+                                  want_cand=False)
+        assert none is None and torch.equal(b1, b2)
+        b1, cand = b1.cpu().numpy(), cand.cpu().numpy()
+        for t in range(4):
+            label = f"B={B} {mode} t={t}"
+            g = check_blocks(x, ho[t], t, b1[t], m, mode == "grid", label)
+            np.testing.assert_array_equal(cand[t], expected_cand(g, int(x.q_len[t]), B, m), err_msg=label)
