@@ -22,8 +22,8 @@ Notation (pages' notation where they have one):
 Status of each function's pin (see tests/test_oracle_*.py):
   pool_keys, route, routed_scores, select_topk, score_topk, dsa_index_dense,
   hier_rerank, misa_indexer, misa_hier_indexer, block_filter,
-  score_topk_in_blocks, block_indexer: pinned (brute force, closed forms,
-  invariants). The router's aggregation rule is a reading of the pages;
+  score_topk_in_blocks, block_indexer, bf16_round, pivot_proxy,
+  pivot_indexer: pinned (brute force, closed forms, invariants). The router's aggregation rule is a reading of the pages;
   agreement with the authors' own (unpublished) router is "parity unpinned".
 """
 from __future__ import annotations
@@ -36,6 +36,7 @@ __all__ = [
     "pool_keys", "router_values", "route", "routed_scores", "select_topk", "score_topk",
     "dsa_index_dense", "hier_rerank", "misa_indexer", "misa_hier_indexer", "mac_count",
     "block_scores", "block_filter", "block_candidates", "score_topk_in_blocks", "block_indexer",
+    "bf16_round", "pivot_proxy", "pivot_indexer",
 ]
 
 
@@ -334,6 +335,75 @@ def block_indexer(q, w, k, q_seq, q_len, B: int, h: int, m: int, topk: int, quer
     blocks = block_filter(q, w, k, heads, q_seq, q_len, B, m, queries=queries)
     idx, val = score_topk_in_blocks(q, w, k, heads, blocks, q_seq, q_len, B, topk, queries=queries)
     return heads, blocks, idx, val
+
+
+# ------------------------------------------------------------------ proxy-query shared scan (PIVOT-Refine)
+# PIVOT (thelatestinai.com paper cards, the PIVOT abstract): nearby queries pick
+# overlapping top-k sets, so a group of them is folded into one proxy query,
+# the proxy scans the full prefix once to give a candidate set, and (the Refine
+# variant) every query of the group re-scores those candidates with its own
+# indexer and keeps its own top-k. Groups are fixed runs of consecutive queries
+# (prefill) or the queries of one multi-token decode step.
+#
+# Readings taken (the page does not say how the proxy is formed):
+#  - the proxy's per-head query is the sum of the group's per-head queries, and
+#    its head weights the sum of theirs: the mean up to the positive factor n
+#    (the group size), which changes no ranking and needs no division;
+#  - the proxy query is handed to the indexer in its input precision, bf16,
+#    rounded to nearest even; the weights stay fp32;
+#  - the proxy scans the longest prefix of its group with the dense indexer
+#    (all H heads) and keeps k' candidates (ties to the lower token id);
+#  - the refine stage is the MISA-dagger re-rank of those candidates for each
+#    query, over its own visible prefix.
+
+
+def bf16_round(x) -> np.ndarray:
+    """Nearest bfloat16 value (ties to even) of each element, as float64.
+
+    A bfloat16 keeps the top 16 bits of a float32: 8 exponent bits and 7
+    fraction bits. x is first taken to float32 (exact for the sums formed
+    here); the low 16 bits are then rounded off, ties to the even neighbour."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    low = u & 0xFFFF
+    keep = u >> 16
+    up = (low > 0x8000) | ((low == 0x8000) & ((keep & 1) == 1))
+    r = ((keep + up.astype(np.uint64)) << 16).astype(np.uint32)
+    return r.view(np.float32).astype(np.float64)
+
+
+def pivot_proxy(q, w, q_seq, q_len, G: int):
+    """Proxy of each group of G consecutive queries (the last group may be shorter).
+
+    Returns q_proxy [ng, H, d] (bf16 values as float64), w_proxy [ng, H],
+    the group's sequence (that of its first query) and its longest prefix."""
+    q = _f64(q)
+    w = _f64(w)
+    T = q.shape[0]
+    ng = -(-T // G)
+    qp = np.stack([bf16_round(q[i * G:(i + 1) * G].sum(axis=0)) for i in range(ng)])
+    wp = np.stack([w[i * G:(i + 1) * G].sum(axis=0) for i in range(ng)])
+    gseq = np.array([int(q_seq[i * G]) for i in range(ng)])
+    glen = np.array([int(np.max(q_len[i * G:(i + 1) * G])) for i in range(ng)])
+    return qp, wp, gseq, glen
+
+
+def pivot_indexer(q, w, k, q_seq, q_len, G: int, kc: int, topk: int, queries=None):
+    """PIVOT-Refine: one dense scan per group by its proxy keeps k' candidates;
+    each query re-ranks them with its own dense indexer (as MISA-dagger's fine
+    stage) to its top-k. Every query of a group must belong to its sequence."""
+    T = np.asarray(q).shape[0]
+    qs = range(T) if queries is None else list(queries)
+    qp, wp, gseq, glen = pivot_proxy(q, w, q_seq, q_len, G)
+    groups = sorted({t // G for t in qs})
+    gcand = {}
+    for gi in groups:
+        ci, _ = dsa_index_dense(qp[gi:gi + 1], wp[gi:gi + 1], k, gseq[gi:gi + 1], glen[gi:gi + 1], kc)
+        gcand[gi] = ci[0]
+    cand = np.stack([gcand[t // G] for t in qs])
+    idx, val = hier_rerank(q, w, k, np.where(cand < np.asarray(q_len)[list(qs)][:, None], cand, -1),
+                           q_seq, q_len, topk, queries=qs)
+    return cand, idx, val
 
 
 def mac_count(q_len, H: int, h: int, d: int, B: int) -> int:

@@ -502,3 +502,79 @@ def test_block_filter_nested_in_m():
                 assert set(prev_b[t]) - {-1} <= set(bl[t]) - {-1}
             assert np.all(val.min(axis=1) >= prev_v.min(axis=1))
         prev_b, prev_v = bl, val
+
+
+# ------------------------------------------------------------------ proxy-query shared scan (PIVOT-Refine)
+def test_bf16_round_ties_and_library():
+    # halfway cases go to the even neighbour; others to the nearest
+    assert O.bf16_round([1 + 2 ** -8])[0] == 1.0
+    assert O.bf16_round([1 + 2 ** -7 + 2 ** -8])[0] == 1 + 2 ** -6
+    assert O.bf16_round([1 + 3 * 2 ** -9])[0] == 1 + 2 ** -7
+    assert O.bf16_round([-(1 + 2 ** -8 + 2 ** -20)])[0] == -(1 + 2 ** -7)
+    import torch
+    x = np.random.default_rng(4).standard_normal(20000).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.bf16_round(x), ref)
+
+
+def test_hand_pivot(hand):
+    """Queries A (p = 5) and B (p = 4) share q and w, so their proxy is 2q with
+    weights 2w (exact), scanning p = 5: dense scores x4 -> candidates top-2 = {2, 4};
+    A keeps {2, 4}; B cannot see token 4 and keeps {2} (then -1)."""
+    g, keys, q, w, q_seq, q_len = hand
+    qp, wp, gseq, glen = O.pivot_proxy(q, w, q_seq, q_len, 2)
+    np.testing.assert_array_equal(qp[0], 2 * q[0])
+    np.testing.assert_array_equal(wp[0], 2 * w[0])
+    assert glen.tolist() == [5] and gseq.tolist() == [0]
+    cand, idx, val = O.pivot_indexer(q, w, keys, q_seq, q_len, 2, 2, 2)
+    assert cand[0].tolist() == [2, 4] and cand[1].tolist() == [2, 4]
+    assert idx[0].tolist() == [2, 4] and idx[1].tolist() == [2, -1]
+    np.testing.assert_array_equal(val[0], [0.75, 1.0])
+
+
+def test_pivot_single_query_groups_are_dense():
+    for mode in ("gauss", "grid"):
+        x = make_inputs("c0", mode=mode)
+        _, idx, val = O.pivot_indexer(x.q, x.w, x.k, x.q_seq, x.q_len, 1, 2 * x.cfg.topk, x.cfg.topk)
+        di, dv = O.dsa_index_dense(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.topk)
+        np.testing.assert_array_equal(idx, di)
+        np.testing.assert_array_equal(val, dv)
+
+
+def test_pivot_full_candidates_are_dense():
+    x = make_inputs("c0")
+    kc = int(x.q_len.max())
+    for G in (3, 4, 16):
+        _, idx, val = O.pivot_indexer(x.q, x.w, x.k, x.q_seq, x.q_len, G, kc, x.cfg.topk)
+        di, dv = O.dsa_index_dense(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.topk)
+        np.testing.assert_array_equal(idx, di)
+        np.testing.assert_array_equal(val, dv)
+
+
+def test_pivot_bruteforce_prefill_groups():
+    """Tiny causal prefill with groups of 4 (the last one short): proxy, scan and
+    refine written out with plain loops and exact rationals."""
+    import torch
+    rng = np.random.default_rng(9)
+    L, H, d, G, kc, k = 23, 2, 4, 4, 6, 3
+    keys = rng.integers(-3, 4, size=(1, L, d)).astype(np.float64)
+    q = rng.integers(-3, 4, size=(L, H, d)).astype(np.float64) / 4
+    w = rng.integers(1, 4, size=(L, H)).astype(np.float64) / 2
+    q_seq, q_len = np.zeros(L, np.int64), np.arange(1, L + 1)
+    cand, idx, _ = O.pivot_indexer(q, w, keys, q_seq, q_len, G, kc, k)
+    for t in range(L):
+        grp = range((t // G) * G, min((t // G) * G + G, L))
+        plen = max(int(q_len[u]) for u in grp)
+        qp = [[float(torch.tensor(sum(q[u, g, c] for u in grp), dtype=torch.float32).to(torch.bfloat16))
+               for c in range(d)] for g in range(H)]
+        wp = [sum(Fraction(float(w[u, g])) for u in grp) for g in range(H)]
+        S = [sum(wp[g] * max(Fraction(0), sum(Fraction(qp[g][c]) * Fraction(float(keys[0, s, c])) for c in range(d)))
+                 for g in range(H)) for s in range(plen)]
+        C = sorted(s for s in range(plen) if sum(1 for r in range(plen) if S[r] > S[s] or (S[r] == S[s] and r < s)) < kc)
+        assert cand[t][:len(C)].tolist() == C and all(v == -1 for v in cand[t][len(C):])
+        p = int(q_len[t])
+        Cp = [s for s in C if s < p]
+        D = {s: sum(Fraction(float(w[t, g])) * max(Fraction(0), sum(Fraction(float(q[t, g, c])) * Fraction(float(keys[0, s, c]))
+                                                                    for c in range(d))) for g in range(H)) for s in Cp}
+        F = sorted(s for s in Cp if sum(1 for r in Cp if D[r] > D[s] or (D[r] == D[s] and r < s)) < k)
+        assert idx[t].tolist() == F + [-1] * (k - len(F))
