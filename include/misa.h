@@ -81,6 +81,7 @@ extern "C" {
 #define MISA_OP_HIER_INDEXER 6
 #define MISA_OP_BLOCK_FILTER 7     /* kc argument = m, the complete blocks kept */
 #define MISA_OP_BLOCK_INDEXER 8    /* kc argument = m */
+#define MISA_OP_PIVOT_INDEXER 9    /* B argument = G, the group size */
 
 /* Library version, major * 10000 + minor * 100 + patch. */
 MISA_API int32_t misa_version(void);
@@ -273,6 +274,29 @@ MISA_API int32_t misa_block_indexer(const void* q, const float* w, const void* k
                                     int64_t nseq, int64_t Lmax, int32_t B, int32_t h, int32_t m, int32_t topk,
                                     int32_t* heads, int32_t* blocks, int32_t* idx, float* score, void* ws,
                                     size_t ws_bytes, void* stream);
+
+/*
+ * Proxy-query shared scan with per-query refinement (PIVOT-Refine;
+ * thelatestinai.com paper cards, the PIVOT abstract). The queries are taken in
+ * groups of G consecutive ones (the last group may be shorter), and every query
+ * of a group must belong to the sequence of its first query (prefill: G
+ * consecutive positions; decode: the positions of one multi-token step). Each
+ * group is folded into a proxy query, the sum of its per-head queries rounded to
+ * bf16 (nearest, ties to even) with the sum of their head weights (the page
+ * leaves the fold open; the sum is the mean up to a positive factor, which
+ * changes no ranking). The proxy scans its group's longest prefix once with the
+ * dense indexer (all H heads) and keeps kc candidates (ties to the lower token
+ * id); each query then re-ranks those candidates with its own dense indexer as
+ * misa_hier_rerank does (ids at or beyond its own prefix are skipped).
+ *   cand   int32 [T][kc] out, may be NULL: the candidates of each query's group
+ *   idx / score as misa_hier_rerank (dense scores)
+ *   ws: misa_workspace_bytes(MISA_OP_PIVOT_INDEXER, T, H, Lmax, G, topk, kc) (sized for d up to 256)
+ * Errors: as misa_hier_rerank, and MISA_ERR_ARG for G < 1 or kc outside [topk, Lmax].
+ */
+MISA_API int32_t misa_pivot_indexer(const void* q, const float* w, const void* k, const int32_t* q_seq,
+                                    const int32_t* q_len, int64_t T, int32_t H, int32_t d, int64_t nseq, int64_t Lmax,
+                                    int32_t G, int32_t kc, int32_t topk, int32_t* cand, int32_t* idx, float* score,
+                                    void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Full score rows of the routed scoring step (a diagnostic of step 3 above):

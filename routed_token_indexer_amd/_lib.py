@@ -29,6 +29,7 @@ OP_INDEXER = 5
 OP_HIER_INDEXER = 6
 OP_BLOCK_FILTER = 7
 OP_BLOCK_INDEXER = 8
+OP_PIVOT_INDEXER = 9
 
 KERNEL_SCORE = 1
 KERNEL_TOPK = 2
@@ -65,6 +66,8 @@ _SIGNATURES = {
                                  _P, _SZ, _P]),
     "misa_block_indexer": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I64, _I64, _I32, _I32, _I32, _I32, _P,
                                   _P, _P, _P, _P, _SZ, _P]),
+    "misa_pivot_indexer": (_I32, [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I64, _I64, _I32, _I32, _I32, _P, _P, _P,
+                                  _P, _SZ, _P]),
     "misa_timing_begin": (_I32, [_I32, _I32]),
     "misa_timing_end": (_I32, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)]),
 }
@@ -279,6 +282,21 @@ def block_indexer(q, w, k, kbar, q_seq, q_len, B: int, h: int, m: int, topk: int
                                                           _ptr(q_len), T, H, d, nseq, L, B, h, m, topk, _ptr(heads),
                                                           _ptr(blocks), _ptr(idx), _ptr(score), _ptr(ws), ws.numel(),
                                                           _stream(stream)))
+    return idx, score
+
+
+def pivot_indexer(q, w, k, q_seq, q_len, G: int, kc: int, topk: int, cand=None, idx=None, score=None,
+                  want_score=True, ws=None, stream=None):
+    """PIVOT-Refine over groups of G consecutive queries: the group proxy's dense
+    scan keeps kc candidates, each query re-ranks them densely to its top-k."""
+    _req(q, torch.bfloat16, "q", 3)
+    T, H, d = q.shape
+    nseq, L, _ = k.shape
+    idx, score = _outs(T, topk, q.device, idx, score, want_score)
+    ws = _workspace(ws, workspace_bytes(OP_PIVOT_INDEXER, T, H, L, G, topk, kc), q.device)
+    _check("misa_pivot_indexer", lib().misa_pivot_indexer(_ptr(q), _ptr(w), _ptr(k), _ptr(q_seq), _ptr(q_len), T, H,
+                                                          d, nseq, L, G, kc, topk, _ptr(cand), _ptr(idx), _ptr(score),
+                                                          _ptr(ws), ws.numel(), _stream(stream)))
     return idx, score
 
 

@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmisa.so")
-SOURCES = ["abi.hip", "pool.hip", "route.hip", "score.hip", "topk.hip", "topk_split.hip", "block.hip"]
+SOURCES = ["abi.hip", "pool.hip", "route.hip", "score.hip", "topk.hip", "topk_split.hip", "block.hip", "pivot.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

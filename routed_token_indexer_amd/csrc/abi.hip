@@ -71,6 +71,13 @@ size_t block_filter_ws_bytes(int64_t T, int64_t Lmax, int32_t B) {
   return round_up((size_t)T * (size_t)(Lmax / B) * sizeof(float)) + round_up((size_t)T * sizeof(int32_t));
 }
 
+// Workspace of the proxy queries (sized for d up to 256), weights, group
+// sequences and prefixes, and the groups' candidate rows.
+size_t pivot_head_bytes(int64_t ng, int32_t H, int32_t kc) {
+  return round_up((size_t)ng * H * 256 * 2) + round_up((size_t)ng * H * 4) + 2 * round_up((size_t)ng * 4) +
+         round_up((size_t)ng * (size_t)kc * 4);
+}
+
 // Workspace of scoring + selection over rows of at most max_len: the fp32 score
 // rows, then (for few long rows) the split top-k's state.
 size_t select_ws_bytes(int64_t T, int64_t max_len) {
@@ -191,6 +198,12 @@ size_t misa_workspace_bytes(int32_t op, int64_t T, int32_t H, int64_t Lmax, int3
       const size_t fs = block_filter_ws_bytes(T, Lmax, B), ss = select_ws_bytes(T, nc);
       return misa_workspace_bytes(MISA_OP_ROUTE, T, H, Lmax, B, 0, 0) + round_up((size_t)T * H * 4) +
              round_up((size_t)T * (size_t)kc * 4) + round_up((size_t)T * (size_t)nc * 4) + (fs > ss ? fs : ss);
+    }
+    case MISA_OP_PIVOT_INDEXER: {
+      if (B < 1 || H < 1 || kc < 1) return 0;
+      const int64_t ng = (T + B - 1) / B;
+      const size_t sa = select_ws_bytes(ng, Lmax), sb = select_ws_bytes(T, kc);
+      return pivot_head_bytes(ng, H, kc) + round_up((size_t)T * (size_t)kc * 4) + (sa > sb ? sa : sb);
     }
     case MISA_OP_INDEXER:
     case MISA_OP_HIER_INDEXER: {
@@ -688,6 +701,62 @@ int32_t misa_block_indexer(const void* q, const float* w, const void* k, const f
   rc = block_filter_run(fn, q, w, kbar, hd, h, q_seq, q_len, T, H, d, nseq, Lmax, B, m, bl, cd, p, st);
   if (rc) return rc;
   return score_and_select(fn, q, w, k, hd, h, cd, kc, q_seq, q_len, T, H, d, nseq, Lmax, topk, idx, score,
+                          reinterpret_cast<float*>(p), kc, st);
+}
+
+int32_t misa_pivot_indexer(const void* q, const float* w, const void* k, const int32_t* q_seq, const int32_t* q_len,
+                           int64_t T, int32_t H, int32_t d, int64_t nseq, int64_t Lmax, int32_t G, int32_t kc,
+                           int32_t topk, int32_t* cand, int32_t* idx, float* score, void* ws, size_t ws_bytes,
+                           void* stream) {
+  const char* fn = "misa_pivot_indexer";
+  int32_t rc = check_common(fn, q, w, k, q_seq, q_len, T, H, d, nseq, Lmax);
+  if (rc) return rc;
+  if (G < 1) return fail(MISA_ERR_ARG, "%s: G = %d < 1", fn, G);
+  if (topk < 1) return fail(MISA_ERR_ARG, "%s: topk = %d < 1", fn, topk);
+  if (kc < topk || kc > Lmax) return fail(MISA_ERR_ARG, "%s: kc = %d not in [topk, Lmax]", fn, kc);
+  if (T == 0) return ok();
+  rc = check_outputs(fn, topk, idx, score);
+  if (rc) return rc;
+  if (!aligned(cand, 4)) return fail(MISA_ERR_ALIGN, "%s: cand must be 4-byte aligned", fn);
+  const int64_t ng = (T + G - 1) / G;
+  if (ng * (int64_t)H * (d / 8) >= (int64_t(1) << 38) || T * (int64_t)kc >= (int64_t(1) << 38))
+    return fail(MISA_ERR_ARG, "%s: grid too large", fn);
+  rc = check_ws(fn, ws, ws_bytes, misa_workspace_bytes(MISA_OP_PIVOT_INDEXER, T, H, Lmax, G, topk, kc));
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  char* p = static_cast<char*>(ws);
+  misa::PivotArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.w = w;
+  a.q_seq = q_seq;
+  a.q_len = q_len;
+  a.T = T;
+  a.H = H;
+  a.d = d;
+  a.G = G;
+  a.ng = ng;
+  a.qp = reinterpret_cast<uint16_t*>(p);
+  p += round_up((size_t)ng * H * 256 * 2);
+  a.wp = reinterpret_cast<float*>(p);
+  p += round_up((size_t)ng * H * 4);
+  a.gseq = reinterpret_cast<int32_t*>(p);
+  p += round_up((size_t)ng * 4);
+  a.glen = reinterpret_cast<int32_t*>(p);
+  p += round_up((size_t)ng * 4);
+  int32_t* gcand = reinterpret_cast<int32_t*>(p);
+  p += round_up((size_t)ng * (size_t)kc * 4);
+  int32_t* cd = cand ? cand : reinterpret_cast<int32_t*>(p);
+  p += round_up((size_t)T * (size_t)kc * 4);
+  hipError_t e = misa::launch_pivot_proxy(a, st);
+  if (e != hipSuccess) return hip_status(e, fn);
+  // the proxies' dense scan of their groups' longest prefixes keeps kc candidates
+  rc = score_and_select(fn, a.qp, a.wp, k, nullptr, H, nullptr, 0, a.gseq, a.glen, ng, H, d, nseq, Lmax, kc, gcand,
+                        nullptr, reinterpret_cast<float*>(p), Lmax, st);
+  if (rc) return rc;
+  e = misa::launch_pivot_broadcast(gcand, cd, T, G, kc, st);
+  if (e != hipSuccess) return hip_status(e, fn);
+  // each query re-ranks its group's candidates with its own dense indexer
+  return score_and_select(fn, q, w, k, nullptr, H, cd, kc, q_seq, q_len, T, H, d, nseq, Lmax, topk, idx, score,
                           reinterpret_cast<float*>(p), kc, st);
 }
 

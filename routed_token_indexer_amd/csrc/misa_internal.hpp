@@ -169,6 +169,27 @@ hipError_t launch_block_expand(const BlockArgs& a, const int32_t* blocks, int m,
 bool block_select_fused(const BlockArgs& a);
 hipError_t launch_block_select(const BlockArgs& a, int m, int32_t* blocks, int32_t* cand, int kc, hipStream_t st);
 
+// Proxy queries of groups of G consecutive queries (sum of the group's queries,
+// rounded to bf16; sum of their weights; the first query's sequence; the longest prefix).
+struct PivotArgs {
+  const uint16_t* q;        // bf16 [T][H][d]
+  const float* w;           // fp32 [T][H]
+  const int32_t* q_seq;
+  const int32_t* q_len;
+  int64_t T;
+  int H;
+  int d;
+  int G;
+  int64_t ng;               // ceil(T / G)
+  uint16_t* qp;             // bf16 [ng][H][d]
+  float* wp;                // fp32 [ng][H]
+  int32_t* gseq;            // [ng]
+  int32_t* glen;            // [ng]
+};
+hipError_t launch_pivot_proxy(const PivotArgs& a, hipStream_t st);
+// cand[t][:] = gcand[t / G][:] for t < T
+hipError_t launch_pivot_broadcast(const int32_t* gcand, int32_t* cand, int64_t T, int G, int kc, hipStream_t st);
+
 // Event timing of one internal kernel class (measurement aid).
 enum KernelId { KID_NONE = 0, KID_SCORE = 1, KID_TOPK = 2, KID_ROUTE = 3, KID_POOL = 4, KID_GATHER_SCORE = 5 };
 void timing_before(int kid, hipStream_t st);

@@ -171,6 +171,18 @@ def test_block_filter_checks(L):
                                 FAKE, None, FAKE, 1 << 30, None) == -1     # m
 
 
+def test_pivot_checks(L):
+    from routed_token_indexer_amd import _lib as B
+    a = lambda G, kc, topk, T=4: [FAKE, FAKE, FAKE, FAKE, FAKE, T, 64, 128, 4, 4096, G, kc, topk, None, FAKE, None,
+                                  FAKE, 1 << 30, None]
+    assert L.misa_pivot_indexer(*a(0, 512, 64)) == -1
+    assert L.misa_pivot_indexer(*a(4, 32, 64)) == -1        # kc < topk
+    assert L.misa_pivot_indexer(*a(4, 5000, 64)) == -1      # kc > Lmax
+    assert L.misa_pivot_indexer(*a(4, 512, 0)) == -1
+    assert L.misa_pivot_indexer(*a(4, 512, 64, T=0)) == 0
+    assert B.workspace_bytes(B.OP_PIVOT_INDEXER, 16, 64, 4096, 4, 64, 512) > 16 * 512 * 4
+
+
 def test_empty_batch_is_a_noop(L):
     # T = 0: valid, nothing enqueued, no pointer touched
     assert L.misa_score_topk(None, None, None, None, 8, None, None, 0, 64, 128, 4, 4096, 64, None, None, None, 0,

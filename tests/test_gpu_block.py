@@ -14,7 +14,7 @@ from oracle import misa_oracle as O
 from routed_token_indexer_amd import _lib as M
 from routed_token_indexer_amd.workloads import make_inputs
 
-from parity import SCORE_RTOL, check_router, upload
+from parity import SCORE_RTOL, check_fine, check_router, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -82,29 +82,6 @@ def check_blocks(x, heads_t, t, blk_gpu, m, exact, label):
     far = diff[np.abs(b[diff] - tau) > BLOCK_TIE_RTOL * mx]
     assert len(far) == 0, f"{label}: blocks {far[:8].tolist()} differ away from the threshold"
     return g
-
-
-def check_fine(idx_g, sc_g, idx_o, S_row, cand, k, exact, label):
-    """Fine stage of one query: the top-k among the candidate tokens."""
-    n = min(k, cand.shape[0])
-    g, o = np.asarray(idx_g), np.asarray(idx_o)
-    assert np.all(g[n:] == -1) and np.all(o[n:] == -1), f"{label}: padding"
-    gs, os_ = g[:n], o[:n]
-    assert np.all(np.diff(gs) > 0), f"{label}: not ascending"
-    assert set(gs.tolist()) <= set(cand.tolist()), f"{label}: token outside the retained blocks"
-    vals = np.asarray(sc_g, np.float64)[:n]
-    mx = max(float(np.max(np.abs(S_row))), 1e-30)
-    if exact:
-        np.testing.assert_array_equal(gs, os_, err_msg=label)
-        np.testing.assert_array_equal(vals, S_row[gs].astype(np.float32).astype(np.float64), err_msg=label)
-    else:
-        tau = float(np.min(S_row[os_])) if n else 0.0
-        diff = np.setxor1d(gs, os_)
-        bad = diff[np.abs(S_row[diff] - tau) > SCORE_RTOL * mx]
-        assert len(bad) == 0, f"{label}: tokens {bad[:8].tolist()} differ away from the threshold"
-        assert np.max(np.abs(vals - S_row[gs]), initial=0.0) <= SCORE_RTOL * mx, label
-    assert np.all(np.asarray(sc_g)[n:] == 0.0), f"{label}: padded scores must be 0"
-    return len(np.intersect1d(gs, os_)), n
 
 
 @pytest.mark.parametrize("mode", MODES)
