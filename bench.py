@@ -309,6 +309,17 @@ def main():
             rows["block_indexer_us"] = timed(lambda i: M.block_indexer(q, w, ks[i % ncopy], kbars[i % ncopy], q_seq,
                                                                        q_len, B, h, m_blk, topk, idx=bidx,
                                                                        want_score=False, ws=ws_blk), n, 3) * 1e3
+        if T > c.nseq:
+            # several queries per sequence: the proxy-query shared scan over groups of
+            # consecutive queries (one multi-token step per sequence, or 16 prefill positions)
+            G_pv = 16 if prefill else T // c.nseq
+            kc_pv = min(L, (2 if prefill else 4) * topk)
+            pidx = torch.empty_like(idx)
+            ws_pv = ws(M.OP_PIVOT_INDEXER, B=G_pv, topk=topk, kc=kc_pv)
+            rows["pivot_us"] = timed(lambda i: M.pivot_indexer(q, w, ks[i % ncopy], q_seq, q_len, G_pv, kc_pv, topk,
+                                                               idx=pidx, want_score=False, ws=ws_pv),
+                                     3 if prefill else n, 1) * 1e3
+            out["pivot"] = {"G": G_pv, "kc": kc_pv}
         out["rows"] = {kk: round(v, 2) for kk, v in rows.items()}
         # recall of the routed selections against the dense indexer on the same inputs (no target)
         if not prefill:
@@ -326,6 +337,10 @@ def main():
                             ws=ws_blk)
             torch.cuda.synchronize()
             out["recall_vs_dense"][f"block_filter_m{m_blk}"] = round(rec(bidx.cpu().numpy()), 4)
+            if T > c.nseq:
+                M.pivot_indexer(q, w, ks[0], q_seq, q_len, G_pv, kc_pv, topk, idx=pidx, want_score=False, ws=ws_pv)
+                torch.cuda.synchronize()
+                out["recall_vs_dense"][f"pivot_G{G_pv}"] = round(rec(pidx.cpu().numpy()), 4)
 
     # ---- the CPU oracle on the host cores, on a bounded sample of the same workload
     if not args.no_cpu_baseline:
