@@ -116,3 +116,69 @@ def test_full_c2_prefill_sampled(mode):
     inner = np.where(idx[:, 1:] >= 0, np.diff(idx, axis=1) > 0, True)
     assert np.all(inner)
     assert np.all(idx.max(axis=1) < q_len)
+
+
+@pytest.mark.parametrize("mode", ["gauss", "grid"])
+@pytest.mark.parametrize("name", ["c1", "c4"])
+def test_full_block_indexer(name, mode):
+    """The block filter composed with routing at full size, in the launch
+    configuration bench.py times (m = 4k / B blocks kept): block sets and the
+    top-k among their tokens on every query."""
+    from parity import check_fine
+    x, dev = get(name, mode)
+    c = x.cfg
+    exact = mode == "grid"
+    m = 4 * c.topk // c.B
+    kbar = M.pool_keys(dev["k"], c.B)
+    heads = torch.empty((c.T, c.h), dtype=torch.int32, device="cuda")
+    blocks = torch.empty((c.T, m), dtype=torch.int32, device="cuda")
+    idx, sc = M.block_indexer(dev["q"], dev["w"], dev["k"], kbar, dev["q_seq"], dev["q_len"], c.B, c.h, m, c.topk,
+                              heads=heads, blocks=blocks)
+    torch.cuda.synchronize()
+    heads, blocks, idx, sc = heads.cpu().numpy(), blocks.cpu().numpy(), idx.cpu().numpy(), sc.cpu().numpy()
+    qs = list(range(c.T))
+    use = check_router(x, heads, qs, c.h, exact)
+    ob = O.block_filter(x.q, x.w, x.k, use, x.q_seq, x.q_len, c.B, m)
+    for t in qs:
+        g = blocks[t]
+        if not np.array_equal(g, ob[t]):
+            assert not exact, f"{name} t={t}: blocks differ"
+            b = O.block_scores(x.q[t], x.w[t], x.k[x.q_seq[t]], use[t], int(x.q_len[t]), c.B)
+            tau = float(np.min(b[ob[t][ob[t] >= 0]]))
+            diff = np.setxor1d(g[g >= 0], ob[t][ob[t] >= 0])
+            assert np.all(np.abs(b[diff] - tau) <= 1e-5 * float(np.max(np.abs(b)))), f"{name} t={t}"
+        p = int(x.q_len[t])
+        oi, _ = O.score_topk_in_blocks(x.q, x.w, x.k, use[t:t + 1], g[None], x.q_seq, x.q_len, c.B, c.topk,
+                                       queries=[t])
+        S_row = O.routed_scores(x.q[t], x.w[t], x.k[x.q_seq[t]], use[t], p)
+        check_fine(idx[t], sc[t], oi[0], S_row, O.block_candidates(g, p, c.B), c.topk, exact, f"{name} t={t}")
+
+
+@pytest.mark.parametrize("mode", ["gauss", "grid"])
+def test_full_c1m_pivot(mode):
+    """PIVOT-Refine on the full multi-token decode step (4 sequences x 4
+    positions over 32768 keys, G = 4, kc = 4k): every group's candidates and
+    every query's re-rank of them."""
+    from parity import check_fine
+    x, dev = get("c1m", mode)
+    c = x.cfg
+    exact = mode == "grid"
+    G, kc = c.T // c.nseq, 4 * c.topk
+    cand = torch.empty((c.T, kc), dtype=torch.int32, device="cuda")
+    idx, sc = M.pivot_indexer(dev["q"], dev["w"], dev["k"], dev["q_seq"], dev["q_len"], G, kc, c.topk, cand=cand)
+    torch.cuda.synchronize()
+    cand, idx, sc = cand.cpu().numpy(), idx.cpu().numpy(), sc.cpu().numpy()
+    qp, wp, gseq, glen = O.pivot_proxy(x.q, x.w, x.q_seq, x.q_len, G)
+    tally = OverlapTally()
+    for gi in range(c.T // G):
+        S = O.routed_scores(qp[gi], wp[gi], x.k[gseq[gi]], range(c.H), int(glen[gi]))
+        oc, _ = O.select_topk(S, kc)
+        tally.add(cand[gi * G], oc, S, kc, exact, label=f"group {gi}")
+    tally.check()
+    for t in range(c.T):
+        p = int(x.q_len[t])
+        cc = cand[t][(cand[t] >= 0) & (cand[t] < p)]
+        oi, _ = O.hier_rerank(x.q, x.w, x.k, np.where(cand[t] < p, cand[t], -1)[None], x.q_seq, x.q_len, c.topk,
+                              queries=[t])
+        S_row = O.routed_scores(x.q[t], x.w[t], x.k[x.q_seq[t]], range(c.H), p)
+        check_fine(idx[t], sc[t], oi[0], S_row, cc, c.topk, exact, f"t={t}")
