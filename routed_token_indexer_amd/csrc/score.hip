@@ -603,7 +603,8 @@ hipError_t launch_decode(ScoreArgs a, int64_t max_len, hipStream_t st) {
   if (a.chunk <= 0) {
     // about 512 workgroups (two per CU), at least 512 keys (two iterations) each: a
     // workgroup of one iteration spends most of its time before its first keys arrive
-    int64_t c = 512;
+    // (gathered candidate rows: at least 256 keys, their loads are not streamed)
+    int64_t c = GATHER ? 256 : 512;
     while (c < 16384 && c * 512 < max_len * a.T) c *= 2;
     a.chunk = (int)c;
   }
