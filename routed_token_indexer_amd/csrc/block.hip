@@ -8,9 +8,9 @@
 // Here the coarse score of complete block j of a query is the routed indexer
 // formula on the block's mean key,
 //     b_j = sum over the routed heads g (in the given order) of w_g * max(q_g . Kbar_j, 0),
-// the m best complete blocks are kept (ties to the lower block id, by the
-// ordinary top-k over the rows of b), and the partial last block is always
-// kept. The candidate list of a query is then the token ids of its retained
+// the m best complete blocks are kept (ties to the lower block id; by
+// block_select_kernel below, or by the ordinary top-k over the rows of b for
+// rows of more than 4096 blocks), and the partial last block is always kept. The candidate list of a query is then the token ids of its retained
 // blocks followed by those of its partial block, ascending, -1 padded; the
 // routed scoring and top-k of the fine stage run over that list in gather mode.
 //
@@ -27,7 +27,8 @@
 
 namespace misa {
 
-// the routed query rows of block_score_kernel, [h][d] bf16 (dynamic LDS)
+// dynamic LDS of block_score_kernel: the routed query rows [h][d] bf16, then
+// the per-head dots [h][64] fp32
 extern __shared__ __attribute__((aligned(16))) uint16_t block_q_lds[];
 
 namespace {
