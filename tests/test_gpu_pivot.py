@@ -84,3 +84,20 @@ def test_pivot_identities_with_dense(case, mode):
     assert torch.equal(pi, di) and torch.equal(ps, ds)
     fi, fs = M.pivot_indexer(dev["q"], dev["w"], dev["k"], dev["q_seq"], dev["q_len"], G, x.cfg.L, k)
     assert torch.equal(fi, di) and torch.equal(fs, ds)
+
+
+@pytest.mark.parametrize("d", [32, 64, 256])
+@pytest.mark.parametrize("H,G", [(8, 2), (40, 5)])
+def test_pivot_shapes(d, H, G):
+    """Other head dims, head counts and group sizes (a group size that does not
+    divide the batch), grid-exact candidates and selections."""
+    x = make_inputs("c1m", mode="grid", L=1500, T=20, nseq=4, H=H, d=d, topk=100)
+    dev = upload(x)
+    kc = 300
+    cand = torch.empty((x.cfg.T, kc), dtype=torch.int32, device="cuda")
+    idx, sc = M.pivot_indexer(dev["q"], dev["w"], dev["k"], dev["q_seq"], dev["q_len"], G, kc, 100, cand=cand)
+    # groups that straddle two sequences take their first query's sequence on both sides
+    oc, oi, ov = O.pivot_indexer(x.q, x.w, x.k, x.q_seq, x.q_len, G, kc, 100)
+    np.testing.assert_array_equal(cand.cpu().numpy(), oc)
+    np.testing.assert_array_equal(idx.cpu().numpy(), oi)
+    np.testing.assert_array_equal(sc.cpu().numpy(), ov.astype(np.float32))
