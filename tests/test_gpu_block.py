@@ -262,3 +262,24 @@ def test_block_selection_paths_agree(mode):
             label = f"B={B} {mode} t={t}"
             g = check_blocks(x, ho[t], t, b1[t], m, mode == "grid", label)
             np.testing.assert_array_equal(cand[t], expected_cand(g, int(x.q_len[t]), B, m), err_msg=label)
+
+
+@pytest.mark.parametrize("L,B,m", [(3001, 64, 8), (40001, 8, 300)])
+def test_block_all_equal_scores(L, B, m):
+    """Every key equal: every block scores the same, so the m lowest block ids
+    are kept (both selection paths), and every candidate token scores the same,
+    so the k lowest candidate ids are selected."""
+    x = make_inputs("c1", mode="grid", L=L, T=4, nseq=4, B=B, topk=200)
+    x.k[:] = x.k[:, :1, :]
+    x.k_bf16[:] = x.k_bf16[:, :1, :]
+    dev = upload(x)
+    kbar = M.pool_keys(dev["k"], B)
+    heads = torch.empty((4, x.cfg.h), dtype=torch.int32, device="cuda")
+    blocks = torch.empty((4, m), dtype=torch.int32, device="cuda")
+    idx, _ = M.block_indexer(dev["q"], dev["w"], dev["k"], kbar, dev["q_seq"], dev["q_len"], B, x.cfg.h, m, 200,
+                             heads=heads, blocks=blocks)
+    blocks, idx, heads = blocks.cpu().numpy(), idx.cpu().numpy(), heads.cpu().numpy()
+    for t in range(4):
+        assert blocks[t].tolist() == list(range(m))
+        cand = O.block_candidates(blocks[t], int(x.q_len[t]), B)
+        assert idx[t].tolist() == cand[:200].tolist()
