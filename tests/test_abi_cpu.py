@@ -193,3 +193,25 @@ def test_empty_batch_is_a_noop(L):
 def test_timing_api_arguments(L):
     assert L.misa_timing_begin(9, 10) == -1
     assert L.misa_timing_begin(1, 0) == -1
+
+
+def test_product_path_never_touches_the_oracle():
+    """The package imports nothing from oracle/ (there is no CPU fallback); only
+    bench.py's cpu_baseline leg and the smoke check may."""
+    import ast
+    pkg = os.path.join(ROOT, "routed_token_indexer_amd")
+    for name in os.listdir(pkg):
+        if name.endswith(".py"):
+            tree = ast.parse(open(os.path.join(pkg, name)).read())
+            for node in ast.walk(tree):
+                if isinstance(node, ast.Import):
+                    assert not any(a.name.split(".")[0] == "oracle" for a in node.names), name
+                if isinstance(node, ast.ImportFrom):
+                    assert (node.module or "").split(".")[0] != "oracle", name
+    tree = ast.parse(open(os.path.join(ROOT, "bench.py")).read())
+    for fn in ast.walk(tree):
+        if isinstance(fn, ast.FunctionDef) and fn.name != "cpu_baseline":
+            for node in ast.walk(fn):
+                if isinstance(node, ast.ImportFrom) and (node.module or "").startswith("oracle"):
+                    # only the cpu_baseline function itself may import it
+                    assert False, f"bench.py: {fn.name} imports the oracle"
