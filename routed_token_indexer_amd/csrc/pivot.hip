@@ -11,7 +11,7 @@
 // needs no division. The proxy scans the longest prefix of its group.
 //
 // pivot_proxy_kernel: one thread per (group, head, 8 dims) sums the group's
-// query pieces in query order in fp32; the group's first thread of each head
+// query pieces in query order in fp32 (eight pieces requested at a time); the group's first thread of each head
 // sums the weights, and thread 0 of the group writes its sequence (that of its
 // first query) and longest prefix. pivot_broadcast_kernel copies each group's
 // candidate row to its queries.
@@ -36,12 +36,22 @@ __global__ __launch_bounds__(256) void pivot_proxy_kernel(PivotArgs a) {
   const int64_t t0 = g * a.G;
   const int64_t t1 = t0 + a.G < a.T ? t0 + a.G : a.T;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int64_t t = t0; t < t1; ++t) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(a.q + (t * per + r) * 8);
+  // eight queries' pieces in flight at a time (clamped reads), added in query order
+  for (int64_t tb = t0; tb < t1; tb += 8) {
+    u32x4 v[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc[2 * e] += bf16_lo(v[e]);
-      acc[2 * e + 1] += bf16_hi(v[e]);
+    for (int j = 0; j < 8; ++j) {
+      const int64_t t = tb + j < t1 ? tb + j : t0;
+      v[j] = *reinterpret_cast<const u32x4*>(a.q + (t * per + r) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (tb + j >= t1) break;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += bf16_lo(v[j][e]);
+        acc[2 * e + 1] += bf16_hi(v[j][e]);
+      }
     }
   }
   u32x4 o;
@@ -62,12 +72,18 @@ __global__ __launch_bounds__(256) void pivot_proxy_kernel(PivotArgs a) {
   }
 }
 
+// one workgroup per (query, 1024 candidate slots): four slots per thread
 __global__ __launch_bounds__(256) void pivot_broadcast_kernel(const int32_t* __restrict__ gcand,
                                                               int32_t* __restrict__ cand, int64_t T, int G, int kc) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= T * kc) return;
-  const int64_t t = i / kc;
-  cand[i] = gcand[(t / G) * kc + i % kc];
+  const int64_t nchunk = (kc + 1023) / 1024;
+  const int64_t t = blockIdx.x / nchunk;
+  const int64_t src = (t / G) * kc, dst = t * kc;
+  const int i0 = (int)(blockIdx.x % nchunk) * 1024 + threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = i0 + 256 * j;
+    if (i < kc) cand[dst + i] = gcand[src + i];
+  }
 }
 
 }  // namespace
@@ -81,9 +97,8 @@ hipError_t launch_pivot_proxy(const PivotArgs& a, hipStream_t st) {
 
 hipError_t launch_pivot_broadcast(const int32_t* gcand, int32_t* cand, int64_t T, int G, int kc, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  const int64_t n = T * kc;
-  hipLaunchKernelGGL(pivot_broadcast_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, gcand, cand, T, G,
-                     kc);
+  const int64_t n = T * ((kc + 1023) / 1024);
+  hipLaunchKernelGGL(pivot_broadcast_kernel, dim3((unsigned)n), dim3(256), 0, st, gcand, cand, T, G, kc);
   return hipGetLastError();
 }
 
