@@ -23,18 +23,22 @@ Status of each function's pin (see tests/test_oracle_*.py):
   pool_keys, route, routed_scores, select_topk, score_topk, dsa_index_dense,
   hier_rerank, misa_indexer, misa_hier_indexer, block_filter,
   score_topk_in_blocks, block_indexer, bf16_round, pivot_proxy,
-  pivot_indexer: pinned (brute force, closed forms, invariants). The router's aggregation rule is a reading of the pages;
-  agreement with the authors' own (unpublished) router is "parity unpinned".
+  pivot_indexer: pinned (brute force, closed forms, invariants). count_macs
+  (the tally of the query-key multiply-adds the oracle performs): pinned to the
+  pages' cost model on regular and ragged prefixes. The router's aggregation
+  rule is a reading of the pages; agreement with the authors' own (unpublished)
+  router is "parity unpinned".
 """
 from __future__ import annotations
 
+from contextlib import contextmanager
 from fractions import Fraction
 
 import numpy as np
 
 __all__ = [
     "pool_keys", "router_values", "route", "routed_scores", "select_topk", "score_topk",
-    "dsa_index_dense", "hier_rerank", "misa_indexer", "misa_hier_indexer", "mac_count",
+    "dsa_index_dense", "hier_rerank", "misa_indexer", "misa_hier_indexer", "count_macs",
     "block_scores", "block_filter", "block_candidates", "score_topk_in_blocks", "block_indexer",
     "bf16_round", "pivot_proxy", "pivot_indexer",
 ]
@@ -42,6 +46,40 @@ __all__ = [
 
 def _f64(x):
     return np.asarray(x, dtype=np.float64)
+
+
+# ------------------------------------------------------------------ work tally
+# The pages state the cost of the method as a count of query-key products: the
+# dense indexer is O(H_I * L), MISA O(h * L + H_I * M) per query
+# ("Probleemstelling", "Methodologie: MISA"). Every query-key (or query-pooled
+# key) dot product the oracle evaluates goes through _dots, which can tally
+# the multiply-adds it performs, so that a test can hold the oracle's actual
+# work against that cost model.
+class MacTally:
+    def __init__(self):
+        self.macs = 0
+
+
+_TALLY = None
+
+
+def _dots(A, x):
+    """A @ x for rows A [n, d] and x [d] or [d, m]; tallies n * d * m multiply-adds."""
+    r = A @ x
+    if _TALLY is not None:
+        _TALLY.macs += int(A.shape[0]) * int(A.shape[1]) * (1 if x.ndim == 1 else int(x.shape[1]))
+    return r
+
+
+@contextmanager
+def count_macs():
+    """Within the block, tally the multiply-adds of every query-key dot product."""
+    global _TALLY
+    prev, _TALLY = _TALLY, MacTally()
+    try:
+        yield _TALLY
+    finally:
+        _TALLY = prev
 
 
 # ------------------------------------------------------------------ a1: pooling
@@ -91,7 +129,7 @@ def router_values(q_t, w_t, keys_seq, p: int, B: int):
     # block j = tokens [jB, min(jB + B, p)); n_j of them are visible
     n = np.array([min((j + 1) * B, p) - j * B for j in range(M)])
     blk_sum = np.stack([keys[j * B:j * B + n[j]].sum(axis=0) for j in range(M)])   # [M, d]
-    a_sum = blk_sum @ q_t.T                       # [M, H]: q_g . (sum of block j's keys)
+    a_sum = _dots(blk_sum, q_t.T)                 # [M, H]: q_g . (sum of block j's keys)
     a = a_sum / n[:, None]                        # q_g . Kbar_j
     r = w_t * np.maximum(a, 0.0).sum(axis=0)
     r_exact = []
@@ -145,7 +183,7 @@ def routed_scores(q_t, w_t, keys_seq, heads_t, p: int) -> np.ndarray:
     keys = _f64(keys_seq)[:p]
     S = np.zeros(p)
     for g in sorted(int(x) for x in heads_t):
-        S = S + w_t[g] * np.maximum(keys @ q_t[g], 0.0)
+        S = S + w_t[g] * np.maximum(_dots(keys, q_t[g]), 0.0)
     return S
 
 
@@ -226,7 +264,7 @@ def hier_rerank(q, w, k, cand, q_seq, q_len, topk: int, queries=None):
         keys = _f64(k[q_seq[t]])[c]
         S = np.zeros(len(c))
         for g in range(H):
-            S = S + w[t, g] * np.maximum(keys @ q[t, g], 0.0)
+            S = S + w[t, g] * np.maximum(_dots(keys, q[t, g]), 0.0)
         # rank candidates by (dense score desc, token id asc)
         order = np.lexsort((c, -S))[:min(topk, len(c))]
         sel = np.sort(order)                       # c ascending => slot order is token order
@@ -283,7 +321,7 @@ def block_scores(q_t, w_t, keys_seq, heads_t, p: int, B: int) -> np.ndarray:
     kbar = _f64(keys_seq)[:nb * B].reshape(nb, B, d).sum(axis=1) / B
     b = np.zeros(nb)
     for g in sorted(int(x) for x in heads_t):
-        b = b + w_t[g] * np.maximum(kbar @ q_t[g], 0.0)
+        b = b + w_t[g] * np.maximum(_dots(kbar, q_t[g]), 0.0)
     return b
 
 
@@ -404,9 +442,3 @@ def pivot_indexer(q, w, k, q_seq, q_len, G: int, kc: int, topk: int, queries=Non
     idx, val = hier_rerank(q, w, k, np.where(cand < np.asarray(q_len)[list(qs)][:, None], cand, -1),
                            q_seq, q_len, topk, queries=qs)
     return cand, idx, val
-
-
-def mac_count(q_len, H: int, h: int, d: int, B: int) -> int:
-    """Multiply-accumulates of MISA as the pages count them: O(h*L + H_I*M) per query
-    ("Methodologie: MISA"), i.e. d * (h * p + H * ceil(p / B)) summed over queries."""
-    return int(sum(d * (h * int(p) + H * (-(-int(p) // B))) for p in q_len))

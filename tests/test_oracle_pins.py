@@ -374,10 +374,51 @@ def test_grid_mode_exactness_bounds():
     assert np.all(units == np.round(units)) and np.abs(units).max() < 2 ** 24
 
 
-def test_mac_count_formula():
-    # O(h L + H M) per query: d * (h * p + H * ceil(p / B))
-    assert O.mac_count([5], 3, 1, 2, 2) == 2 * (1 * 5 + 3 * 3)
-    assert O.mac_count([32768] * 4, 64, 8, 128, 64) == 4 * 128 * (8 * 32768 + 64 * 512)
+def _cost_model(q_len, H, h, d, B):
+    """The pages' cost of MISA per query ("Methodologie: MISA"): h routed heads
+    times every visible token, plus H heads times the ceil(p / B) pooled blocks,
+    each a d-long dot product."""
+    return sum(d * (h * int(p) + H * (-(-int(p) // B))) for p in q_len)
+
+
+def _ragged_inputs():
+    """One sequence of 130 keys, queries at prefixes that start, end, fill and
+    straddle blocks of 32 (partial blocks of 1, 31 and 2 tokens, none at 32 / 64)."""
+    rng = np.random.default_rng(5)
+    q_len = np.array([1, 2, 31, 32, 33, 64, 65, 130], np.int32)
+    T, H, d, L = len(q_len), 6, 8, 130
+    q = rng.standard_normal((T, H, d))
+    w = rng.random((T, H)) + 0.1
+    k = rng.standard_normal((1, L, d))
+    return q, w, k, np.zeros(T, np.int32), q_len, H, d
+
+
+def test_instrumented_macs_match_the_pages_cost_model():
+    """The oracle's actual query-key multiply-adds (tallied inside its dot
+    products) equal the pages' cost model: MISA d (h Sum p + H Sum ceil(p / B)),
+    dense DSA d H Sum p, MISA-dagger's fine stage d H per re-scored candidate.
+    Routing over floor instead of ceil blocks, scoring with every head, or a
+    re-rank over the whole prefix would each change the count."""
+    x = make_inputs("c0", mode="gauss")
+    c = x.cfg
+    cases = [(x.q, x.w, x.k, x.q_seq, x.q_len, c.H, c.d, c.B, c.h, c.topk)]
+    q, w, k, q_seq, q_len, H, d = _ragged_inputs()
+    cases.append((q, w, k, q_seq, q_len, H, d, 32, 2, 16))
+    for q, w, k, q_seq, q_len, H, d, B, h, topk in cases:
+        with O.count_macs() as tally:
+            O.misa_indexer(q, w, k, q_seq, q_len, B, h, topk)
+        assert tally.macs == _cost_model(q_len, H, h, d, B)
+        with O.count_macs() as tally:
+            O.dsa_index_dense(q, w, k, q_seq, q_len, topk)
+        assert tally.macs == d * H * int(np.sum(q_len))
+        kc = 2 * topk
+        with O.count_macs() as tally:
+            O.misa_hier_indexer(q, w, k, q_seq, q_len, B, h, kc, topk)
+        fine = d * H * sum(min(kc, int(p)) for p in q_len)
+        assert tally.macs == _cost_model(q_len, H, h, d, B) + fine
+    # nothing is tallied outside the block
+    O.misa_indexer(x.q, x.w, x.k, x.q_seq, x.q_len, c.B, c.h, c.topk)
+    assert O._TALLY is None
 
 
 # ------------------------------------------------------------------ block filter + routed heads
