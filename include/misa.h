@@ -311,14 +311,17 @@ MISA_API int32_t misa_debug_scores(const void* q, const float* w, const void* k,
  * Event timing of one internal kernel class, for measurement tools:
  * kernel 1 = token scoring over prefixes (routed or dense), 2 = top-k,
  * 3 = router, 4 = pooling, 5 = token scoring over candidate lists (re-rank).
- * After misa_timing_begin(kernel, capacity), each launch of that kernel (up to
- * `capacity` launches) is bracketed by hipEventRecord on its stream;
- * misa_timing_end waits for the recorded events and returns the summed
- * duration in ms and the number of launches timed. Process-wide state: not for
- * concurrent use from several threads.
+ * After misa_timing_begin(kernel, capacity, stream), each launch of that kernel
+ * class on `stream` (up to `capacity` launches) is bracketed by events on that
+ * stream; launches on other streams are not touched. misa_timing_end(stream,
+ * ...) waits for the recorded events, returns the summed duration in ms and
+ * the number of launches timed, and ends the timing of that stream. A second
+ * begin on a stream replaces the first. While no stream is timed the launch
+ * hooks cost one atomic load. Beginning or ending the timing of a stream while
+ * another thread launches on that same stream is not supported.
  */
-MISA_API int32_t misa_timing_begin(int32_t kernel, int32_t capacity);
-MISA_API int32_t misa_timing_end(float* total_ms, int32_t* launches);
+MISA_API int32_t misa_timing_begin(int32_t kernel, int32_t capacity, void* stream);
+MISA_API int32_t misa_timing_end(void* stream, float* total_ms, int32_t* launches);
 
 #ifdef __cplusplus
 }

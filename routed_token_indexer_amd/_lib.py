@@ -68,8 +68,8 @@ _SIGNATURES = {
                                   _P, _P, _P, _P, _SZ, _P]),
     "misa_pivot_indexer": (_I32, [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I64, _I64, _I32, _I32, _I32, _P, _P, _P,
                                   _P, _SZ, _P]),
-    "misa_timing_begin": (_I32, [_I32, _I32]),
-    "misa_timing_end": (_I32, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)]),
+    "misa_timing_begin": (_I32, [_I32, _I32, _P]),
+    "misa_timing_end": (_I32, [_P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)]),
 }
 
 
@@ -313,12 +313,13 @@ def debug_scores(q, w, k, heads, q_seq, q_len, out=None, stream=None):
     return out
 
 
-def timing_begin(kernel: int, capacity: int = 4096):
-    _check("misa_timing_begin", lib().misa_timing_begin(kernel, capacity))
+def timing_begin(kernel: int, capacity: int = 4096, stream=None):
+    """Time the launches of one kernel class on ``stream`` (default: the current stream)."""
+    _check("misa_timing_begin", lib().misa_timing_begin(kernel, capacity, _stream(stream)))
 
 
-def timing_end():
+def timing_end(stream=None):
     ms = ctypes.c_float(0.0)
     n = ctypes.c_int32(0)
-    _check("misa_timing_end", lib().misa_timing_end(ctypes.byref(ms), ctypes.byref(n)))
+    _check("misa_timing_end", lib().misa_timing_end(_stream(stream), ctypes.byref(ms), ctypes.byref(n)))
     return float(ms.value), int(n.value)

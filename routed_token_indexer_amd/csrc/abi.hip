@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -128,32 +129,60 @@ FusedLayout fused_layout(int64_t T, int H, int64_t Lmax, int B, int64_t kc, void
 }
 
 // ---------------------------------------------------------------- timing
-struct Timing {
-  std::mutex mu;
+// Event timing for measurement tools, registered per stream: only launches on
+// a stream whose timing was begun are bracketed, and the launch hooks of every
+// other call return after one atomic load while no stream is being timed.
+struct TimingEntry {
+  hipStream_t stream = nullptr;
   int kid = 0;
   int cap = 0;
   int n = 0;
   std::vector<hipEvent_t> ev;
 };
+struct Timing {
+  std::mutex mu;
+  std::atomic<int> active{0};   // entries registered (guarded writes, lock-free reads)
+  std::vector<TimingEntry> entries;
+};
 Timing g_timing;
+
+// The entry of stream st timing kernel class kid with room left (mu held).
+TimingEntry* timing_entry(int kid, hipStream_t st) {
+  for (TimingEntry& e : g_timing.entries)
+    if (e.stream == st) return (e.kid == kid && e.n < e.cap) ? &e : nullptr;
+  return nullptr;
+}
+
+void timing_release(TimingEntry& e) {
+  for (hipEvent_t ev : e.ev)
+    if (ev) (void)hipEventDestroy(ev);
+  e.ev.clear();
+}
 
 }  // namespace
 
 namespace misa {
 void timing_before(int kid, hipStream_t st) {
-  if (g_timing.kid != kid || g_timing.n >= g_timing.cap) return;
-  (void)hipEventRecord(g_timing.ev[2 * g_timing.n], st);
+  if (g_timing.active.load(std::memory_order_acquire) == 0) return;
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  if (TimingEntry* e = timing_entry(kid, st)) (void)hipEventRecord(e->ev[2 * e->n], st);
 }
 void timing_after(int kid, hipStream_t st) {
-  if (g_timing.kid != kid || g_timing.n >= g_timing.cap) return;
-  (void)hipEventRecord(g_timing.ev[2 * g_timing.n + 1], st);
-  ++g_timing.n;
+  if (g_timing.active.load(std::memory_order_acquire) == 0) return;
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  if (TimingEntry* e = timing_entry(kid, st)) {
+    (void)hipEventRecord(e->ev[2 * e->n + 1], st);
+    ++e->n;
+  }
 }
-bool timing_take(int kid, hipEvent_t& start, hipEvent_t& stop) {
-  if (g_timing.kid != kid || g_timing.n >= g_timing.cap) return false;
-  start = g_timing.ev[2 * g_timing.n];
-  stop = g_timing.ev[2 * g_timing.n + 1];
-  ++g_timing.n;
+bool timing_take(int kid, hipStream_t st, hipEvent_t& start, hipEvent_t& stop) {
+  if (g_timing.active.load(std::memory_order_acquire) == 0) return false;
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  TimingEntry* e = timing_entry(kid, st);
+  if (!e) return false;
+  start = e->ev[2 * e->n];
+  stop = e->ev[2 * e->n + 1];
+  ++e->n;
   return true;
 }
 }  // namespace misa
@@ -774,40 +803,59 @@ int32_t misa_debug_scores(const void* q, const float* w, const void* k, const in
                           scores, Lmax, (hipStream_t)stream);
 }
 
-int32_t misa_timing_begin(int32_t kernel, int32_t capacity) {
-  std::lock_guard<std::mutex> lk(g_timing.mu);
+int32_t misa_timing_begin(int32_t kernel, int32_t capacity, void* stream) {
   if (kernel < 1 || kernel > 5 || capacity < 1) return fail(MISA_ERR_ARG, "misa_timing_begin: bad kernel or capacity");
-  for (hipEvent_t ev : g_timing.ev) (void)hipEventDestroy(ev);
-  g_timing.ev.assign(2 * (size_t)capacity, nullptr);
-  for (auto& ev : g_timing.ev) {
+  hipStream_t st = (hipStream_t)stream;
+  TimingEntry fresh;
+  fresh.stream = st;
+  fresh.kid = kernel;
+  fresh.cap = capacity;
+  fresh.ev.assign(2 * (size_t)capacity, nullptr);
+  for (auto& ev : fresh.ev) {
     hipError_t e = hipEventCreate(&ev);
     if (e != hipSuccess) {
-      g_timing.kid = 0;
+      timing_release(fresh);
       return hip_status(e, "misa_timing_begin");
     }
   }
-  g_timing.cap = capacity;
-  g_timing.n = 0;
-  g_timing.kid = kernel;
+  std::lock_guard<std::mutex> lk(g_timing.mu);
+  for (auto it = g_timing.entries.begin(); it != g_timing.entries.end(); ++it)
+    if (it->stream == st) {   // a second begin on the stream replaces the first
+      timing_release(*it);
+      g_timing.entries.erase(it);
+      break;
+    }
+  g_timing.entries.push_back(std::move(fresh));
+  g_timing.active.store((int)g_timing.entries.size(), std::memory_order_release);
   return ok();
 }
 
-int32_t misa_timing_end(float* total_ms, int32_t* launches) {
-  std::lock_guard<std::mutex> lk(g_timing.mu);
-  const int n = g_timing.n;
-  g_timing.kid = 0;
+int32_t misa_timing_end(void* stream, float* total_ms, int32_t* launches) {
+  hipStream_t st = (hipStream_t)stream;
+  TimingEntry e;
+  {
+    std::lock_guard<std::mutex> lk(g_timing.mu);
+    auto it = g_timing.entries.begin();
+    while (it != g_timing.entries.end() && it->stream != st) ++it;
+    if (it == g_timing.entries.end()) return fail(MISA_ERR_ARG, "misa_timing_end: no timing begun on this stream");
+    e = std::move(*it);
+    g_timing.entries.erase(it);
+    g_timing.active.store((int)g_timing.entries.size(), std::memory_order_release);
+  }
   float tot = 0.f;
-  for (int i = 0; i < n; ++i) {
-    hipError_t e = hipEventSynchronize(g_timing.ev[2 * i + 1]);
-    if (e != hipSuccess) return hip_status(e, "misa_timing_end");
+  for (int i = 0; i < e.n; ++i) {
+    hipError_t r = hipEventSynchronize(e.ev[2 * i + 1]);
     float ms = 0.f;
-    e = hipEventElapsedTime(&ms, g_timing.ev[2 * i], g_timing.ev[2 * i + 1]);
-    if (e != hipSuccess) return hip_status(e, "misa_timing_end");
+    if (r == hipSuccess) r = hipEventElapsedTime(&ms, e.ev[2 * i], e.ev[2 * i + 1]);
+    if (r != hipSuccess) {
+      timing_release(e);
+      return hip_status(r, "misa_timing_end");
+    }
     tot += ms;
   }
+  timing_release(e);
   if (total_ms) *total_ms = tot;
-  if (launches) *launches = n;
-  g_timing.n = 0;
+  if (launches) *launches = e.n;
   return ok();
 }
 

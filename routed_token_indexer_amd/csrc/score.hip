@@ -591,7 +591,7 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a) {
 template <typename K, typename... Args>
 hipError_t launch_timed(int kid, K kernel, dim3 grid, dim3 block, hipStream_t st, Args... args) {
   hipEvent_t e0, e1;
-  if (timing_take(kid, e0, e1))
+  if (timing_take(kid, st, e0, e1))
     hipExtLaunchKernelGGL(kernel, grid, block, 0, st, e0, e1, 0, args...);
   else
     hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);

@@ -159,3 +159,43 @@ def check_fine(idx_g, sc_g, idx_o, S_row, cand, k, exact, label):
         assert np.max(np.abs(vals - S_row[gs]), initial=0.0) <= SCORE_RTOL * mx, label
     assert np.all(np.asarray(sc_g)[n:] == 0.0), f"{label}: padded scores must be 0"
     return len(np.intersect1d(gs, os_)), n
+
+
+def check_hier_end_to_end(x, queries, cand_gpu, idx_gpu, cand_orc, idx_orc, routed_rows, kc, k, exact, label=""):
+    """MISA-dagger end to end: the GPU's candidate sets and final sets against
+    the oracle's (row i <-> query queries[i]; routed_rows: the oracle's routed
+    score rows with the heads both sides used).
+
+    Grid inputs: both sets bit-equal. Gaussian inputs: the candidate sets obey
+    the top-k rule of OverlapTally on the routed scores; a final token that one
+    side has and the other lacks must either score (densely) within the
+    tolerance of the oracle's k-th dense score, or be a candidate only one side
+    kept (itself near the coarse threshold); and the final sets overlap by at
+    least OVERLAP_MIN."""
+    coarse = OverlapTally()
+    hit = tot = 0
+    for i, t in enumerate(queries):
+        coarse.add(cand_gpu[i], cand_orc[i], routed_rows[i], kc, exact, label=f"{label} coarse t={t}")
+        g = np.asarray(idx_gpu[i])
+        o = np.asarray(idx_orc[i])
+        if exact:
+            np.testing.assert_array_equal(g, o, err_msg=f"{label} fine t={t}")
+        else:
+            p = int(x.q_len[t])
+            dense = O.routed_scores(x.q[t], x.w[t], x.k[x.q_seq[t]], range(x.cfg.H), p)
+            n = min(k, p)
+            assert np.all(g[n:] == -1) and np.all(o[n:] == -1), f"{label} t={t}: padding"
+            mx = max(float(np.max(np.abs(dense))), 1e-30)
+            tau = float(np.min(dense[o[:n]])) if n else 0.0
+            cg, co = np.asarray(cand_gpu[i]), np.asarray(cand_orc[i])
+            swapped = np.setxor1d(cg[cg >= 0], co[co >= 0])
+            diff = np.setxor1d(g[:n], o[:n])
+            bad = [s for s in diff.tolist()
+                   if abs(dense[s] - tau) > SCORE_RTOL * mx and s not in set(swapped.tolist())]
+            assert not bad, f"{label} t={t}: final tokens {bad[:8]} differ away from both thresholds"
+        hit += len(np.intersect1d(g[g >= 0], o[o >= 0]))
+        tot += min(k, int(x.q_len[t]))
+    coarse.check()
+    ov = hit / max(tot, 1)
+    assert ov >= OVERLAP_MIN, f"{label}: final overlap {ov:.5f} < {OVERLAP_MIN}"
+    return ov

@@ -191,8 +191,11 @@ def test_empty_batch_is_a_noop(L):
 
 
 def test_timing_api_arguments(L):
-    assert L.misa_timing_begin(9, 10) == -1
-    assert L.misa_timing_begin(1, 0) == -1
+    assert L.misa_timing_begin(9, 10, None) == -1
+    assert L.misa_timing_begin(1, 0, None) == -1
+    # ending a stream that was never timed is an argument error, not a crash
+    assert L.misa_timing_end(None, None, None) == -1
+    assert b"no timing" in L.misa_last_error()
 
 
 def test_product_path_never_touches_the_oracle():

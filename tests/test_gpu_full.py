@@ -1,8 +1,11 @@
-"""GPU parity at the full workload sizes, in the library's default launch
-configuration (the one bench.py times): DeepSeek-V3.2-like decode (4 x 32768,
+"""GPU parity at the full workload sizes: DeepSeek-V3.2-like decode (4 x 32768,
 H=64), GLM-5-like decode (16 x 65536, H=32), hierarchical MISA at 128K (4 x
 131072, k'=8192 -> k=2048, plus dense DSA on the same inputs) on every query,
-and causal prefill at 16384 on a sample of rows the oracle computes one by one."""
+and causal prefill at 16384 on a sample of rows the oracle computes one by one.
+The whole-indexer entry points misa_indexer and misa_hier_indexer are called
+exactly as bench.py calls them (the fused decode pipeline) and checked against
+the oracle; the separate calls (route, score_topk, hier_rerank, dense) are
+checked too."""
 import numpy as np
 import pytest
 import torch
@@ -11,7 +14,8 @@ from oracle import misa_oracle as O
 from routed_token_indexer_amd import _lib as M
 from routed_token_indexer_amd.workloads import make_inputs
 
-from parity import OverlapTally, check_router, oracle_rows, selected_scores_ok, upload
+from parity import (OverlapTally, check_hier_end_to_end, check_router, oracle_rows, selected_scores_ok,
+                    upload)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -51,6 +55,67 @@ def test_full_decode_misa(name, mode):
         tally.add(idx[t], oi[t], rows[t], c.topk, exact, label=f"{name}/{mode} t={t}")
         selected_scores_ok(idx[t], sc[t], rows[t], c.topk, exact, label=f"{name}/{mode} t={t}")
     print(f"[full] {name} {mode}: MISA overlap {tally.check():.5f}")
+
+
+@pytest.mark.parametrize("mode", ["gauss", "grid"])
+@pytest.mark.parametrize("name", ["c1", "c3"])
+def test_full_fused_misa_indexer(name, mode):
+    """misa_indexer (route, routed scoring, top-k in one call) at full size, as
+    bench.py calls it: routed heads and selected tokens of every query against
+    the oracle, and the result bit-equal to the separate calls."""
+    x, dev = get(name, mode)
+    c = x.cfg
+    exact = mode == "grid"
+    kbar = M.pool_keys(dev["k"], c.B)
+    heads = torch.empty((c.T, c.h), dtype=torch.int32, device="cuda")
+    ws = torch.empty(M.workspace_bytes(M.OP_INDEXER, c.T, c.H, c.L, c.B, c.topk), dtype=torch.uint8, device="cuda")
+    idx, sc = M.indexer(dev["q"], dev["w"], dev["k"], kbar, dev["q_seq"], dev["q_len"], c.B, c.h, c.topk,
+                        heads=heads, ws=ws)
+    i2, s2 = M.score_topk(dev["q"], dev["w"], dev["k"], heads, dev["q_seq"], dev["q_len"], c.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, i2) and torch.equal(sc, s2)
+    qs = list(range(c.T))
+    use = check_router(x, heads.cpu().numpy(), qs, c.h, exact)
+    oi, _ = O.score_topk(x.q, x.w, x.k, use, x.q_seq, x.q_len, c.topk)
+    rows = oracle_rows(x, use, qs)
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    tally = OverlapTally()
+    for t in qs:
+        tally.add(idx[t], oi[t], rows[t], c.topk, exact, label=f"{name}/{mode} fused t={t}")
+        selected_scores_ok(idx[t], sc[t], rows[t], c.topk, exact, label=f"{name}/{mode} fused t={t}")
+    print(f"[full] {name} {mode}: misa_indexer overlap {tally.check():.5f}")
+
+
+@pytest.mark.parametrize("mode", ["gauss", "grid"])
+def test_full_c4_fused_hier_indexer(mode):
+    """misa_hier_indexer at 128K exactly as bench.py times it (k' = 8192,
+    k = 2048, routed heads and candidates returned): heads, candidate sets,
+    final sets and their dense scores of every query against the oracle."""
+    x, dev = get("c4", mode)
+    c = x.cfg
+    exact = mode == "grid"
+    kbar = M.pool_keys(dev["k"], c.B)
+    heads = torch.empty((c.T, c.h), dtype=torch.int32, device="cuda")
+    cand = torch.empty((c.T, c.kc), dtype=torch.int32, device="cuda")
+    idx = torch.empty((c.T, c.topk), dtype=torch.int32, device="cuda")
+    sc = torch.empty((c.T, c.topk), dtype=torch.float32, device="cuda")
+    ws = torch.empty(M.workspace_bytes(M.OP_HIER_INDEXER, c.T, c.H, c.L, c.B, c.topk, c.kc), dtype=torch.uint8,
+                     device="cuda")
+    M.hier_indexer(dev["q"], dev["w"], dev["k"], kbar, dev["q_seq"], dev["q_len"], c.B, c.h, c.kc, c.topk,
+                   heads=heads, cand=cand, idx=idx, score=sc, ws=ws)
+    torch.cuda.synchronize()
+    qs = list(range(c.T))
+    use = check_router(x, heads.cpu().numpy(), qs, c.h, exact)
+    cand, idx, sc = cand.cpu().numpy(), idx.cpu().numpy(), sc.cpu().numpy()
+    oc, _ = O.score_topk(x.q, x.w, x.k, use, x.q_seq, x.q_len, c.kc)
+    oi, _ = O.hier_rerank(x.q, x.w, x.k, oc, x.q_seq, x.q_len, c.topk)
+    routed = oracle_rows(x, use, qs)
+    ov = check_hier_end_to_end(x, qs, cand, idx, oc, oi, routed, c.kc, c.topk, exact, label=f"c4/{mode} fused")
+    # the returned scores are the dense scores of the returned tokens
+    for t in qs:
+        dense = O.routed_scores(x.q[t], x.w[t], x.k[x.q_seq[t]], range(c.H), int(x.q_len[t]))
+        selected_scores_ok(idx[t], sc[t], dense, c.topk, exact, label=f"c4/{mode} fused t={t}")
+    print(f"[full] c4 {mode}: misa_hier_indexer final overlap {ov:.5f}")
 
 
 @pytest.mark.parametrize("mode", ["gauss", "grid"])

@@ -9,8 +9,8 @@ from oracle import misa_oracle as O
 from routed_token_indexer_amd import _lib as M
 from routed_token_indexer_amd.workloads import make_inputs
 
-from parity import (OverlapTally, check_router, check_scores, oracle_rows, run_misa, selected_scores_ok,
-                    upload)
+from parity import (OverlapTally, check_hier_end_to_end, check_router, check_scores, oracle_rows, run_misa,
+                    selected_scores_ok, upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -26,6 +26,9 @@ CASES = {
     # rows above 32K scores: the multi-workgroup (split) top-k
     "c1x": ("c1", dict(L=40001, T=4, nseq=4, topk=1000)),
     "c4s": ("c4", dict(L=40000, T=4, nseq=4, kc=4096, topk=512)),
+    # rows of 65536 scores and more: four scores per thread in the split top-k's
+    # chunks (the configuration of the 128K workload)
+    "c4x": ("c4", dict(L=70001, T=4, nseq=4, kc=4096, topk=512)),
     # several consecutive decode positions per sequence: the shared key pass
     "c1m": ("c1m", dict(L=3001, topk=256)),
     # ... over rows of the split top-k
@@ -198,7 +201,7 @@ def test_dense(case, mode):
 
 
 @pytest.mark.parametrize("mode", MODES)
-@pytest.mark.parametrize("case", ["c0", "c1r", "c4r", "c4s"])
+@pytest.mark.parametrize("case", ["c0", "c1r", "c4r", "c4s", "c4x"])
 def test_hier_rerank(case, mode):
     """MISA†: the GPU re-rank of a candidate set against the oracle's re-rank of the
     same set, and the GPU's whole coarse-to-fine pass against the oracle's."""
@@ -223,14 +226,8 @@ def test_hier_rerank(case, mode):
     # end to end against the oracle's MISA† with the same heads
     _, oc, oi, _ = O.misa_hier_indexer(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h, kc, x.cfg.topk,
                                        queries=qs)
-    hits = sum(len(np.intersect1d(idx[t][idx[t] >= 0], oi[i][oi[i] >= 0])) for i, t in enumerate(qs))
-    tot = sum(min(x.cfg.topk, int(x.q_len[t])) for t in qs)
-    if exact:
-        for i, t in enumerate(qs):
-            np.testing.assert_array_equal(idx[t], oi[i])
-            np.testing.assert_array_equal(cand[t], oc[i])
-    else:
-        assert hits / tot >= 0.99
+    routed = oracle_rows(x, ho[qs], qs)
+    check_hier_end_to_end(x, qs, cand[qs], idx[qs], oc, oi, routed, kc, x.cfg.topk, exact, label=f"{case}/{mode}")
 
 
 # ------------------------------------------------------------------ invariants on the GPU
