@@ -20,11 +20,12 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - All array arguments are DEVICE pointers to caller-owned memory. The library
- *    never retains, frees or allocates them, and allocates no device memory of
- *    its own: scratch space is the caller's workspace `ws` of at least
+ *    never retains, frees or allocates them, and allocates no device memory at
+ *    run time: scratch space is the caller's workspace `ws` of at least
  *    misa_workspace_bytes(...) bytes (256-byte aligned). A workspace may be
  *    reused by later calls on the same stream; calls that overlap in time must
- *    not share one.
+ *    not share one. (misa_hier_indexer_noalloc instead uses a fixed device
+ *    array that the library holds per GPU; see there.)
  *  - `stream` is a hipStream_t passed as void* (NULL = the legacy default
  *    stream). Work is enqueued asynchronously on it; no call synchronizes.
  *  - Layouts (row-major, contiguous):
@@ -231,6 +232,34 @@ MISA_API int32_t misa_hier_indexer(const void* q, const float* w, const void* k,
                                    int64_t nseq, int64_t Lmax, int32_t B, int32_t h, int32_t kc, int32_t topk,
                                    int32_t* heads, int32_t* cand, int32_t* idx, float* score, void* ws,
                                    size_t ws_bytes, void* stream);
+
+/*
+ * misa_hier_indexer for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. It
+ * takes no workspace argument and allocates nothing; its scratch is a device
+ * array of MISA_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends. The caller still passes the inputs and outputs, with
+ * the meaning, layout and results of misa_hier_indexer (same kernels, bit for
+ * bit).
+ *  - Sizes whose workspace (misa_workspace_bytes(MISA_OP_HIER_INDEXER, ...))
+ *    exceeds MISA_SCRATCH_BYTES are refused with MISA_ERR_WORKSPACE before
+ *    anything is enqueued (decode batches fit: 4 x 128K tokens need about
+ *    7 MiB; a long causal prefill does not).
+ *  - The scratch belongs to the GPU of `stream` (NULL: the current device). Its
+ *    address is looked up once per device, on the first call there. Every call
+ *    on a GPU shares that GPU's array and leaves its contents behind; each call
+ *    clears, with its own kernels, the state it needs zeroed. Calls that overlap
+ *    in time on one GPU (other streams, other host threads) race on the array
+ *    and must be serialized by the caller.
+ * Errors: as misa_hier_indexer; MISA_ERR_HIP if the scratch address cannot be
+ * obtained.
+ */
+#define MISA_SCRATCH_BYTES (32u << 20)
+MISA_API int32_t misa_hier_indexer_noalloc(const void* q, const float* w, const void* k, const float* kbar,
+                                           const int32_t* q_seq, const int32_t* q_len, int64_t T, int32_t H,
+                                           int32_t d, int64_t nseq, int64_t Lmax, int32_t B, int32_t h, int32_t kc,
+                                           int32_t topk, int32_t* heads, int32_t* cand, int32_t* idx, float* score,
+                                           void* stream);
 
 /*
  * Block filter on the pooled keys, composed with head routing: the coarse stage

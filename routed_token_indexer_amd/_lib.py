@@ -68,6 +68,8 @@ _SIGNATURES = {
                                   _P, _P, _P, _P, _SZ, _P]),
     "misa_pivot_indexer": (_I32, [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I64, _I64, _I32, _I32, _I32, _P, _P, _P,
                                   _P, _SZ, _P]),
+    "misa_hier_indexer_noalloc": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I64, _I64, _I32, _I32, _I32,
+                                         _I32, _P, _P, _P, _P, _P]),
     "misa_timing_begin": (_I32, [_I32, _I32, _P]),
     "misa_timing_end": (_I32, [_P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)]),
 }
@@ -311,6 +313,21 @@ def debug_scores(q, w, k, heads, q_seq, q_len, out=None, stream=None):
     _check("misa_debug_scores", lib().misa_debug_scores(_ptr(q), _ptr(w), _ptr(k), _ptr(heads), h, _ptr(q_seq),
                                                         _ptr(q_len), T, H, d, nseq, L, _ptr(out), _stream(stream)))
     return out
+
+
+def hier_indexer_noalloc(q, w, k, kbar, q_seq, q_len, B: int, h: int, kc: int, topk: int, heads=None, cand=None,
+                         idx=None, score=None, want_score=True, stream=None):
+    """misa_hier_indexer with the library's own per-GPU scratch: no workspace,
+    nothing allocated by the library (outputs passed in are used as they are)."""
+    _req(q, torch.bfloat16, "q", 3)
+    T, H, d = q.shape
+    nseq, L, _ = k.shape
+    idx, score = _outs(T, topk, q.device, idx, score, want_score)
+    _check("misa_hier_indexer_noalloc",
+           lib().misa_hier_indexer_noalloc(_ptr(q), _ptr(w), _ptr(k), _ptr(kbar), _ptr(q_seq), _ptr(q_len), T, H, d,
+                                           nseq, L, B, h, kc, topk, _ptr(heads), _ptr(cand), _ptr(idx), _ptr(score),
+                                           _stream(stream)))
+    return idx, score
 
 
 def timing_begin(kernel: int, capacity: int = 4096, stream=None):

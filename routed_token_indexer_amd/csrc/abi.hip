@@ -187,6 +187,48 @@ bool timing_take(int kid, hipStream_t st, hipEvent_t& start, hipEvent_t& stop) {
 }
 }  // namespace misa
 
+namespace {
+
+// ---------------------------------------------------------------- library-owned scratch
+// Device memory of the allocation-free entry point: one array per GPU (each
+// device holds its own copy while the library is loaded). Host code never
+// passes the array's name to a kernel or a copy (on the host it only stands in
+// for the symbol); it uses the device address that hipGetSymbolAddress returns
+// for the GPU in question, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[MISA_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the scratch array on the device of stream st.
+int32_t scratch_of_stream(const char* fn, hipStream_t st, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(MISA_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  int dev = cur;
+  if (st) {
+    e = hipStreamGetDevice(st, &dev);
+    if (e != hipSuccess) return fail(MISA_ERR_HIP, "%s: hipStreamGetDevice: %s", fn, hipGetErrorString(e));
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(MISA_ERR_ARG, "%s: device %d out of range", fn, dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(MISA_ERR_HIP, "%s: hipSetDevice(%d): %s", fn, dev, hipGetErrorString(e));
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p)
+      return fail(MISA_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MISA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t misa_version(void) { return 100; }
@@ -615,6 +657,24 @@ int32_t misa_hier_indexer(const void* q, const float* w, const void* k, const fl
                           float* score, void* ws, size_t ws_bytes, void* stream) {
   return run_indexer("misa_hier_indexer", true, q, w, k, kbar, q_seq, q_len, T, H, d, nseq, Lmax, B, h, kc, topk,
                      heads, cand, idx, score, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int32_t misa_hier_indexer_noalloc(const void* q, const float* w, const void* k, const float* kbar,
+                                  const int32_t* q_seq, const int32_t* q_len, int64_t T, int32_t H, int32_t d,
+                                  int64_t nseq, int64_t Lmax, int32_t B, int32_t h, int32_t kc, int32_t topk,
+                                  int32_t* heads, int32_t* cand, int32_t* idx, float* score, void* stream) {
+  const char* fn = "misa_hier_indexer_noalloc";
+  const size_t need = misa_workspace_bytes(MISA_OP_HIER_INDEXER, T, H, Lmax, B, topk, kc);
+  if (need > (size_t)MISA_SCRATCH_BYTES)
+    return fail(MISA_ERR_WORKSPACE, "%s: these sizes need %zu bytes of scratch; the library holds %zu per GPU", fn,
+                need, (size_t)MISA_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (T > 0) {
+    const int32_t rc = scratch_of_stream(fn, (hipStream_t)stream, &ws);
+    if (rc) return rc;
+  }
+  return run_indexer(fn, true, q, w, k, kbar, q_seq, q_len, T, H, d, nseq, Lmax, B, h, kc, topk, heads, cand, idx,
+                     score, ws, (size_t)MISA_SCRATCH_BYTES, (hipStream_t)stream);
 }
 
 namespace {

@@ -198,6 +198,23 @@ def test_timing_api_arguments(L):
     assert b"no timing" in L.misa_last_error()
 
 
+def test_noalloc_refuses_sizes_beyond_its_scratch(L):
+    """The allocation-free MISA-dagger entry point checks its sizes against the
+    library's fixed per-GPU scratch before anything else (no device is needed):
+    a 128K causal prefill would need far more than it holds."""
+    need = L.misa_workspace_bytes(6, 16384, 64, 131072, 64, 2048, 8192)
+    assert need > (32 << 20)
+    rc = L.misa_hier_indexer_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16384, 64, 128, 1, 131072, 64, 8, 8192,
+                                     2048, None, None, FAKE, None, None)
+    assert rc == -3 and b"scratch" in L.misa_last_error()
+    # the decode shapes fit: 4 x 128K, and 16 x 64K with k' = 8192
+    assert L.misa_workspace_bytes(6, 4, 64, 131072, 128, 2048, 8192) <= (32 << 20)
+    assert L.misa_workspace_bytes(6, 16, 32, 65536, 64, 2048, 8192) <= (32 << 20)
+    # T = 0 needs no scratch and touches no device
+    assert L.misa_hier_indexer_noalloc(None, None, None, None, None, None, 0, 64, 128, 4, 4096, 64, 8, 512, 256,
+                                       None, None, None, None, None) == 0
+
+
 def test_product_path_never_touches_the_oracle():
     """The package imports nothing from oracle/ (there is no CPU fallback); only
     bench.py's cpu_baseline leg and the smoke check may."""
