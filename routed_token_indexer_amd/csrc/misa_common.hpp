@@ -68,6 +68,48 @@ __device__ __forceinline__ T wave_sum(T v) {
   return v;
 }
 
+// Hand-offs between workgroups of one launch. Stores and loads of device
+// (agent) scope carry the sc1 bit: a store is written through to the memory
+// side, where every XCD's loads with sc1 read it, instead of staying in the
+// writer's L2; read-modify-write atomics of agent scope are performed at the
+// memory side. A workgroup hands data over by storing it, waiting until its
+// stores have completed (wait_stores) and only then counting its arrival with
+// an atomic; a workgroup that has seen the count complete reads the data with
+// agent-scope loads issued after that observation.
+__device__ __forceinline__ void store_coherent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_coherent(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_coherent(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<uint32_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ uint32_t atomic_add_coherent(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until this thread's stores and atomics have completed (the sc1 stores
+// above: reached the memory side). The asm's memory clobber also keeps the
+// compiler from moving memory operations across it.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// The 4096-bin histograms that many workgroups add into with atomics keep bin
+// b at word hist_word(b): consecutive bins fall in different 128-byte lines
+// (bin b in line b % 128), so the adds of the many workgroups to the few busy
+// bins of a row spread over many lines instead of queueing on one or two.
+__device__ __forceinline__ int hist_word(int b) { return ((b & 127) << 5) | (b >> 7); }
+__device__ __forceinline__ int hist_bin(int word) { return ((word & 31) << 7) | (word >> 5); }
+
 // Visible prefix of query t clamped to [0, Lmax]; -1 for an invalid sequence id.
 __device__ __forceinline__ int query_prefix_len(const int32_t* q_seq, const int32_t* q_len, int64_t nseq,
                                                 int64_t Lmax, int64_t t) {

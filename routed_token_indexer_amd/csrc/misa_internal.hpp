@@ -25,7 +25,8 @@ struct ScoreArgs {
   float* out;               // [T][out_stride]
   int64_t out_stride;
   int chunk;                // keys per workgroup chunk
-  uint32_t* hist;           // optional [T][4096]: level-1 histogram of the written scores (decode kernel)
+  uint32_t* hist;           // optional [T][4096]: level-1 histogram of the written scores (decode
+                            // kernel; bin b at word hist_word(b))
   // fused decode pipeline: heads selected in the kernel from the router's partials
   const float* partial;     // [T][nchunk_r][H] or null (then heads come from `heads`)
   const float* xtail;       // [T][H]
@@ -101,7 +102,7 @@ int64_t topk_row_reg_max();
 // Split top-k for few long rows: several workgroups per row cooperate through
 // global memory (level-1 histogram, candidate list, per-chunk offsets).
 struct SplitTopkWs {
-  uint32_t* hist;      // [T][4096] level-1 histogram (zero on entry)
+  uint32_t* hist;      // [T][4096] level-1 histogram (zero on entry; bin b at word hist_word(b))
   uint32_t* hist2;     // [T][4096] key bits 8..19 of the level-1 threshold bin's keys (zero on entry)
   uint32_t* state;     // [T][8] threshold key and how many keys equal to it are kept
   uint32_t* counter;   // [T][4] candidate-list cursor, arrivals of the filter (zero on entry)

@@ -580,8 +580,8 @@ __global__ __launch_bounds__(256) void score_decode_kernel(ScoreArgs a) {
     uint32_t* gh = a.hist + t * 4096;
     for (int i = threadIdx.x; i < 2048; i += 256) {
       const uint32_t v = lh[i];
-      if (v & 0xffffu) atomicAdd(&gh[2 * i], v & 0xffffu);
-      if (v >> 16) atomicAdd(&gh[2 * i + 1], v >> 16);
+      if (v & 0xffffu) atomicAdd(&gh[hist_word(2 * i)], v & 0xffffu);
+      if (v >> 16) atomicAdd(&gh[hist_word(2 * i + 1)], v >> 16);
     }
   }
 }

@@ -41,22 +41,6 @@ enum { ST_THR = 0, ST_KREM = 1 };
 // counter[t][*] (zero on entry)
 enum { CT_CAND = 0, CT_DONE = 1 };
 
-__device__ __forceinline__ void store_coherent(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void store_coherent(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t load_coherent(const uint32_t* p) {
-  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t load_coherent(const uint64_t* p) {
-  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Waits until this thread's stores have completed (for the sc1 stores above:
-// reached memory).
-__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 __device__ __forceinline__ int64_t row_len_of(const TopkArgs& a, int64_t t, int& p) {
   p = query_prefix_len(a.q_seq, a.q_len, a.nseq, a.Lmax, t);
   if (p < 0) {
@@ -121,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void split_hist_kernel(TopkArgs a, SplitT
   __syncthreads();
   uint32_t* gh = w.hist + t * kBins;
   for (int i = tid; i < kBins; i += kThreads)
-    if (lh[i]) atomicAdd(&gh[i], lh[i]);
+    if (lh[i]) atomicAdd(&gh[hist_word(i)], lh[i]);
 }
 
 // Every chunk finds the row's threshold bin b1 from the finished histogram,
@@ -165,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void split_filter_kernel(TopkArgs a, Spli
 #pragma unroll
   for (int k = 0; k < kBins / kThreads; ++k) hv[k] = gh[tid + k * kThreads];
 #pragma unroll
-  for (int k = 0; k < kBins / kThreads; ++k) lh[tid + k * kThreads] = hv[k];
+  for (int k = 0; k < kBins / kThreads; ++k) lh[hist_bin(tid + k * kThreads)] = hv[k];
   __syncthreads();
   find_threshold(lh, kBins, (uint32_t)a.k, wsum, sh);
   const uint32_t b1 = sh[0], krem1 = sh[1], m_all = lh[b1];
@@ -529,7 +513,7 @@ __global__ __launch_bounds__(kThreads) void split_compact_kernel(TopkArgs a, Spl
     __syncthreads();
     uint32_t* gh = r.hist + t * kBins;
     for (int i = tid; i < kBins; i += kThreads)
-      if (lh[i]) atomicAdd(&gh[i], lh[i]);
+      if (lh[i]) atomicAdd(&gh[hist_word(i)], lh[i]);
   }
 }
 
