@@ -51,6 +51,7 @@ def parse():
     ap.add_argument("--no-subconfigs", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="skip the per-row timings")
+    ap.add_argument("--no-warm", action="store_true", help="skip the warm-cache figures")
     ap.add_argument("--eager", action="store_true",
                     help="time eager launches instead of HIP-graph replays of the step")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -342,7 +343,7 @@ def main():
             out["recall_vs_dense"] = rec
 
     # ---- the same step with one key-cache copy (warm: served partly from the MALL)
-    if not wl.prefill:
+    if not wl.prefill and not args.no_warm:
         warm = Workload(args.config, M, dev, warm=True)
         mw = measure(warm, args.steps, args.warmup)
         out["warm_cache"] = summary(warm, mw)
