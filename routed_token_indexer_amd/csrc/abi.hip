@@ -618,8 +618,14 @@ int32_t run_indexer(const char* fn, bool hier, const void* q, const float* w, co
     r.d = d;
     r.scores = f.rr_scores;
     r.hist = fine_split ? f.rw.hist : nullptr;   // level-1 histogram of the split fine stage
+    // rows of at most 8192 candidates: the fine stage runs inside the same
+    // launch, in the last workgroup of each row to finish its re-scoring
+    r.fine = !fine_split && kc <= 8192;
+    r.fidx = idx;
+    r.fscore = score;
+    r.ftopk = topk;
     e = misa::launch_topk_split_rescore(b, f.sw, r, st);
-    if (e == hipSuccess) {
+    if (e == hipSuccess && !r.fine) {
       // 4. MISA† fine stage: top-k of the candidates' dense scores
       misa::TopkArgs b2{};
       b2.scores = f.rr_scores;

@@ -96,6 +96,11 @@ struct TopkArgs {
   float* score;             // [T][k] or null
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
+// The register-resident select of row t by the calling workgroup (EPT * NT
+// slots at most). COH: the row was written earlier in the same launch by other
+// workgroups (device-coherent loads).
+template <int EPT, bool GATHER, int NT, bool MANY, bool COH>
+__device__ void topk_row_reg_row(const TopkArgs& a, int64_t t);
 // Longest row the register-resident single-workgroup top-k handles.
 int64_t topk_row_reg_max();
 
@@ -136,6 +141,12 @@ struct RescoreArgs {
   int d;
   float* scores;            // [T][kc] dense score of each candidate slot
   uint32_t* hist;           // [T][4096] level-1 histogram of those scores (zero on entry)
+  // fine stage in the same launch (rows of at most 8192 candidates): the last
+  // workgroup of a row to finish its re-scoring selects the row's final top-k
+  bool fine;
+  int32_t* fidx;            // [T][ftopk]
+  float* fscore;            // [T][ftopk] or null
+  int ftopk;
 };
 // filter + compact of the coarse pass (level-1 histogram already built), the
 // compact writing the candidate list (a.idx, k = kc) and its dense scores.

@@ -337,9 +337,13 @@ constexpr int kWinBits = 26;     // window of 2^26 key units: 8 octaves of posit
 constexpr int kBinShift = kWinBits - 12;
 constexpr int kCandCap = 512;    // keys of the threshold bin ranked in LDS
 
-template <int EPT, bool GATHER, int NT, bool MANY>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MANY ? 8 : NT / 256))) void topk_row_reg_kernel(
-    TopkArgs a) {
+}  // namespace
+
+// The register-resident select of row t (the body of topk_row_reg_kernel).
+// COH: the row (and its token ids) were written earlier in the same launch by
+// other workgroups, so they are read with device-coherent loads.
+template <int EPT, bool GATHER, int NT, bool MANY, bool COH>
+__device__ void topk_row_reg_row(const TopkArgs& a, int64_t t) {
   constexpr int NW = NT / 64;
   // the few-rows variants run the fallback in place; the many-rows (MANY) variants
   // mark the row for topk_fallback_kernel and keep their registers for the fast
@@ -354,7 +358,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MANY ? 8 : N
   uint32_t* const c_key = &rs.hist[0][0];          // after the level-1 scan
   uint32_t* const c_slot = &rs.hist[0][kCandCap];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t = (int64_t)a.T - 1 - blockIdx.x;   // causal batches: longest rows first
   int64_t n;
   int p;
   row_geometry(a, t, n, p);
@@ -377,8 +380,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MANY ? 8 : N
       for (int u = 0; u < U; ++u) {
         const int j = j0 + u * NT + tid;
         const int jc = j < nl ? j : 0;
-        v[u] = nl > 0 ? row[jc] : 0.f;
-        m[u] = (imap && nl > 0) ? imap[jc] : 0;
+        if constexpr (COH) {
+          v[u] = nl > 0 ? load_coherent(row + jc) : 0.f;
+          m[u] = (imap && nl > 0) ? (int32_t)load_coherent(reinterpret_cast<const uint32_t*>(imap) + jc) : 0;
+        } else {
+          v[u] = nl > 0 ? row[jc] : 0.f;
+          m[u] = (imap && nl > 0) ? imap[jc] : 0;
+        }
       }
       // all of them consumed from here on (an s_waitcnt the compiler sees: it
       // would otherwise also wait for the stores below before each use)
@@ -433,10 +441,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MANY ? 8 : N
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
     if (j >= nvs) continue;
-    // raw bits (keys in place below); non-temporal: every score is read once
-    u[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rview, (int)((uint32_t)base * 4u), (int)(256u * j),
-                                                          kNonTemporal);
-    if constexpr (kPrefetchIds) ids[j] = (int32_t)buffer_load_u32(iview, (uint32_t)base * 4u, 256u * j);
+    if constexpr (COH) {
+      // (every lane loads from a clamped slot; slots past the row are not used)
+      const int e = base + 64 * j < n ? base + 64 * j : 0;
+      u[j] = load_coherent(reinterpret_cast<const uint32_t*>(row) + e);
+      if constexpr (kPrefetchIds) ids[j] = (int32_t)load_coherent(reinterpret_cast<const uint32_t*>(imap) + e);
+    } else {
+      // raw bits (keys in place below); non-temporal: every score is read once
+      u[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rview, (int)((uint32_t)base * 4u), (int)(256u * j),
+                                                            kNonTemporal);
+      if constexpr (kPrefetchIds) ids[j] = (int32_t)buffer_load_u32(iview, (uint32_t)base * 4u, 256u * j);
+    }
   }
   if (tid == 0) s_m = 0u;
   radix_clear(rs);
@@ -625,6 +640,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MANY ? 8 : N
     general_select<EPT, NT>(u, fresh_nvalid, fresh_nvs, k, rs, wmin, wmax, wgt, weq, emit);
   else if (tid == 0)
     oi[0] = kFallbackMark;
+}
+
+// The fine stage of the fused MISA-dagger pass selects its rows inside the
+// compaction launch (rows of at most 8192 candidates, 1024 threads).
+template __device__ void topk_row_reg_row<8, true, 1024, false, true>(const TopkArgs& a, int64_t t);
+
+namespace {
+
+template <int EPT, bool GATHER, int NT, bool MANY>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MANY ? 8 : NT / 256))) void topk_row_reg_kernel(
+    TopkArgs a) {
+  topk_row_reg_row<EPT, GATHER, NT, MANY, false>(a, (int64_t)a.T - 1 - blockIdx.x);   // longest rows first
 }
 
 }  // namespace

@@ -39,7 +39,7 @@ constexpr int kCandReg = 8 * kThreads;       // candidates the last chunk holds 
 // state[t][*]: written by the last chunk of the filter launch
 enum { ST_THR = 0, ST_KREM = 1 };
 // counter[t][*] (zero on entry)
-enum { CT_CAND = 0, CT_DONE = 1 };
+enum { CT_CAND = 0, CT_DONE = 1, CT_FINE = 2 };
 
 __device__ __forceinline__ int64_t row_len_of(const TopkArgs& a, int64_t t, int& p) {
   p = query_prefix_len(a.q_seq, a.q_len, a.nseq, a.Lmax, t);
@@ -418,9 +418,13 @@ __global__ __launch_bounds__(kThreads) void split_compact_kernel(TopkArgs a, Spl
       int32_t id;
       float sc;
       out_entry(imap, p, e, score_key(row[e]), id, sc);
-      oi[e] = id;
+      if constexpr (RESCORE) {
+        store_coherent(reinterpret_cast<uint32_t*>(oi + e), (uint32_t)id);
+        s_tok[e - e0] = (int)e;
+      } else {
+        oi[e] = id;
+      }
       if (os) os[e] = sc;
-      if constexpr (RESCORE) s_tok[e - e0] = (int)e;
     }
     if constexpr (RESCORE) {
       off = (uint32_t)e0;
@@ -430,11 +434,13 @@ __global__ __launch_bounds__(kThreads) void split_compact_kernel(TopkArgs a, Spl
     }
     // padding [n, k), spread over the row's chunks
     for (int64_t j = n + (int64_t)c * kThreads + tid; j < a.k; j += (int64_t)w.nchunk * kThreads) {
-      oi[j] = -1;
       if (os) os[j] = 0.f;
       if constexpr (RESCORE) {
-        r.scores[t * (int64_t)a.k + j] = -INFINITY;
+        store_coherent(reinterpret_cast<uint32_t*>(oi + j), 0xffffffffu);
+        store_coherent(r.scores + t * (int64_t)a.k + j, -INFINITY);
         if (r.hist) atomicAdd(&lh[score_key(-INFINITY) >> 20], 1u);
+      } else {
+        oi[j] = -1;
       }
     }
     if constexpr (!RESCORE) return;
@@ -481,9 +487,13 @@ __global__ __launch_bounds__(kThreads) void split_compact_kernel(TopkArgs a, Spl
         int32_t id;
         float sc;
         out_entry(imap, p, base + 64 * j, u[j], id, sc);
-        oi[pos] = id;
+        if constexpr (RESCORE) {
+          store_coherent(reinterpret_cast<uint32_t*>(oi + pos), (uint32_t)id);
+          s_tok[pos - sel_before] = (int)(base + 64 * j);
+        } else {
+          oi[pos] = id;
+        }
         if (os) os[pos] = sc;
-        if constexpr (RESCORE) s_tok[pos - sel_before] = (int)(base + 64 * j);
       }
       eq_run += (uint32_t)__popcll(meq);
       sel_run += (uint32_t)__popcll(msel);
@@ -505,15 +515,37 @@ __global__ __launch_bounds__(kThreads) void split_compact_kernel(TopkArgs a, Spl
       load_key_tiles<D, 1>(kseq, b, (int)nsel, col, [&](int s) { return s_tok[s]; }, 0, tile);
       const float v = score_one_tile_lds<D, RT>(s_q, LDQ, s_w, tile, grp, col);
       if (grp == 0 && b + col < (int)nsel) {
-        rrow[off + b + col] = v;
+        store_coherent(rrow + off + b + col, v);
         if (r.hist) atomicAdd(&lh[score_key(v) >> 20], 1u);
       }
     }
-    if (!r.hist) return;
+    if (r.hist) {
+      __syncthreads();
+      uint32_t* gh = r.hist + t * kBins;
+      for (int i = tid; i < kBins; i += kThreads)
+        if (lh[i]) atomicAdd(&gh[hist_word(i)], lh[i]);
+    }
+    if (!r.fine) return;
+    // ---- the last workgroup of the row to finish selects the row's final top-k
+    // among its kc candidate slots: the candidate ids and dense scores of every
+    // chunk are stored (written through) before the chunk counts its arrival
+    __shared__ uint32_t s_fine_last;
+    wait_stores();
     __syncthreads();
-    uint32_t* gh = r.hist + t * kBins;
-    for (int i = tid; i < kBins; i += kThreads)
-      if (lh[i]) atomicAdd(&gh[hist_word(i)], lh[i]);
+    const uint32_t arrivals = n <= a.k ? (uint32_t)w.nchunk : (uint32_t)((n + CH - 1) / CH);
+    if (tid == 0)
+      s_fine_last = atomic_add_coherent(w.counter + t * 4 + CT_FINE, 1u) == arrivals - 1 ? 1u : 0u;
+    __syncthreads();
+    if (!s_fine_last) return;
+    TopkArgs f = a;
+    f.scores = r.scores;
+    f.stride = a.k;
+    f.imap = a.idx;
+    f.kc = a.k;
+    f.k = r.ftopk;
+    f.idx = r.fidx;
+    f.score = r.fscore;
+    topk_row_reg_row<8, true, kThreads, false, true>(f, t);
   }
 }
 
