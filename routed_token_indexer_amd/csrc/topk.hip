@@ -343,7 +343,7 @@ constexpr int kCandCap = 512;    // keys of the threshold bin ranked in LDS
 // COH: the row (and its token ids) were written earlier in the same launch by
 // other workgroups, so they are read with device-coherent loads.
 template <int EPT, bool GATHER, int NT, bool MANY, bool COH>
-__device__ void topk_row_reg_row(const TopkArgs& a, int64_t t) {
+__device__ __attribute__((always_inline)) void topk_row_reg_row(const TopkArgs& a, int64_t t) {
   constexpr int NW = NT / 64;
   // the few-rows variants run the fallback in place; the many-rows (MANY) variants
   // mark the row for topk_fallback_kernel and keep their registers for the fast
