@@ -94,6 +94,10 @@ struct TopkArgs {
   int k;
   int32_t* idx;             // [T][k]
   float* score;             // [T][k] or null
+  // rows of length n with len_lo < n <= len_hi only (the register select; a
+  // batch split over two launches by row length)
+  int64_t len_lo = -1;
+  int64_t len_hi = INT64_MAX;
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
 // The register-resident select of row t by the calling workgroup (EPT * NT

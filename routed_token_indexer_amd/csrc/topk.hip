@@ -361,6 +361,7 @@ __device__ __attribute__((always_inline)) void topk_row_reg_row(const TopkArgs& 
   int64_t n;
   int p;
   row_geometry(a, t, n, p);
+  if (n <= a.len_lo || n > a.len_hi) return;   // the other launch's row
   const int k = a.k;
   const float* row = a.scores + t * a.stride;
   int32_t* oi = a.idx + t * (int64_t)k;
@@ -696,7 +697,23 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t st) {
     }
     MISA_TOPK_MANY(16, 256)
     MISA_TOPK_MANY(32, 256)
-    MISA_TOPK_MANY(32, 512)
+    if (!done && max_len <= 32 * 512) {
+      // rows of up to 8192 scores on 256-thread workgroups (eight per CU), longer
+      // ones on 512-thread workgroups (four per CU): two launches over the batch,
+      // each leaving the other's rows alone. A causal batch has rows of every
+      // length, and its shorter half then runs twice as many rows per CU
+      TopkArgs s = a, l = a;
+      s.len_hi = 32 * 256;
+      l.len_lo = 32 * 256;
+      if (a.imap) {
+        hipLaunchKernelGGL((topk_row_reg_kernel<32, true, 256, true>), grid, dim3(256), 0, st, s);
+        hipLaunchKernelGGL((topk_row_reg_kernel<32, true, 512, true>), grid, dim3(512), 0, st, l);
+      } else {
+        hipLaunchKernelGGL((topk_row_reg_kernel<32, false, 256, true>), grid, dim3(256), 0, st, s);
+        hipLaunchKernelGGL((topk_row_reg_kernel<32, false, 512, true>), grid, dim3(512), 0, st, l);
+      }
+      done = true;
+    }
 #undef MISA_TOPK_MANY
     if (done) {
       const hipError_t e = hipGetLastError();

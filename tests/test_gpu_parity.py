@@ -386,6 +386,27 @@ def test_prefill_mixed_sign_many_rows(k):
     np.testing.assert_array_equal(rv, ov2.astype(np.float32))
 
 
+@pytest.mark.parametrize("k", [1, 500, 8192])
+def test_many_rows_split_by_length(k):
+    """300 queries over 9000 keys with prefixes spread from 1 to 9000: the
+    many-rows top-k selects the rows of up to 8192 scores and the longer ones in
+    two launches (256- and 512-thread workgroups); every row, routed and dense,
+    bit-exact in grid mode, including rows of at most k scores."""
+    x = make_inputs("c0", mode="grid", L=9000, T=300, q_len0=1, topk=k)
+    x.q_len = np.linspace(1, 9000, 300).round().astype(np.int32)
+    assert (x.q_len <= 8192).any() and (x.q_len > 8192).any()
+    dev = upload(x)
+    idx, sc = M.dsa_index_dense(dev["q"], dev["w"], dev["k"], dev["q_seq"], dev["q_len"], k)
+    oi, ov = O.dsa_index_dense(x.q, x.w, x.k, x.q_seq, x.q_len, k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), oi)
+    np.testing.assert_array_equal(sc.cpu().numpy(), ov.astype(np.float32))
+    ho, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, x.cfg.B, x.cfg.h)
+    _, _, ri, rv = run_misa(dev, x.cfg, heads=ho, topk=k)
+    oi2, ov2 = O.score_topk(x.q, x.w, x.k, ho, x.q_seq, x.q_len, k)
+    np.testing.assert_array_equal(ri, oi2)
+    np.testing.assert_array_equal(rv, ov2.astype(np.float32))
+
+
 @pytest.mark.parametrize("k", [1, 100, 699, 700, 900])
 def test_prefill_all_equal_scores(k):
     """Many rows of equal scores (zero keys): each row keeps its lowest token
