@@ -386,15 +386,27 @@ def test_prefill_mixed_sign_many_rows(k):
     np.testing.assert_array_equal(rv, ov2.astype(np.float32))
 
 
+def _split_layout(layout):
+    if layout == "spread":   # both classes, and the rows on either side of the boundary
+        q_len = np.linspace(1, 9000, 300).round().astype(np.int32)
+        q_len[100:104] = [8191, 8192, 8193, 8194]
+        return np.sort(q_len)
+    if layout == "all_long":   # the short-row launch finds nothing to do
+        return np.linspace(8193, 9000, 300).round().astype(np.int32)
+    return np.linspace(1, 8192, 300).round().astype(np.int32)   # all_short: nothing for the long-row launch
+
+
+@pytest.mark.parametrize("layout", ["spread", "all_long", "all_short"])
 @pytest.mark.parametrize("k", [1, 500, 8192])
-def test_many_rows_split_by_length(k):
-    """300 queries over 9000 keys with prefixes spread from 1 to 9000: the
-    many-rows top-k selects the rows of up to 8192 scores and the longer ones in
-    two launches (256- and 512-thread workgroups); every row, routed and dense,
-    bit-exact in grid mode, including rows of at most k scores."""
+def test_many_rows_split_by_length(k, layout):
+    """300 queries over 9000 keys: the many-rows top-k selects the rows of up to
+    8192 scores and the longer ones in two launches (256- and 512-thread
+    workgroups), each leaving the other's rows alone. Prefixes spread over both
+    classes (with rows of 8191..8194 scores at the boundary), or all in one of
+    them; every row, routed and dense, bit-exact in grid mode, including rows of
+    at most k scores."""
     x = make_inputs("c0", mode="grid", L=9000, T=300, q_len0=1, topk=k)
-    x.q_len = np.linspace(1, 9000, 300).round().astype(np.int32)
-    assert (x.q_len <= 8192).any() and (x.q_len > 8192).any()
+    x.q_len = _split_layout(layout)
     dev = upload(x)
     idx, sc = M.dsa_index_dense(dev["q"], dev["w"], dev["k"], dev["q_seq"], dev["q_len"], k)
     oi, ov = O.dsa_index_dense(x.q, x.w, x.k, x.q_seq, x.q_len, k)
