@@ -113,12 +113,9 @@ int64_t topk_row_reg_max();
 struct SplitTopkWs {
   uint32_t* hist;      // [T][4096] level-1 histogram (zero on entry; bin b at word hist_word(b))
   uint32_t* hist2;     // [T][4096] key bits 8..19 of the level-1 threshold bin's keys (zero on entry)
-  uint32_t* state;     // [T][8] threshold key and how many keys equal to it are kept
-  uint32_t* counter;   // [T][4] candidate-list cursor, arrivals of the filter (zero on entry)
+  uint32_t* state;     // [T][8] level-1 threshold bin, how many of its keys are kept, how many it holds
+  uint32_t* counter;   // [T][4] candidate-list cursor, arrivals of the MISA† fine stage (zero on entry)
   uint32_t* ndef;      // [T][nchunk] keys above the level-1 threshold bin in each chunk
-  uint32_t* selb;      // [T][nchunk] output offset of each chunk
-  uint32_t* eqb;       // [T][nchunk] keys equal to the threshold key before each chunk
-  uint32_t* seg;       // [T][nchunk][2] each chunk's run of the candidate list (start, count)
   uint32_t* cand;      // [T][cap][2] (key, index) of the level-1 threshold bin
   int64_t cap;
   int chunk;

@@ -11,16 +11,19 @@
 //   2. filter   each chunk reads the finished histogram, finds the threshold
 //               bin b1, counts its keys above b1, appends the keys of bin b1
 //               (key, index) to the row's candidate list and counts their next
-//               12 key bits into the row's level-2 histogram. The last chunk of
-//               the row to finish resolves the exact threshold key from the
-//               level-2 histogram (and, when its threshold bin is not kept
-//               whole, the low 8 bits of that bin's few candidates) and turns
-//               the per-chunk counts into per-chunk output offsets.
-//   3. compact  each chunk writes its kept indices in index order from its
-//               offset (ballots inside waves, counts across waves).
-// Within a launch, chunks hand data to the last one through device-coherent
-// stores (sc1: written through to memory, which every XCD's loads with sc1
-// see) completed before an atomic arrival count; the L2 write-back fence that a
+//               12 key bits into the row's level-2 histogram.
+//   3. compact  each chunk resolves the exact threshold key from the level-2
+//               histogram (and, when its threshold bin is not kept whole, the
+//               low 8 bits of that bin's few candidates) and its own output
+//               offset from the candidates' per-chunk counts, then writes its
+//               kept indices in index order from that offset (ballots inside
+//               waves, counts across waves).
+// Each chunk of the compaction works the threshold out for itself (the same
+// result in every chunk), so no chunk waits for another within a launch. Only
+// the MISA† re-rank hands data on within a launch: the compaction's chunks pass
+// their candidates' dense scores to the last of them through device-coherent
+// stores (sc1: written through to memory, which every XCD's loads with sc1 see)
+// completed before an atomic arrival count; the L2 write-back fence that a
 // release would add costs more than the whole selection on gfx950.
 #include "misa_common.hpp"
 #include "misa_internal.hpp"
@@ -36,10 +39,11 @@ constexpr int kBins = kSelBins;
 constexpr int kMaxChunks = 1024;
 constexpr int kCandReg = 8 * kThreads;       // candidates the last chunk holds in registers
 
-// state[t][*]: written by the last chunk of the filter launch
-enum { ST_THR = 0, ST_KREM = 1 };
-// counter[t][*] (zero on entry)
-enum { CT_CAND = 0, CT_DONE = 1, CT_FINE = 2 };
+// state[t][*]: the row's level-1 threshold bin, how many of its keys are kept,
+// and how many keys it holds (written by the filter launch's first chunk)
+enum { ST_B1 = 0, ST_KREM1 = 1, ST_M = 2 };
+// counter[t][*] (zero on entry): candidate-list cursor, arrivals of the MISA† fine stage
+enum { CT_CAND = 0, CT_FINE = 2 };
 
 __device__ __forceinline__ int64_t row_len_of(const TopkArgs& a, int64_t t, int& p) {
   p = query_prefix_len(a.q_seq, a.q_len, a.nseq, a.Lmax, t);
@@ -111,27 +115,15 @@ __global__ __launch_bounds__(kThreads) void split_hist_kernel(TopkArgs a, SplitT
 // Every chunk finds the row's threshold bin b1 from the finished histogram,
 // counts its keys above b1 and appends the keys of bin b1 (key, index) to the
 // row's candidate list (one cursor reservation per workgroup), and counts key
-// bits 8..19 of those keys into the row's level-2 histogram. The last chunk of
-// the row to arrive then
-//   - resolves the threshold key thr: the level-2 threshold bin b2 (all the
-//     candidates share the top 12 bits b1); when b2 is not kept whole, a
-//     256-bin histogram of the low 8 bits of its keys (usually one or two)
-//     gives the rest, and how many keys equal to thr are kept (krem; all of
-//     them when b2 is kept whole);
-//   - counts the kept candidates of every chunk, and writes each chunk's output
-//     offset (keys kept in the chunks before it) and the number of keys equal
-//     to thr in front of it, for the compaction launch.
+// bits 8..19 of those keys into the row's level-2 histogram. The first chunk
+// records b1, how many of its keys are kept and how many it holds; the
+// compaction launch resolves the rest (resolve_threshold below).
 template <int EPT>
 __global__ __launch_bounds__(kThreads) void split_filter_kernel(TopkArgs a, SplitTopkWs w) {
   __shared__ uint32_t lh[kBins];
   __shared__ uint32_t sh[4];
   __shared__ uint32_t wsum[kWaves];
   __shared__ uint32_t wcnt[kWaves], wdef[kWaves], wbase[kWaves];
-  __shared__ uint32_t s_last;
-  // the last chunk only
-  __shared__ uint32_t s_p[kCandReg];   // level-3 histogram, then the list prefix
-  __shared__ uint32_t wsum2[3][kWaves], sh2[4], sh3[4];
-  __shared__ uint32_t cgt[kMaxChunks], ceq[kMaxChunks];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t = blockIdx.y;
   const int c = blockIdx.x;
@@ -162,8 +154,7 @@ __global__ __launch_bounds__(kThreads) void split_filter_kernel(TopkArgs a, Spli
     mk[j] = __ballot(in[j] && bin == b1);
     ncand += (uint32_t)__popcll(mk[j]);
   }
-  // level 2: bits 8..19 of the keys of bin b1 (device-scope atomics, complete
-  // before this chunk's arrival below)
+  // level 2: bits 8..19 of the keys of bin b1
   uint32_t* h2 = w.hist2 + t * kBins;
 #pragma unroll
   for (int j = 0; j < EPT; ++j)
@@ -181,12 +172,16 @@ __global__ __launch_bounds__(kThreads) void split_filter_kernel(TopkArgs a, Spli
       nd += wdef[ww];
     }
     uint32_t b = tot ? atomicAdd(w.counter + t * 4 + CT_CAND, tot) : 0u;
-    store_coherent(reinterpret_cast<uint64_t*>(w.seg) + t * w.nchunk + c, ((uint64_t)tot << 32) | b);
     for (int ww = 0; ww < kWaves; ++ww) {
       wbase[ww] = b;
       b += wcnt[ww];
     }
-    store_coherent(w.ndef + t * w.nchunk + c, nd);
+    w.ndef[t * w.nchunk + c] = nd;
+    if (c == 0) {   // the row's threshold bin, found alike by every chunk
+      w.state[t * 8 + ST_B1] = b1;
+      w.state[t * 8 + ST_KREM1] = krem1;
+      w.state[t * 8 + ST_M] = m_all;
+    }
   }
   __syncthreads();
   uint64_t* cand = reinterpret_cast<uint64_t*>(w.cand) + t * w.cap;
@@ -197,45 +192,62 @@ __global__ __launch_bounds__(kThreads) void split_filter_kernel(TopkArgs a, Spli
   for (int j = 0; j < EPT; ++j) {
     const uint32_t pos = run + (uint32_t)__popcll(mk[j] & lt);
     if (((mk[j] >> lane) & 1ull) && pos < (uint32_t)w.cap)
-      store_coherent(cand + pos, ((uint64_t)(uint32_t)(base + 64 * j) << 32) | u[j]);
+      cand[pos] = ((uint64_t)(uint32_t)(base + 64 * j) << 32) | u[j];
     run += (uint32_t)__popcll(mk[j]);
   }
-  // ---- arrival: this chunk's list entries and count are in memory before it counts
-  wait_stores();
-  __syncthreads();
-  const int nact = (int)((n + kThreads * EPT - 1) / (kThreads * EPT));
-  if (tid == 0) {
-    const uint32_t before =
-        __hip_atomic_fetch_add(w.counter + t * 4 + CT_DONE, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = before == (uint32_t)(nact - 1) ? 1u : 0u;
-  }
-  __syncthreads();
-  if (!s_last) return;
+}
 
-  // ---- the last chunk: exact threshold among the m candidates of bin b1.
-  // Thread i holds list entries 8i .. 8i + 7, so that per-chunk counts are
-  // differences of one prefix sum over the list order (each chunk appended its
-  // candidates as one run).
-  const uint32_t m = m_all < (uint32_t)w.cap ? m_all : (uint32_t)w.cap;
-  const bool inreg = m <= (uint32_t)kCandReg;
+// The exact threshold of row t and the output offset of chunk c, worked out by
+// every chunk of the compaction launch from what the filter launch left: the
+// threshold bin b1 and how many of its keys are kept (krem1), the candidate list
+// (key, index) of bin b1, the level-2 histogram of those keys' bits 8..19 and each
+// chunk's count of keys above b1.
+//   - level 2: the threshold sub-bin b2 of the candidates; when it is not kept
+//     whole, a 256-bin histogram of the low 8 bits of its keys (usually one or
+//     two) gives the rest of the threshold key thr, and how many keys equal to
+//     thr are kept (krem; all of them when b2 is kept whole);
+//   - this chunk's output offset: the keys the chunks before it keep (their keys
+//     above b1, and their candidates above thr), plus as many of their
+//     candidates equal to thr as are kept, which is also the number of keys
+//     equal to thr in front of it.
+// Every load (the list requested speculatively up to kCandReg entries) goes out
+// with the chunk's own scores, so the resolution costs one memory round trip
+// and a few barriers instead of the last-arriving chunk's extra round of the
+// filter launch.
+template <int EPT>
+__device__ __forceinline__ void resolve_threshold(const TopkArgs& a, const SplitTopkWs& w, int64_t t, int c,
+                                                  int64_t n, const float* row, int64_t e0, uint32_t (&u)[EPT],
+                                                  bool (&in)[EPT], uint32_t& thr, uint32_t& krem_eq,
+                                                  uint32_t& sel_before, uint32_t& eq_before) {
+  __shared__ uint32_t s_h[kBins];
+  __shared__ uint32_t s_h3[256];
+  __shared__ uint32_t s_ws[3][2 * kWaves];
+  __shared__ uint32_t s_o[3][4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  constexpr int CH = kThreads * EPT;
+  const int nact = (int)((n + CH - 1) / CH);
+  // ---- every request at once
+  const uint32_t* st = w.state + t * 8;
+  const uint32_t b1 = st[ST_B1], krem1 = st[ST_KREM1], m_all = st[ST_M];
+  const uint64_t* cand = reinterpret_cast<const uint64_t*>(w.cand) + t * w.cap;
   uint64_t cv[8];
-  // unconditional loads from a clamped index (m >= 1: bin b1 holds the krem1-th
-  // key), so that all of them go out before the first wait
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t i = (uint32_t)(8 * tid + j);
-    const uint64_t x = load_coherent(cand + (i < m ? i : m - 1u));
-    cv[j] = (inreg && i < m) ? x : 0ull;
+  for (int j = 0; j < 8; ++j) {   // list slots past the list's length are masked below
+    const int64_t i = 8 * tid + j;
+    cv[j] = cand[i < w.cap ? i : w.cap - 1];
   }
-  const int tc = tid < nact ? tid : 0;
-  const uint32_t nd_l = load_coherent(w.ndef + t * w.nchunk + tc);
-  const uint64_t sg_l = load_coherent(reinterpret_cast<const uint64_t*>(w.seg) + t * w.nchunk + tc);
-  // the level-2 histogram, requested with the list (one round trip for all)
   constexpr int H2PT = kBins / kThreads;
   uint32_t h2v[H2PT];
 #pragma unroll
-  for (int k = 0; k < H2PT; ++k) h2v[k] = load_coherent(w.hist2 + t * kBins + tid + k * kThreads);
-  // visit(f): f(key, index) for each of this thread's candidates
+  for (int k = 0; k < H2PT; ++k) h2v[k] = w.hist2[t * kBins + tid + k * kThreads];
+  const uint32_t nd_l = w.ndef[t * w.nchunk + (tid < nact ? tid : 0)];
+  load_chunk<EPT>(row, e0, n, u, in);
+  const uint32_t m = m_all < (uint32_t)w.cap ? m_all : (uint32_t)w.cap;
+  const bool inreg = m <= (uint32_t)kCandReg;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (!inreg || (uint32_t)(8 * tid + j) >= m) cv[j] = 0ull;
+  // visit(f): f(key, index) for each candidate of this thread
   auto visit = [&](auto&& f) {
     if (inreg) {
 #pragma unroll
@@ -243,107 +255,57 @@ __global__ __launch_bounds__(kThreads) void split_filter_kernel(TopkArgs a, Spli
         if ((uint32_t)(8 * tid + j) < m) f((uint32_t)cv[j], (uint32_t)(cv[j] >> 32));
     } else {
       for (uint32_t i = tid; i < m; i += kThreads) {
-        const uint64_t x = load_coherent(cand + i);
+        const uint64_t x = cand[i];
         f((uint32_t)x, (uint32_t)(x >> 32));
       }
     }
   };
-  if (!inreg)
-    for (int i = tid; i < kMaxChunks; i += kThreads) {
-      cgt[i] = 0;
-      ceq[i] = 0;
-    }
-  // level 2: the threshold sub-bin b2 of bits 8..19 among the m keys of bin b1
-  uint32_t* const h3 = s_p;   // level 3: 256 bins of the low 8 bits
-  const uint32_t nd_c = tid < nact ? nd_l : 0u;
-  const uint64_t sg = tid < nact ? sg_l : 0ull;
 #pragma unroll
-  for (int k = 0; k < H2PT; ++k) lh[tid + k * kThreads] = h2v[k];
-  if (tid < 256) h3[tid] = 0u;
+  for (int k = 0; k < H2PT; ++k) s_h[tid + k * kThreads] = h2v[k];
+  if (tid < 256) s_h3[tid] = 0u;
   __syncthreads();
-  find_threshold(lh, kBins, krem1, wsum2[0], sh2);
-  const uint32_t b2 = sh2[0], krem2 = sh2[1];
-  uint32_t thr, krem_eq;
-  if (sh2[2]) {
+  // ---- level 2 (and 3): the threshold key
+  find_threshold(s_h, kBins, krem1, s_ws[0], s_o[0]);
+  const uint32_t b2 = s_o[0][0], krem2 = s_o[0][1];
+  if (s_o[0][2]) {
     // the sub-bin is kept whole: every key from its lowest value up
     thr = (b1 << 20) | (b2 << 8);
     krem_eq = 0xffffffffu;
   } else {
-    // level 3: the low 8 bits of the (usually few) keys of sub-bin b2
     visit([&](uint32_t key, uint32_t) {
-      if (((key >> 8) & 0xfffu) == b2) atomicAdd(&h3[key & 0xffu], 1u);
+      if (((key >> 8) & 0xfffu) == b2) atomicAdd(&s_h3[key & 0xffu], 1u);
     });
     __syncthreads();
-    find_threshold(h3, 256, krem2, wsum2[1], sh3);
-    thr = (b1 << 20) | (b2 << 8) | sh3[0];
-    krem_eq = sh3[1];   // all 32 bits resolved: the first krem_eq keys equal to thr
+    find_threshold(s_h3, 256, krem2, s_ws[1], s_o[1]);
+    thr = (b1 << 20) | (b2 << 8) | s_o[1][0];
+    krem_eq = s_o[1][1];   // all 32 bits resolved: the first krem_eq keys equal to thr
   }
-  // ---- kept candidates of every chunk (keys above thr, keys equal to thr)
-  uint32_t gt_c = 0, eq_c = 0;
-  if (inreg) {
-    // prefix over the list of (above << 16 | equal), m <= 8192 keeps both
-    // halves below 2^16; the level-3 histogram is free again
-    uint32_t* P = s_p;
-    uint32_t loc[8], run = 0;
+  // ---- what the chunks before this one keep: their keys above b1 and their
+  // candidates above thr, and their candidates equal to thr (a candidate lies
+  // in an earlier chunk when its index is below this chunk's first one)
+  const int64_t e0c = e0;
+  uint32_t g = tid < c ? nd_l : 0u, q = 0u;
+  visit([&](uint32_t key, uint32_t idx) {
+    if ((int64_t)idx < e0c) {
+      g += key > thr ? 1u : 0u;
+      q += key == thr ? 1u : 0u;
+    }
+  });
+  g = wave_sum(g);
+  q = wave_sum(q);
+  if (lane == 0) {
+    s_ws[2][tid >> 6] = g;
+    s_ws[2][kWaves + (tid >> 6)] = q;
+  }
+  __syncthreads();
+  uint32_t gtb = 0, eqb = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t key = (uint32_t)cv[j];
-      const bool ok = (uint32_t)(8 * tid + j) < m;
-      run += ok ? (((key > thr) ? 1u << 16 : 0u) | (key == thr ? 1u : 0u)) : 0u;
-      loc[j] = run;
-    }
-    uint32_t tot;
-    const uint32_t pre = block_excl_scan(run, wsum2[0], tot);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if ((uint32_t)(8 * tid + j) < m) P[8 * tid + j] = pre + loc[j];
-    __syncthreads();
-    if (tid < nact) {
-      const uint32_t start = (uint32_t)sg, cnt = (uint32_t)(sg >> 32);
-      const uint32_t hiv = cnt ? P[start + cnt - 1] : 0u, lov = (cnt && start) ? P[start - 1] : 0u;
-      gt_c = nd_c + ((hiv - lov) >> 16);
-      eq_c = (hiv - lov) & 0xffffu;
-    }
-  } else {
-    // long lists: one LDS atomic per (wave, chunk) group of list entries
-    constexpr int CH = kThreads * EPT;
-    auto count_chunks = [&](uint64_t x, bool valid) {   // called by the whole wave
-      const uint32_t key = (uint32_t)x;
-      const int cc = valid ? (int)((uint32_t)(x >> 32) / CH) : -1;
-      const uint64_t mg = __ballot(valid && key > thr), mq = __ballot(valid && key == thr);
-      uint64_t pending = __ballot(valid);
-      while (pending) {
-        const int leader = __ffsll((unsigned long long)pending) - 1;
-        const int lc = __builtin_amdgcn_readlane(cc, leader);
-        const uint64_t mask = __ballot(cc == lc) & pending;
-        if (lane == leader) {
-          const uint32_t ng = (uint32_t)__popcll(mg & mask), nq = (uint32_t)__popcll(mq & mask);
-          if (ng) atomicAdd(&cgt[lc], ng);
-          if (nq) atomicAdd(&ceq[lc], nq);
-        }
-        pending &= ~mask;
-      }
-    };
-    for (uint32_t b0 = 0; b0 < m; b0 += kThreads) {
-      const uint32_t i = b0 + tid;
-      count_chunks(i < m ? load_coherent(cand + i) : 0ull, i < m);
-    }
-    __syncthreads();
-    if (tid < nact) {
-      gt_c = nd_c + cgt[tid];
-      eq_c = ceq[tid];
-    }
+  for (int ww = 0; ww < kWaves; ++ww) {
+    gtb += s_ws[2][ww];
+    eqb += s_ws[2][kWaves + ww];
   }
-  uint32_t eq_before;
-  const uint32_t gt_before = block_excl_scan2(gt_c, eq_c, &wsum2[1][0], eq_before);
-  if (tid < nact) {
-    w.selb[t * w.nchunk + tid] = gt_before + (eq_before < krem_eq ? eq_before : krem_eq);
-    w.eqb[t * w.nchunk + tid] = eq_before;
-  }
-  if (tid == 0) {
-    w.state[t * 8 + ST_THR] = thr;
-    w.state[t * 8 + ST_KREM] = krem_eq;
-  }
+  sel_before = gtb + (eqb < krem_eq ? eqb : krem_eq);
+  eq_before = eqb;
 }
 
 // Every chunk writes its kept indices in index order: the keys above the row's
@@ -446,12 +408,10 @@ __global__ __launch_bounds__(kThreads) void split_compact_kernel(TopkArgs a, Spl
     if constexpr (!RESCORE) return;
   } else {
     if (e0 >= n) return;
-    const uint32_t* st = w.state + t * 8;
-    const uint32_t ustar = st[ST_THR], krem = st[ST_KREM];
-    const uint32_t sel_before = w.selb[t * w.nchunk + c], eq_before = w.eqb[t * w.nchunk + c];
+    uint32_t ustar, krem, sel_before, eq_before;
     uint32_t u[EPT];
     bool in[EPT];
-    load_chunk<EPT>(row, e0, n, u, in);
+    resolve_threshold<EPT>(a, w, t, c, n, row, e0, u, in, ustar, krem, sel_before, eq_before);
     // ---- compaction of this chunk (from registers)
     uint32_t cgt = 0, ceq = 0;
 #pragma unroll
@@ -570,8 +530,8 @@ inline int64_t cand_cap(int64_t max_len) { return max_len; }
 size_t split_topk_ws_bytes(int64_t T, int64_t max_len) {
   const int chunk = split_chunk(max_len);
   const int64_t nchunk = (max_len + chunk - 1) / chunk;
-  return al((size_t)T * (2 * kBins + 4) * 4) + al((size_t)T * 8 * 4) + 3 * al((size_t)T * nchunk * 4) +
-         al((size_t)T * nchunk * 8) + al((size_t)T * cand_cap(max_len) * 8);
+  return al((size_t)T * (2 * kBins + 4) * 4) + al((size_t)T * 8 * 4) + al((size_t)T * nchunk * 4) +
+         al((size_t)T * cand_cap(max_len) * 8);
 }
 
 SplitTopkWs split_topk_carve(void* base, int64_t T, int64_t max_len) {
@@ -589,12 +549,6 @@ SplitTopkWs split_topk_carve(void* base, int64_t T, int64_t max_len) {
   p += al((size_t)T * 8 * 4);
   w.ndef = reinterpret_cast<uint32_t*>(p);
   p += al((size_t)T * w.nchunk * 4);
-  w.selb = reinterpret_cast<uint32_t*>(p);
-  p += al((size_t)T * w.nchunk * 4);
-  w.eqb = reinterpret_cast<uint32_t*>(p);
-  p += al((size_t)T * w.nchunk * 4);
-  w.seg = reinterpret_cast<uint32_t*>(p);
-  p += al((size_t)T * w.nchunk * 8);
   w.cand = reinterpret_cast<uint32_t*>(p);
   return w;
 }
