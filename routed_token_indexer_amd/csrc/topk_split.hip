@@ -37,7 +37,7 @@ constexpr int kThreads = kSelThreads;       // 16 waves: four per SIMD hide LDS 
 constexpr int kWaves = kThreads / 64;
 constexpr int kBins = kSelBins;
 constexpr int kMaxChunks = 1024;
-constexpr int kCandReg = 8 * kThreads;       // candidates the last chunk holds in registers
+constexpr int kCandReg = 8 * kThreads;       // candidates a compaction chunk holds in registers
 
 // state[t][*]: the row's level-1 threshold bin, how many of its keys are kept,
 // and how many keys it holds (written by the filter launch's first chunk)
@@ -212,8 +212,7 @@ __global__ __launch_bounds__(kThreads) void split_filter_kernel(TopkArgs a, Spli
 //     equal to thr in front of it.
 // Every load (the list requested speculatively up to kCandReg entries) goes out
 // with the chunk's own scores, so the resolution costs one memory round trip
-// and a few barriers instead of the last-arriving chunk's extra round of the
-// filter launch.
+// and a few barriers, and no chunk waits for another.
 template <int EPT>
 __device__ __forceinline__ void resolve_threshold(const TopkArgs& a, const SplitTopkWs& w, int64_t t, int c,
                                                   int64_t n, const float* row, int64_t e0, uint32_t (&u)[EPT],
@@ -310,8 +309,8 @@ __device__ __forceinline__ void resolve_threshold(const TopkArgs& a, const Split
 
 // Every chunk writes its kept indices in index order: the keys above the row's
 // threshold key thr, and of the keys equal to thr those ranked (in index
-// order) below krem. Its output offset and the number of keys equal to thr in
-// front of it come from the filter's last chunk.
+// order) below krem. thr, krem, its output offset and the number of keys equal
+// to thr in front of it come from resolve_threshold.
 // RESCORE (the coarse pass of the fused MISA† pipeline): the kept tokens of the
 // chunk are then scored with all H heads (D-dim keys, RT row tiles) into the
 // candidate-slot score row r.scores (and, with r.hist, the re-rank's level-1
