@@ -652,7 +652,10 @@ namespace {
 template <int EPT, bool GATHER, int NT, bool MANY>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MANY ? 8 : NT / 256))) void topk_row_reg_kernel(
     TopkArgs a) {
-  topk_row_reg_row<EPT, GATHER, NT, MANY, false>(a, (int64_t)a.T - 1 - blockIdx.x);   // longest rows first
+  // causal batches: longest rows first, unless the launch takes only the shorter
+  // rows (then the rows it leaves alone, the longer ones, come last and fill the tail)
+  topk_row_reg_row<EPT, GATHER, NT, MANY, false>(a, a.len_hi != INT64_MAX ? (int64_t)blockIdx.x
+                                                                        : (int64_t)a.T - 1 - blockIdx.x);
 }
 
 }  // namespace
