@@ -90,7 +90,8 @@ size_t select_ws_bytes(int64_t T, int64_t max_len) {
 // Workspace of the fused decode pipeline (misa_indexer / misa_hier_indexer):
 // router partials and partial-block dots, the coarse score rows and their split
 // top-k state, and for MISA† the candidate list, its dense scores and their
-// split top-k state.
+// split top-k state, and the dense scores of the coarse members of the
+// one-launch MISA† selection.
 struct FusedLayout {
   size_t bytes = 0;
   int nchunk_r = 1, chunk_blocks = 1;
@@ -101,6 +102,7 @@ struct FusedLayout {
   int32_t* cand = nullptr;
   float* rr_scores = nullptr;
   misa::SplitTopkWs rw{};
+  float* mscore = nullptr;
 };
 
 FusedLayout fused_layout(int64_t T, int H, int64_t Lmax, int B, int64_t kc, void* base) {
@@ -123,6 +125,7 @@ FusedLayout fused_layout(int64_t T, int H, int64_t Lmax, int B, int64_t kc, void
     f.rr_scores = reinterpret_cast<float*>(take((size_t)T * kc * 4));
     char* rw = take(misa::split_topk_ws_bytes(T, kc));
     if (p) f.rw = misa::split_topk_carve(rw, T, kc);
+    if (kc <= 8192) f.mscore = reinterpret_cast<float*>(take((size_t)T * Lmax * 4));
   }
   f.bytes = off;
   return f;
@@ -618,14 +621,14 @@ int32_t run_indexer(const char* fn, bool hier, const void* q, const float* w, co
     r.d = d;
     r.scores = f.rr_scores;
     r.hist = fine_split ? f.rw.hist : nullptr;   // level-1 histogram of the split fine stage
-    // rows of at most 8192 candidates: the fine stage runs inside the same
-    // launch, in the last workgroup of each row to finish its re-scoring
-    r.fine = !fine_split && kc <= 8192;
     r.fidx = idx;
     r.fscore = score;
     r.ftopk = topk;
-    e = misa::launch_topk_split_rescore(b, f.sw, r, st);
-    if (e == hipSuccess && !r.fine) {
+    // rows of at most 8192 candidates: coarse selection, re-scoring and fine
+    // selection in one launch
+    const bool one = kc <= 8192;
+    e = one ? misa::launch_hier_select(b, f.sw, r, f.mscore, st) : misa::launch_topk_split_rescore(b, f.sw, r, st);
+    if (e == hipSuccess && !one) {
       // 4. MISA† fine stage: top-k of the candidates' dense scores
       misa::TopkArgs b2{};
       b2.scores = f.rr_scores;

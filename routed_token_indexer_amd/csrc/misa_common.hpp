@@ -22,6 +22,11 @@ __device__ __forceinline__ floatx4 mfma_16x16x32(const u32x4& a, const u32x4& b,
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Set bits of the wave mask m in the lanes below the calling lane (v_mbcnt).
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 // max(x, 0) as one integer instruction on the bits: a float with the sign bit
 // set (negative, -0) is a negative int and becomes +0, any other is kept as is.
 // (A float max or median needs the compiler to quiet a possible signalling NaN
@@ -97,6 +102,9 @@ __device__ __forceinline__ float load_coherent(const float* p) {
 }
 __device__ __forceinline__ uint32_t atomic_add_coherent(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t atomic_max_coherent(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // Waits until this thread's stores and atomics have completed (the sc1 stores
 // above: reached the memory side). The asm's memory clobber also keeps the

@@ -115,7 +115,8 @@ struct SplitTopkWs {
   uint32_t* hist2;     // [T][4096] key bits 8..19 of the level-1 threshold bin's keys (zero on entry)
   uint32_t* state;     // [T][8] level-1 threshold bin, how many of its keys are kept, how many it holds
   uint32_t* counter;   // [T][4] candidate-list cursor, arrivals of the MISA† fine stage (zero on entry)
-  uint32_t* ndef;      // [T][nchunk] keys above the level-1 threshold bin in each chunk
+  uint32_t* ndef;      // [T][nchunk] keys above the level-1 threshold bin in each chunk; then
+                       // [T][nchunk][3] the MISA† selection's member count and dense-key range
   uint32_t* cand;      // [T][cap][2] (key, index) of the level-1 threshold bin
   int64_t cap;
   int chunk;
@@ -142,9 +143,7 @@ struct RescoreArgs {
   int d;
   float* scores;            // [T][kc] dense score of each candidate slot
   uint32_t* hist;           // [T][4096] level-1 histogram of those scores (zero on entry)
-  // fine stage in the same launch (rows of at most 8192 candidates): the last
-  // workgroup of a row to finish its re-scoring selects the row's final top-k
-  bool fine;
+  // the final top-k, selected in the same launch (launch_hier_select only)
   int32_t* fidx;            // [T][ftopk]
   float* fscore;            // [T][ftopk] or null
   int ftopk;
@@ -152,6 +151,13 @@ struct RescoreArgs {
 // filter + compact of the coarse pass (level-1 histogram already built), the
 // compact writing the candidate list (a.idx, k = kc) and its dense scores.
 hipError_t launch_topk_split_rescore(const TopkArgs& a, const SplitTopkWs& w, const RescoreArgs& r, hipStream_t st);
+// The whole MISA† selection of rows of at most 8192 candidates in one launch
+// (level-1 histogram of the routed scores already built; counters zero on
+// entry): coarse top-k' (a.idx, k = k'), dense scores of the candidates
+// (r.scores) and the final top-k (r.fidx, r.fscore). mscore: [T][w.cap] dense
+// scores of the coarse members (workspace).
+hipError_t launch_hier_select(const TopkArgs& a, const SplitTopkWs& w, const RescoreArgs& r, float* mscore,
+                              hipStream_t st);
 
 
 // Coarse stage of the block filter: the routed indexer formula on the pooled

@@ -128,14 +128,17 @@ __device__ __forceinline__ void radix_clear(RadixScratch<NT, NH>& rs) {
 
 // Radix select among values v in [0, 2^nbits) (nbits <= 32) that each thread
 // visits with visit(f) (f(v) for each of its values). Levels of up to 12 bits
-// from the top bit down find where the krem-th largest value lies; a level
+// from the top bit down find where the krem-th largest value lies (krem: on
+// entry, how many values to keep, at least 1 and at most their number); a level
 // whose threshold bin is kept whole ends the select. On return (same in every
 // thread) the kept values are those with (v & pmask) > prefix, then krem of
 // those with (v & pmask) == prefix (the lowest indices first). `full` tells
-// whether every one of the nbits bits was resolved.
+// whether every one of the nbits bits was resolved. xn further copies of the
+// value xv take part (counted by thread 0), ranked after every visited value.
 template <int NT, int NH, typename Visit>
 __device__ __forceinline__ void radix_select(Visit visit, int nbits, uint32_t& prefix, uint32_t& pmask,
-                                             uint32_t& krem, bool& full, RadixScratch<NT, NH>& rs) {
+                                             uint32_t& krem, bool& full, RadixScratch<NT, NH>& rs,
+                                             uint32_t xv = 0u, uint32_t xn = 0u) {
   prefix = 0;
   pmask = 0;
   full = true;
@@ -155,6 +158,7 @@ __device__ __forceinline__ void radix_select(Visit visit, int nbits, uint32_t& p
     visit([&](uint32_t v) {
       if ((v & pm) == pf) atomicAdd(&h[(v >> shift) & dm], 1u);
     });
+    if (threadIdx.x == 0 && xn && (xv & pm) == pf) atomicAdd(&h[(xv >> shift) & dm], xn);
     __syncthreads();
     find_threshold<NT>(h, 1 << width, krem, rs.wsum[lv], rs.out[lv]);
     prefix |= rs.out[lv][0] << shift;

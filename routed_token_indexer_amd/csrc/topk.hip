@@ -643,10 +643,6 @@ __device__ __attribute__((always_inline)) void topk_row_reg_row(const TopkArgs& 
     oi[0] = kFallbackMark;
 }
 
-// The fine stage of the fused MISA-dagger pass selects its rows inside the
-// compaction launch (rows of at most 8192 candidates, 1024 threads).
-template __device__ void topk_row_reg_row<8, true, 1024, false, true>(const TopkArgs& a, int64_t t);
-
 namespace {
 
 template <int EPT, bool GATHER, int NT, bool MANY>

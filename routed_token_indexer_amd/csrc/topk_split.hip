@@ -19,12 +19,13 @@
 //               kept indices in index order from that offset (ballots inside
 //               waves, counts across waves).
 // Each chunk of the compaction works the threshold out for itself (the same
-// result in every chunk), so no chunk waits for another within a launch. Only
-// the MISA† re-rank hands data on within a launch: the compaction's chunks pass
-// their candidates' dense scores to the last of them through device-coherent
-// stores (sc1: written through to memory, which every XCD's loads with sc1 see)
-// completed before an atomic arrival count; the L2 write-back fence that a
-// release would add costs more than the whole selection on gfx950.
+// result in every chunk), so no chunk waits for another within a launch.
+// The MISA† selection of up to 8192 candidates (hier_select_kernel) takes one
+// launch instead: its chunks hand their members on to the last of them through
+// device-coherent stores (sc1: written through to memory, which every XCD's
+// loads with sc1 see) completed before an atomic arrival count; the L2
+// write-back fence that a release would add costs more than the whole selection
+// on gfx950.
 #include "misa_common.hpp"
 #include "misa_internal.hpp"
 #include "misa_score_dev.hpp"
@@ -42,7 +43,8 @@ constexpr int kCandReg = 8 * kThreads;       // candidates a compaction chunk ho
 // state[t][*]: the row's level-1 threshold bin, how many of its keys are kept,
 // and how many keys it holds (written by the filter launch's first chunk)
 enum { ST_B1 = 0, ST_KREM1 = 1, ST_M = 2 };
-// counter[t][*] (zero on entry): candidate-list cursor, arrivals of the MISA† fine stage
+// counter[t][*] (zero on entry): candidate-list cursor, arrivals of the MISA†
+// selection
 enum { CT_CAND = 0, CT_FINE = 2 };
 
 __device__ __forceinline__ int64_t row_len_of(const TopkArgs& a, int64_t t, int& p) {
@@ -379,12 +381,8 @@ __global__ __launch_bounds__(kThreads) void split_compact_kernel(TopkArgs a, Spl
       int32_t id;
       float sc;
       out_entry(imap, p, e, score_key(row[e]), id, sc);
-      if constexpr (RESCORE) {
-        store_coherent(reinterpret_cast<uint32_t*>(oi + e), (uint32_t)id);
-        s_tok[e - e0] = (int)e;
-      } else {
-        oi[e] = id;
-      }
+      oi[e] = id;
+      if constexpr (RESCORE) s_tok[e - e0] = (int)e;
       if (os) os[e] = sc;
     }
     if constexpr (RESCORE) {
@@ -396,12 +394,10 @@ __global__ __launch_bounds__(kThreads) void split_compact_kernel(TopkArgs a, Spl
     // padding [n, k), spread over the row's chunks
     for (int64_t j = n + (int64_t)c * kThreads + tid; j < a.k; j += (int64_t)w.nchunk * kThreads) {
       if (os) os[j] = 0.f;
+      oi[j] = -1;
       if constexpr (RESCORE) {
-        store_coherent(reinterpret_cast<uint32_t*>(oi + j), 0xffffffffu);
-        store_coherent(r.scores + t * (int64_t)a.k + j, -INFINITY);
+        r.scores[t * (int64_t)a.k + j] = -INFINITY;
         if (r.hist) atomicAdd(&lh[score_key(-INFINITY) >> 20], 1u);
-      } else {
-        oi[j] = -1;
       }
     }
     if constexpr (!RESCORE) return;
@@ -446,12 +442,8 @@ __global__ __launch_bounds__(kThreads) void split_compact_kernel(TopkArgs a, Spl
         int32_t id;
         float sc;
         out_entry(imap, p, base + 64 * j, u[j], id, sc);
-        if constexpr (RESCORE) {
-          store_coherent(reinterpret_cast<uint32_t*>(oi + pos), (uint32_t)id);
-          s_tok[pos - sel_before] = (int)(base + 64 * j);
-        } else {
-          oi[pos] = id;
-        }
+        oi[pos] = id;
+        if constexpr (RESCORE) s_tok[pos - sel_before] = (int)(base + 64 * j);
         if (os) os[pos] = sc;
       }
       eq_run += (uint32_t)__popcll(meq);
@@ -474,7 +466,7 @@ __global__ __launch_bounds__(kThreads) void split_compact_kernel(TopkArgs a, Spl
       load_key_tiles<D, 1>(kseq, b, (int)nsel, col, [&](int s) { return s_tok[s]; }, 0, tile);
       const float v = score_one_tile_lds<D, RT>(s_q, LDQ, s_w, tile, grp, col);
       if (grp == 0 && b + col < (int)nsel) {
-        store_coherent(rrow + off + b + col, v);
+        rrow[off + b + col] = v;
         if (r.hist) atomicAdd(&lh[score_key(v) >> 20], 1u);
       }
     }
@@ -484,27 +476,569 @@ __global__ __launch_bounds__(kThreads) void split_compact_kernel(TopkArgs a, Spl
       for (int i = tid; i < kBins; i += kThreads)
         if (lh[i]) atomicAdd(&gh[hist_word(i)], lh[i]);
     }
-    if (!r.fine) return;
-    // ---- the last workgroup of the row to finish selects the row's final top-k
-    // among its kc candidate slots: the candidate ids and dense scores of every
-    // chunk are stored (written through) before the chunk counts its arrival
-    __shared__ uint32_t s_fine_last;
-    wait_stores();
+  }
+}
+
+// MISA† coarse selection, dense re-scoring and fine selection in one launch
+// (k' <= 8192; one workgroup per (chunk, row), the routed scores' level-1
+// histogram already built by the scoring kernel).
+//   - Members of a chunk: for a row of more than k' visible tokens, its keys in
+//     the level-1 threshold bin b1 or above it. That is a superset of the
+//     chunk's share of the exact top-k': all the keys above b1 are in it, and of
+//     the keys of b1 only krem1 are. For a row of at most k' tokens, every
+//     visible token is a member and is kept.
+//   - Each chunk scores its members with all H heads and stores them in index
+//     order as (index, routed key) and dense score in its own region of the
+//     row's member lists; it adds key bits 8..19 of its members in b1 to the
+//     row's level-2 histogram and its members' dense-key range to the row's,
+//     stores its member count and counts its arrival (everything written
+//     through before the count).
+//   - The chunk that arrives last resolves the exact top-k' among the members
+//     (level 2 from the histogram, level 3 over the members of the threshold
+//     sub-bin): the kept ones are above the threshold key, or equal to it and
+//     among the first krem in index order. It writes their indices as the
+//     candidate list (ascending, -1 padded to k') and selects the final top-k
+//     among them by dense score out of registers: a histogram of the dense keys
+//     over their range, then the few keys of the threshold bin ranked in LDS.
+// Compared with the filter and compaction launches and a fine-stage select,
+// this saves a launch, the exact threshold's round before the re-scoring and
+// the candidate list's round trip through memory. The price is re-scoring the
+// members of b1 that are not kept, usually a few thousand keys of a 128K row.
+template <int EPT, int D, int RT>
+__global__ __launch_bounds__(kThreads) void hier_select_kernel(TopkArgs a, SplitTopkWs w, RescoreArgs r,
+                                                               float* mscore) {
+  constexpr int CH = kThreads * EPT;
+  constexpr int LDQ = D + 8;    // padded row stride of the staged query rows (bf16)
+  constexpr int G = 8, NS = 2;  // last chunk: members per lane and chunk in registers, chunks per wave
+  constexpr int kCand = 512;    // keys of the fine threshold bin ranked in LDS
+  // histograms: the routed keys' level 1, then the last chunk's coarse level 2
+  // and the fine selection's fallback
+  __shared__ __attribute__((aligned(16))) RadixScratch<kThreads, 1> rs;
+  uint32_t* const lh = rs.hist[0];
+  __shared__ uint32_t lf[kBins];   // the fine level 1
+  __shared__ uint32_t s_h3[256];
+  __shared__ uint32_t sh[3][4];
+  __shared__ __attribute__((aligned(16))) uint32_t wsum[4][kWaves];
+  __shared__ uint32_t wcnt[kWaves];
+  __shared__ int s_tok[CH];
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[16 * RT * LDQ];
+  __shared__ float s_w[16 * RT];
+  __shared__ uint32_t s_last, s_mm[2];
+  // the last chunk, per chunk: members; coarse and fine counts and offsets
+  __shared__ uint32_t s_cnt[kMaxChunks], s_gt[kMaxChunks], s_eq[kMaxChunks], s_fgt[kMaxChunks], s_feq[kMaxChunks];
+  __shared__ uint32_t s_tot, s_nc, s_fthr, s_fkrem;
+  __shared__ uint32_t c_key[kCand], c_w[kCand], c_ch[kCand];   // the fine threshold bin's keys
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int64_t t = blockIdx.y;
+  const int c = blockIdx.x;
+  int p;
+  const int64_t n = row_len_of(a, t, p);
+  const int nact = n > 0 ? (int)((n + CH - 1) / CH) : 1;   // chunk 0 always takes part
+  if (c >= nact) return;
+  const int64_t e0 = (int64_t)c * CH;
+  const bool all = n <= a.k;   // every visible token is a candidate
+
+  // ---- every request at once: query rows and weights, the chunk's routed
+  // scores, the row's level-1 histogram
+  const int seq = a.q_seq[t];
+  const uint16_t* kseq = r.k + (int64_t)((seq >= 0 && seq < a.nseq) ? seq : 0) * a.Lmax * D + grp * 8;
+  constexpr int PIECES = 16 * RT * D / 8;   // 16-byte pieces of the padded row block
+  constexpr int QPT = (PIECES + kThreads - 1) / kThreads;
+  u32x4 qv[QPT];
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {   // (clamped addresses; rows past H are zeroed when staged)
+    const int i = tid + k * kThreads;
+    const int rr = i / (D / 8), cc = (i % (D / 8)) * 8;
+    const bool ok = i < PIECES && rr < r.H;
+    qv[k] = *reinterpret_cast<const u32x4*>(r.q + (t * r.H + (ok ? rr : 0)) * D + (ok ? cc : 0));
+  }
+  const float wq = r.w[t * r.H + (tid < r.H ? tid : 0)];
+  uint32_t u[EPT];
+  bool in[EPT];
+  load_chunk<EPT>(a.scores + t * a.stride, e0, n, u, in);
+  constexpr int HPT = kBins / kThreads;
+  uint32_t b1 = 0u, krem1 = 0u;
+  if (!all) {
+    uint32_t hv[HPT];
+#pragma unroll
+    for (int k = 0; k < HPT; ++k) hv[k] = w.hist[t * kBins + tid + k * kThreads];
+#pragma unroll
+    for (int k = 0; k < HPT; ++k) lh[hist_bin(tid + k * kThreads)] = hv[k];
     __syncthreads();
-    const uint32_t arrivals = n <= a.k ? (uint32_t)w.nchunk : (uint32_t)((n + CH - 1) / CH);
-    if (tid == 0)
-      s_fine_last = atomic_add_coherent(w.counter + t * 4 + CT_FINE, 1u) == arrivals - 1 ? 1u : 0u;
+    find_threshold(lh, kBins, (uint32_t)a.k, wsum[0], sh[0]);
+    b1 = sh[0][0];
+    krem1 = sh[0][1];
+  }
+
+  // ---- the chunk's members, in index order; the level-2 histogram of those in b1
+  bool mem[EPT];
+  uint32_t cm = 0;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    mem[j] = in[j] && (all || (u[j] >> 20) >= b1);
+    cm += (uint32_t)__popcll(__ballot(mem[j]));
+  }
+  if (lane == 0) wcnt[wave] = cm;
+  if (tid == 0) {
+    s_mm[0] = 0xffffffffu;
+    s_mm[1] = 0u;
+  }
+  __syncthreads();
+  uint32_t run = 0, nsel = 0;
+#pragma unroll
+  for (int ww = 0; ww < kWaves; ++ww) {
+    run += ww < wave ? wcnt[ww] : 0u;
+    nsel += wcnt[ww];
+  }
+  const int64_t cap = w.cap;
+  uint64_t* const mlist = reinterpret_cast<uint64_t*>(w.cand) + t * cap;
+  float* const mrow = mscore + t * cap;
+  uint32_t* const h2 = w.hist2 + t * kBins;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  const int64_t base = e0 + (int64_t)wave * 64 * EPT + lane;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const uint64_t mk = __ballot(mem[j]);
+    const uint32_t pos = run + (uint32_t)__popcll(mk & lt);
+    if (mem[j]) {
+      s_tok[pos] = (int)(base + 64 * j);
+      store_coherent(mlist + e0 + pos, ((uint64_t)(uint32_t)(base + 64 * j) << 32) | u[j]);
+      if (!all && (u[j] >> 20) == b1) (void)atomic_add_coherent(h2 + ((u[j] >> 8) & 0xfffu), 1u);
+    }
+    run += (uint32_t)__popcll(mk);
+  }
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {
+    const int i = tid + k * kThreads;
+    const int rr = i / (D / 8), cc = (i % (D / 8)) * 8;
+    if (i < PIECES) *reinterpret_cast<u32x4*>(s_q + rr * LDQ + cc) = rr < r.H ? qv[k] : u32x4{0u, 0u, 0u, 0u};
+  }
+  if (tid < 16 * RT) s_w[tid] = tid < r.H ? wq : 0.f;
+  __syncthreads();
+
+  // ---- dense scores of the members, one 16-key tile per wave, and their key range
+  uint32_t mlo = 0xffffffffu, mhi = 0u;
+  for (int b = wave * 16; b < (int)nsel; b += kWaves * 16) {
+    KeyTiles<D, 1> tile;
+    load_key_tiles<D, 1>(kseq, b, (int)nsel, col, [&](int s) { return s_tok[s]; }, 0, tile);
+    const float v = score_one_tile_lds<D, RT>(s_q, LDQ, s_w, tile, grp, col);
+    if (grp == 0 && b + col < (int)nsel) {
+      store_coherent(mrow + e0 + b + col, v);
+      mlo = min(mlo, score_key(v));
+      mhi = max(mhi, score_key(v));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    mlo = min(mlo, (uint32_t)__shfl_xor((int)mlo, off, kWave));
+    mhi = max(mhi, (uint32_t)__shfl_xor((int)mhi, off, kWave));
+  }
+  if (lane == 0) {
+    atomicMin(&s_mm[0], mlo);
+    atomicMax(&s_mm[1], mhi);
+  }
+  // per chunk: member count, smallest and largest dense key
+  uint32_t* const cinfo = w.ndef + (int64_t)a.T * w.nchunk + (t * w.nchunk) * 3;
+  __syncthreads();
+  if (tid == 0) {
+    store_coherent(cinfo + 3 * c, nsel);
+    store_coherent(cinfo + 3 * c + 1, s_mm[0]);
+    store_coherent(cinfo + 3 * c + 2, s_mm[1]);
+  }
+  // ---- arrival: this chunk's members, count and range are in memory before it counts
+  wait_stores();
+  __syncthreads();
+  if (tid == 0) s_last = atomic_add_coherent(w.counter + t * 4 + CT_FINE, 1u) == (uint32_t)nact - 1 ? 1u : 0u;
+  if (tid == 0) {   // for the last chunk's reduction of the ranges
+    s_mm[0] = 0xffffffffu;
+    s_mm[1] = 0u;
+  }
+  __syncthreads();
+  if (!s_last) return;
+
+  // ---- the last chunk. The members of chunk c2 are the first cnt(c2) entries
+  // of its region, in index order; wave w takes the chunks w, w + kWaves, ...
+  // and lane l the entries l, l + 64, ... of each, G at a time. When every chunk
+  // fits (at most NS per wave, 64 * G members each), all of them stay in
+  // registers (loaded with the counts, before the counts are known); otherwise
+  // every pass loads them again.
+  const uint32_t cnt_l = tid < nact ? load_coherent(cinfo + 3 * tid) : 0u;
+  uint32_t klo = tid < nact ? load_coherent(cinfo + 3 * tid + 1) : 0xffffffffu;
+  uint32_t khi = tid < nact ? load_coherent(cinfo + 3 * tid + 2) : 0u;
+  uint32_t h2v[HPT];
+#pragma unroll
+  for (int k = 0; k < HPT; ++k) h2v[k] = all ? 0u : load_coherent(h2 + tid + k * kThreads);
+  uint64_t rx[NS][G];
+  float rd[NS][G];
+  const int64_t slot_max = n > 0 ? n - 1 : 0;
+#pragma unroll
+  for (int s2 = 0; s2 < NS; ++s2) {
+    const int c2 = wave + s2 * kWaves;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      int64_t slot = (int64_t)c2 * CH + g * 64 + lane;
+      slot = slot < slot_max ? slot : slot_max;
+      if (c2 < nact) {
+        rx[s2][g] = load_coherent(mlist + slot);
+        rd[s2][g] = load_coherent(mrow + slot);
+      }
+    }
+  }
+  if (tid < nact) {
+    s_cnt[tid] = cnt_l;
+    s_gt[tid] = 0u;
+    s_eq[tid] = 0u;
+    s_fgt[tid] = 0u;
+    s_feq[tid] = 0u;
+  }
+#pragma unroll
+  for (int k = 0; k < HPT; ++k) {
+    lh[tid + k * kThreads] = h2v[k];
+    lf[tid + k * kThreads] = 0u;
+  }
+  if (tid < 256) s_h3[tid] = 0u;
+  if (tid == 0) s_nc = 0u;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    klo = min(klo, (uint32_t)__shfl_xor((int)klo, off, kWave));
+    khi = max(khi, (uint32_t)__shfl_xor((int)khi, off, kWave));
+  }
+  if (lane == 0 && khi >= klo) {
+    atomicMin(&s_mm[0], klo);
+    atomicMax(&s_mm[1], khi);
+  }
+  uint32_t nbig;
+  (void)block_excl_scan(cnt_l > 64u * G ? 1u : 0u, wsum[1], nbig);   // (its barrier publishes the above)
+  const bool fast = nact <= NS * kWaves && nbig == 0;
+  klo = s_mm[0];   // the members' dense-key range
+  khi = s_mm[1];
+  uint32_t rn[NS];
+#pragma unroll
+  for (int s2 = 0; s2 < NS; ++s2) rn[s2] = wave + s2 * kWaves < nact ? s_cnt[wave + s2 * kWaves] : 0u;
+  // body(x, d, nb, c2, j0) for each block of G * 64 members: entry g of the lane
+  // is member j0 + 64 * g + lane of chunk c2, valid when 64 * g + lane < nb;
+  // a chunk's blocks come in order, from j0 = 0
+  auto each_block = [&](auto&& body) {
+    if (fast) {
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2)
+        if (wave + s2 * kWaves < nact) body(rx[s2], rd[s2], rn[s2], wave + s2 * kWaves, 0u);
+    } else {
+      for (int c2 = wave; c2 < nact; c2 += kWaves) {
+        const uint32_t cn = s_cnt[c2];
+        for (uint32_t j0 = 0; j0 < cn; j0 += 64u * G) {
+          uint64_t x[G];
+          float d[G];
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const uint32_t j = j0 + (uint32_t)(g * 64 + lane);
+            const int64_t slot = j < cn ? (int64_t)c2 * CH + j : 0;
+            x[g] = load_coherent(mlist + slot);
+            d[g] = load_coherent(mrow + slot);
+          }
+          body(x, d, cn - j0, c2, j0);
+        }
+      }
+    }
+  };
+  // ---- coarse threshold: the k'-th largest routed key thr, and how many of
+  // the members equal to it are kept (the first krem_eq in index order)
+  uint32_t thr = 0u, krem_eq = 0xffffffffu;
+  if (!all) {
+    // level 2: bits 8..19 of the keys of b1 (every one of them is a member)
+    find_threshold(lh, kBins, krem1, wsum[0], sh[1]);
+    const uint32_t b2 = sh[1][0], krem2 = sh[1][1];
+    for (int i = tid; i < kBins; i += kThreads) lh[i] = 0u;   // for the fine selection's fallback
+    if (sh[1][2]) {
+      thr = (b1 << 20) | (b2 << 8);   // the sub-bin is kept whole
+    } else {
+      // level 3: the low 8 bits of the members in sub-bin b2
+      const uint32_t hi24 = (b1 << 12) | b2;
+      each_block([&](auto& x, auto&, uint32_t nb, int, uint32_t) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          if (g * 64 >= (int)nb) break;
+          const uint32_t key = (uint32_t)x[g];
+          if (((uint32_t)(g * 64 + lane) < nb) & ((key >> 8) == hi24)) atomicAdd(&s_h3[key & 0xffu], 1u);
+        }
+      });
+      __syncthreads();
+      find_threshold(s_h3, 256, krem2, wsum[2], sh[2]);
+      thr = (b1 << 20) | (b2 << 8) | sh[2][0];
+      krem_eq = sh[2][1];
+    }
+  }
+  // per chunk: members above thr and equal to it
+  // (predicates below are combined with & and |, not && and ||: no branch per entry)
+  each_block([&](auto& x, auto&, uint32_t nb, int c2, uint32_t) {
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (g * 64 >= (int)nb) break;   // (the rest of the block lies past its members)
+      const uint32_t key = (uint32_t)x[g];
+      const bool v = (uint32_t)(g * 64 + lane) < nb;
+      gt += (uint32_t)__popcll(__ballot(v & (key > thr)));
+      eq += (uint32_t)__popcll(__ballot(v & (key == thr)));
+    }
+    if (lane == 0) {
+      s_gt[c2] += gt;
+      s_eq[c2] += eq;
+    }
+  });
+  __syncthreads();
+  // over the chunks in order: selected members and members at the threshold
+  // before each chunk (sg, se), and in the whole row (s_tot)
+  auto chunk_offsets = [&](uint32_t* sg, uint32_t* se, uint32_t kr) {
+    const uint32_t gt = tid < nact ? sg[tid] : 0u, eq = tid < nact ? se[tid] : 0u;
+    uint32_t eq_before;
+    const uint32_t gt_before = block_excl_scan2(gt, eq, &wsum[2][0], eq_before);
+    if (tid < nact) {
+      sg[tid] = gt_before + (eq_before < kr ? eq_before : kr);
+      se[tid] = eq_before;
+    }
+    if (tid == nact - 1) s_tot = gt_before + gt + (eq_before + eq < kr ? eq_before + eq : kr);
     __syncthreads();
-    if (!s_fine_last) return;
-    TopkArgs f = a;
-    f.scores = r.scores;
-    f.stride = a.k;
-    f.imap = a.idx;
-    f.kc = a.k;
-    f.k = r.ftopk;
-    f.idx = r.fidx;
-    f.score = r.fscore;
-    topk_row_reg_row<8, true, kThreads, false, true>(f, t);
+  };
+  chunk_offsets(s_gt, s_eq, krem_eq);
+  // coarse selection of a block's entries (bit g of the mask): above thr, or
+  // equal to it and among the first krem_eq such in index order; eq_run counts
+  // the members equal to thr before the block
+  auto coarse_kept = [&](auto& x, uint32_t nb, uint32_t& eq_run) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (g * 64 >= (int)nb) break;
+      const uint32_t key = (uint32_t)x[g];
+      const bool v = (uint32_t)(g * 64 + lane) < nb;
+      const bool eq = v & (key == thr);
+      const uint64_t meq = __ballot(eq);
+      const bool sel = (v & (key > thr)) | (eq & (eq_run + lanes_below(meq) < krem_eq));
+      m |= sel ? 1u << g : 0u;
+      eq_run += (uint32_t)__popcll(meq);
+    }
+    return m;
+  };
+  // ---- the candidate list: kept members at their slots (index order), -1 after
+  // them. The fine selection ranks their dense-score keys less the smallest of
+  // the members' (flo); level 1 takes the top 12 of the range's bits. When the
+  // row has fewer than k' visible tokens, its k' - n empty candidate slots take
+  // part with the key of -inf, after every member in slot order.
+  const uint32_t kpad = score_key(-INFINITY);
+  const uint32_t npad = all ? (uint32_t)(a.k - n) : 0u;
+  const uint32_t flo = npad ? min(klo, kpad) : klo, fhi = npad ? max(khi, kpad) : khi;
+  const int nbits = fhi > flo ? 32 - __clz((int)(fhi - flo)) : 0;
+  const int fsh = nbits > 12 ? nbits - 12 : 0;
+  int32_t* const oi = a.idx + t * (int64_t)a.k;
+  uint32_t km[NS];       // (fast) coarse selection of the lane's entries
+  uint32_t fkr[NS][G];   // (fast) their dense-score keys
+  {
+    auto emit = [&](auto& x, auto& fk, uint32_t m, uint32_t nb, uint32_t& sel_run) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if (g * 64 >= (int)nb) break;
+        const bool sel = (m >> g) & 1u;
+        const uint64_t msel = __ballot(sel);
+        const uint32_t pos = sel_run + lanes_below(msel);
+        if (sel & (pos < (uint32_t)a.k)) {   // (every kept member's slot is below k')
+          oi[pos] = (int32_t)(x[g] >> 32);
+          atomicAdd(&lf[(fk[g] - flo) >> fsh], 1u);
+        }
+        sel_run += (uint32_t)__popcll(msel);
+      }
+    };
+    if (fast) {
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2) {
+        const int c2 = wave + s2 * kWaves;
+        km[s2] = 0u;
+        if (c2 < nact) {
+          uint32_t eq_run = s_eq[c2], sel_run = s_gt[c2];
+          km[s2] = coarse_kept(rx[s2], rn[s2], eq_run);
+#pragma unroll
+          for (int g = 0; g < G; ++g) fkr[s2][g] = score_key(rd[s2][g]);
+          emit(rx[s2], fkr[s2], km[s2], rn[s2], sel_run);
+        }
+      }
+    } else {
+      uint32_t eq_run = 0, sel_run = 0;
+      each_block([&](auto& x, auto& d, uint32_t nb, int c2, uint32_t j0) {
+        if (j0 == 0) {
+          eq_run = s_eq[c2];
+          sel_run = s_gt[c2];
+        }
+        const uint32_t m = coarse_kept(x, nb, eq_run);
+        uint32_t fk[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) fk[g] = score_key(d[g]);
+        emit(x, fk, m, nb, sel_run);
+      });
+    }
+  }
+  for (int64_t j = (all ? n : (int64_t)a.k) + tid; j < a.k; j += kThreads) oi[j] = -1;
+  if (tid == 0 && npad) atomicAdd(&lf[(kpad - flo) >> fsh], npad);
+  // body(fk, m, x, nb, c2, j0) for each block: dense keys, coarse selection, members
+  auto each_kept = [&](auto&& body) {
+    if (fast) {
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2)
+        if (wave + s2 * kWaves < nact) body(fkr[s2], km[s2], rx[s2], rn[s2], wave + s2 * kWaves, 0u);
+    } else {
+      uint32_t eq_run = 0;
+      each_block([&](auto& x, auto& d, uint32_t nb, int c2, uint32_t j0) {
+        if (j0 == 0) eq_run = s_eq[c2];
+        const uint32_t m = coarse_kept(x, nb, eq_run);
+        uint32_t fk[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) fk[g] = score_key(d[g]);
+        body(fk, m, x, nb, c2, j0);
+      });
+    }
+  };
+  __syncthreads();
+  // ---- fine threshold: the rule keeps the kept members whose key less flo,
+  // masked by fmask, is above fpre, and of those equal to fpre the first fkrem
+  find_threshold(lf, kBins, (uint32_t)r.ftopk, wsum[0], sh[0]);
+  const uint32_t d0 = sh[0][0];
+  uint32_t fpre = d0 << fsh, fmask = 0xfffu << fsh, fkrem = sh[0][1];
+  // the bin decides when it holds whole keys or is kept whole; otherwise its
+  // keys are ranked among themselves in LDS
+  const bool by_bin = fsh == 0 || sh[0][2];
+  // per chunk: kept members above bin d0 (and, when the bin decides, in it);
+  // the keys of bin d0 listed with their chunk
+  each_kept([&](auto& fk, uint32_t m, auto&, uint32_t nb, int c2, uint32_t) {
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (g * 64 >= (int)nb) break;
+      const uint32_t bin = (fk[g] - flo) >> fsh;
+      const bool kept = (m >> g) & 1u;
+      const bool inb = kept & (bin == d0);
+      gt += (uint32_t)__popcll(__ballot(kept & (bin > d0)));
+      eq += (uint32_t)__popcll(__ballot(inb));
+      if (inb & !by_bin) {
+        const uint32_t s = atomicAdd(&s_nc, 1u);
+        if (s < (uint32_t)kCand) {
+          c_key[s] = fk[g];
+          c_w[s] = 1u;
+          c_ch[s] = (uint32_t)c2;
+        }
+      }
+    }
+    if (lane == 0) {
+      s_fgt[c2] += gt;
+      s_feq[c2] += by_bin ? eq : 0u;
+    }
+  });
+  if (!by_bin && tid == 0 && npad && ((kpad - flo) >> fsh) == d0) {
+    const uint32_t s = atomicAdd(&s_nc, 1u);
+    if (s < (uint32_t)kCand) {
+      c_key[s] = kpad;
+      c_w[s] = npad;
+      c_ch[s] = 0xffffffffu;   // the empty slots: after every chunk
+    }
+  }
+  __syncthreads();
+  if (!by_bin) {
+    const uint32_t nc = s_nc;
+    if (nc <= (uint32_t)kCand) {
+      // the key K with fewer than krem keys of the bin above it and at least
+      // krem at or above it; krem - (keys above K) of those equal to K are kept
+      const uint32_t kr = fkrem;
+      if (tid < (int)nc) {
+        const uint32_t ki = c_key[tid];
+        uint32_t gt = 0, eq = 0;
+        for (uint32_t j = 0; j < nc; ++j) {
+          const uint32_t kj = c_key[j], wj = c_w[j];
+          gt += kj > ki ? wj : 0u;
+          eq += kj == ki ? wj : 0u;
+        }
+        if ((gt < kr) & (kr <= gt + eq)) {
+          s_fthr = ki;
+          s_fkrem = kr - gt;
+        }
+      }
+      __syncthreads();
+      const uint32_t fthr = s_fthr;
+      fpre = fthr - flo;
+      fmask = 0xffffffffu;
+      fkrem = s_fkrem;
+      // each listed key above K or at it counts in its chunk
+      if (tid < (int)nc && c_ch[tid] != 0xffffffffu) {
+        const uint32_t ki = c_key[tid];
+        if (ki > fthr) atomicAdd(&s_fgt[c_ch[tid]], 1u);
+        if (ki == fthr) atomicAdd(&s_feq[c_ch[tid]], 1u);
+      }
+      __syncthreads();
+    } else {
+      // more keys in the bin than the list holds (heavy ties): radix select over
+      // all of the kept members, then their counts per chunk again
+      fkrem = (uint32_t)r.ftopk;
+      bool full;
+      radix_select<kThreads, 1>(
+          [&](auto&& f) {
+            each_kept([&](auto& fk, uint32_t m, auto&, uint32_t, int, uint32_t) {
+#pragma unroll
+              for (int g = 0; g < G; ++g)
+                if ((m >> g) & 1u) f(fk[g] - flo);
+            });
+          },
+          nbits, fpre, fmask, fkrem, full, rs, kpad - flo, npad);
+      if (tid < nact) s_fgt[tid] = 0u;
+      __syncthreads();
+      each_kept([&](auto& fk, uint32_t m, auto&, uint32_t nb, int c2, uint32_t) {
+        uint32_t gt = 0, eq = 0;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          if (g * 64 >= (int)nb) break;
+          const uint32_t v = (fk[g] - flo) & fmask;
+          const bool kept = (m >> g) & 1u;
+          gt += (uint32_t)__popcll(__ballot(kept & (v > fpre)));
+          eq += (uint32_t)__popcll(__ballot(kept & (v == fpre)));
+        }
+        if (lane == 0) {
+          s_fgt[c2] += gt;
+          s_feq[c2] += eq;
+        }
+      });
+      __syncthreads();
+    }
+  }
+  chunk_offsets(s_fgt, s_feq, fkrem);
+  // ---- the final top-k in index order: token ids and dense scores, then -1 / 0
+  int32_t* const fi = r.fidx + t * (int64_t)r.ftopk;
+  float* const fs = r.fscore ? r.fscore + t * (int64_t)r.ftopk : nullptr;
+  {
+    uint32_t feq_run = 0, fsel_run = 0;
+    each_kept([&](auto& fk, uint32_t m, auto& x, uint32_t nb, int c2, uint32_t j0) {
+      if (j0 == 0) {
+        feq_run = s_feq[c2];
+        fsel_run = s_fgt[c2];
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if (g * 64 >= (int)nb) break;
+        const uint32_t v = (fk[g] - flo) & fmask;
+        const bool kept = (m >> g) & 1u;
+        const bool eq = kept & (v == fpre);
+        const uint64_t meq = __ballot(eq);
+        const bool sel = (kept & (v > fpre)) | (eq & (feq_run + lanes_below(meq) < fkrem));
+        const uint64_t msel = __ballot(sel);
+        const uint32_t pos = fsel_run + lanes_below(msel);
+        if (sel & (pos < (uint32_t)r.ftopk)) {
+          fi[pos] = (int32_t)(x[g] >> 32);
+          if (fs) fs[pos] = key_score(fk[g]);
+        }
+        feq_run += (uint32_t)__popcll(meq);
+        fsel_run += (uint32_t)__popcll(msel);
+      }
+    });
+  }
+  // after the selected members (ftopk of them, or fewer when empty candidate
+  // slots were selected)
+  for (int j = (int)s_tot + tid; j < r.ftopk; j += kThreads) {
+    fi[j] = -1;
+    if (fs) fs[j] = 0.f;
   }
 }
 
@@ -529,7 +1063,7 @@ inline int64_t cand_cap(int64_t max_len) { return max_len; }
 size_t split_topk_ws_bytes(int64_t T, int64_t max_len) {
   const int chunk = split_chunk(max_len);
   const int64_t nchunk = (max_len + chunk - 1) / chunk;
-  return al((size_t)T * (2 * kBins + 4) * 4) + al((size_t)T * 8 * 4) + al((size_t)T * nchunk * 4) +
+  return al((size_t)T * (2 * kBins + 4) * 4) + al((size_t)T * 8 * 4) + al((size_t)T * nchunk * 4 * 4) +
          al((size_t)T * cand_cap(max_len) * 8);
 }
 
@@ -546,8 +1080,8 @@ SplitTopkWs split_topk_carve(void* base, int64_t T, int64_t max_len) {
   p += al((size_t)T * (2 * kBins + 4) * 4);
   w.state = reinterpret_cast<uint32_t*>(p);
   p += al((size_t)T * 8 * 4);
-  w.ndef = reinterpret_cast<uint32_t*>(p);
-  p += al((size_t)T * w.nchunk * 4);
+  w.ndef = reinterpret_cast<uint32_t*>(p);   // (and after it, per chunk, three words of the MISA† selection)
+  p += al((size_t)T * w.nchunk * 4 * 4);
   w.cand = reinterpret_cast<uint32_t*>(p);
   return w;
 }
@@ -596,6 +1130,38 @@ hipError_t launch_rescore_e(const TopkArgs& a, const SplitTopkWs& w, const Resco
 hipError_t launch_topk_split_rescore(const TopkArgs& a, const SplitTopkWs& w, const RescoreArgs& r, hipStream_t st) {
   if (a.T == 0) return hipSuccess;
   return w.chunk == kThreads * 4 ? launch_rescore_e<4>(a, w, r, st) : launch_rescore_e<1>(a, w, r, st);
+}
+
+namespace {
+template <int EPT, int D>
+void launch_hier_d(const TopkArgs& a, const SplitTopkWs& w, const RescoreArgs& r, float* mscore, hipStream_t st) {
+  dim3 grid(w.nchunk, (unsigned)a.T);
+  switch ((r.H + 15) / 16) {
+    case 1: hipLaunchKernelGGL((hier_select_kernel<EPT, D, 1>), grid, dim3(kThreads), 0, st, a, w, r, mscore); break;
+    case 2: hipLaunchKernelGGL((hier_select_kernel<EPT, D, 2>), grid, dim3(kThreads), 0, st, a, w, r, mscore); break;
+    case 3: hipLaunchKernelGGL((hier_select_kernel<EPT, D, 3>), grid, dim3(kThreads), 0, st, a, w, r, mscore); break;
+    default: hipLaunchKernelGGL((hier_select_kernel<EPT, D, 4>), grid, dim3(kThreads), 0, st, a, w, r, mscore); break;
+  }
+}
+template <int EPT>
+hipError_t launch_hier_e(const TopkArgs& a, const SplitTopkWs& w, const RescoreArgs& r, float* mscore,
+                         hipStream_t st) {
+  switch (r.d) {
+    case 32: launch_hier_d<EPT, 32>(a, w, r, mscore, st); break;
+    case 64: launch_hier_d<EPT, 64>(a, w, r, mscore, st); break;
+    case 128: launch_hier_d<EPT, 128>(a, w, r, mscore, st); break;
+    case 256: launch_hier_d<EPT, 256>(a, w, r, mscore, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_hier_select(const TopkArgs& a, const SplitTopkWs& w, const RescoreArgs& r, float* mscore,
+                              hipStream_t st) {
+  if (a.T == 0) return hipSuccess;
+  if (a.imap || a.k > 8192 || r.ftopk > a.k) return hipErrorInvalidValue;
+  return w.chunk == kThreads * 4 ? launch_hier_e<4>(a, w, r, mscore, st) : launch_hier_e<1>(a, w, r, mscore, st);
 }
 
 bool split_topk_always_ok(int64_t max_len) { return max_len <= (int64_t)kMaxChunks * kThreads * 4; }
