@@ -103,9 +103,6 @@ __device__ __forceinline__ float load_coherent(const float* p) {
 __device__ __forceinline__ uint32_t atomic_add_coherent(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t atomic_max_coherent(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // Waits until this thread's stores and atomics have completed (the sc1 stores
 // above: reached the memory side). The asm's memory clobber also keeps the
 // compiler from moving memory operations across it.

@@ -100,11 +100,6 @@ struct TopkArgs {
   int64_t len_hi = INT64_MAX;
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t st);
-// The register-resident select of row t by the calling workgroup (EPT * NT
-// slots at most). COH: the row was written earlier in the same launch by other
-// workgroups (device-coherent loads).
-template <int EPT, bool GATHER, int NT, bool MANY, bool COH>
-__device__ void topk_row_reg_row(const TopkArgs& a, int64_t t);
 // Longest row the register-resident single-workgroup top-k handles.
 int64_t topk_row_reg_max();
 

@@ -337,12 +337,8 @@ constexpr int kWinBits = 26;     // window of 2^26 key units: 8 octaves of posit
 constexpr int kBinShift = kWinBits - 12;
 constexpr int kCandCap = 512;    // keys of the threshold bin ranked in LDS
 
-}  // namespace
-
 // The register-resident select of row t (the body of topk_row_reg_kernel).
-// COH: the row (and its token ids) were written earlier in the same launch by
-// other workgroups, so they are read with device-coherent loads.
-template <int EPT, bool GATHER, int NT, bool MANY, bool COH>
+template <int EPT, bool GATHER, int NT, bool MANY>
 __device__ __attribute__((always_inline)) void topk_row_reg_row(const TopkArgs& a, int64_t t) {
   constexpr int NW = NT / 64;
   // the few-rows variants run the fallback in place; the many-rows (MANY) variants
@@ -381,13 +377,8 @@ __device__ __attribute__((always_inline)) void topk_row_reg_row(const TopkArgs& 
       for (int u = 0; u < U; ++u) {
         const int j = j0 + u * NT + tid;
         const int jc = j < nl ? j : 0;
-        if constexpr (COH) {
-          v[u] = nl > 0 ? load_coherent(row + jc) : 0.f;
-          m[u] = (imap && nl > 0) ? (int32_t)load_coherent(reinterpret_cast<const uint32_t*>(imap) + jc) : 0;
-        } else {
-          v[u] = nl > 0 ? row[jc] : 0.f;
-          m[u] = (imap && nl > 0) ? imap[jc] : 0;
-        }
+        v[u] = nl > 0 ? row[jc] : 0.f;
+        m[u] = (imap && nl > 0) ? imap[jc] : 0;
       }
       // all of them consumed from here on (an s_waitcnt the compiler sees: it
       // would otherwise also wait for the stores below before each use)
@@ -442,17 +433,10 @@ __device__ __attribute__((always_inline)) void topk_row_reg_row(const TopkArgs& 
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
     if (j >= nvs) continue;
-    if constexpr (COH) {
-      // (every lane loads from a clamped slot; slots past the row are not used)
-      const int e = base + 64 * j < n ? base + 64 * j : 0;
-      u[j] = load_coherent(reinterpret_cast<const uint32_t*>(row) + e);
-      if constexpr (kPrefetchIds) ids[j] = (int32_t)load_coherent(reinterpret_cast<const uint32_t*>(imap) + e);
-    } else {
-      // raw bits (keys in place below); non-temporal: every score is read once
-      u[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rview, (int)((uint32_t)base * 4u), (int)(256u * j),
-                                                            kNonTemporal);
-      if constexpr (kPrefetchIds) ids[j] = (int32_t)buffer_load_u32(iview, (uint32_t)base * 4u, 256u * j);
-    }
+    // raw bits (keys in place below); non-temporal: every score is read once
+    u[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rview, (int)((uint32_t)base * 4u), (int)(256u * j),
+                                                          kNonTemporal);
+    if constexpr (kPrefetchIds) ids[j] = (int32_t)buffer_load_u32(iview, (uint32_t)base * 4u, 256u * j);
   }
   if (tid == 0) s_m = 0u;
   radix_clear(rs);
@@ -643,14 +627,12 @@ __device__ __attribute__((always_inline)) void topk_row_reg_row(const TopkArgs& 
     oi[0] = kFallbackMark;
 }
 
-namespace {
-
 template <int EPT, bool GATHER, int NT, bool MANY>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(MANY ? 8 : NT / 256))) void topk_row_reg_kernel(
     TopkArgs a) {
   // causal batches: longest rows first, unless the launch takes only the shorter
   // rows (then the rows it leaves alone, the longer ones, come last and fill the tail)
-  topk_row_reg_row<EPT, GATHER, NT, MANY, false>(a, a.len_hi != INT64_MAX ? (int64_t)blockIdx.x
+  topk_row_reg_row<EPT, GATHER, NT, MANY>(a, a.len_hi != INT64_MAX ? (int64_t)blockIdx.x
                                                                         : (int64_t)a.T - 1 - blockIdx.x);
 }
 

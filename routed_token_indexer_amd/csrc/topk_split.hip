@@ -526,8 +526,9 @@ __global__ __launch_bounds__(kThreads) void hier_select_kernel(TopkArgs a, Split
   __shared__ uint32_t s_last, s_mm[2];
   // the last chunk, per chunk: members; coarse and fine counts and offsets
   __shared__ uint32_t s_cnt[kMaxChunks], s_gt[kMaxChunks], s_eq[kMaxChunks], s_fgt[kMaxChunks], s_feq[kMaxChunks];
-  __shared__ uint32_t s_tot, s_nc, s_fthr, s_fkrem;
-  __shared__ uint32_t c_key[kCand], c_w[kCand], c_ch[kCand];   // the fine threshold bin's keys
+  __shared__ uint32_t s_tot, s_nc, s_nc2, s_fthr, s_fkrem;
+  // keys of the coarse threshold sub-bin, then of the fine threshold bin, with their chunks
+  __shared__ uint32_t c_key[kCand], c_w[kCand], c_ch[kCand];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int64_t t = blockIdx.y;
@@ -698,7 +699,10 @@ __global__ __launch_bounds__(kThreads) void hier_select_kernel(TopkArgs a, Split
     lf[tid + k * kThreads] = 0u;
   }
   if (tid < 256) s_h3[tid] = 0u;
-  if (tid == 0) s_nc = 0u;
+  if (tid == 0) {
+    s_nc = 0u;
+    s_nc2 = 0u;
+  }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     klo = min(klo, (uint32_t)__shfl_xor((int)klo, off, kWave));
@@ -743,50 +747,83 @@ __global__ __launch_bounds__(kThreads) void hier_select_kernel(TopkArgs a, Split
     }
   };
   // ---- coarse threshold: the k'-th largest routed key thr, and how many of
-  // the members equal to it are kept (the first krem_eq in index order)
+  // the members equal to it are kept (the first krem_eq in index order); per
+  // chunk, its members above thr (s_gt) and equal to it (s_eq)
+  // (predicates below are combined with & and |, not && and ||: no branch per entry)
   uint32_t thr = 0u, krem_eq = 0xffffffffu;
-  if (!all) {
+  if (all) {
+    if (tid < nact) s_gt[tid] = s_cnt[tid];   // every member is kept
+  } else {
     // level 2: bits 8..19 of the keys of b1 (every one of them is a member)
     find_threshold(lh, kBins, krem1, wsum[0], sh[1]);
     const uint32_t b2 = sh[1][0], krem2 = sh[1][1];
+    const bool whole = sh[1][2] != 0u;   // the threshold sub-bin is kept whole
     for (int i = tid; i < kBins; i += kThreads) lh[i] = 0u;   // for the fine selection's fallback
-    if (sh[1][2]) {
-      thr = (b1 << 20) | (b2 << 8);   // the sub-bin is kept whole
-    } else {
-      // level 3: the low 8 bits of the members in sub-bin b2
-      const uint32_t hi24 = (b1 << 12) | b2;
-      each_block([&](auto& x, auto&, uint32_t nb, int, uint32_t) {
+    const uint32_t hi24 = (b1 << 12) | b2;
+    if (whole) thr = hi24 << 8;
+    // one pass: per chunk, the members above sub-bin b2, and when it is kept
+    // whole those in it too; otherwise the level-3 histogram of the low 8 bits
+    // of its members, which are listed with their chunk
+    each_block([&](auto& x, auto&, uint32_t nb, int c2, uint32_t) {
+      uint32_t gt = 0, eq = 0;
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          if (g * 64 >= (int)nb) break;
-          const uint32_t key = (uint32_t)x[g];
-          if (((uint32_t)(g * 64 + lane) < nb) & ((key >> 8) == hi24)) atomicAdd(&s_h3[key & 0xffu], 1u);
+      for (int g = 0; g < G; ++g) {
+        if (g * 64 >= (int)nb) break;   // (the rest of the block lies past its members)
+        const uint32_t key = (uint32_t)x[g];
+        const bool v = (uint32_t)(g * 64 + lane) < nb;
+        const bool mid = v & ((key >> 8) == hi24);
+        gt += (uint32_t)__popcll(__ballot(v & ((key >> 8) > hi24)));
+        if (whole) {
+          gt += (uint32_t)__popcll(__ballot(mid & (key > thr)));
+          eq += (uint32_t)__popcll(__ballot(mid & (key == thr)));
+        } else if (mid) {
+          atomicAdd(&s_h3[key & 0xffu], 1u);
+          const uint32_t s = atomicAdd(&s_nc2, 1u);
+          if (s < (uint32_t)kCand) {
+            c_key[s] = key & 0xffu;
+            c_ch[s] = (uint32_t)c2;
+          }
         }
-      });
-      __syncthreads();
+      }
+      if (lane == 0) {
+        s_gt[c2] += gt;
+        s_eq[c2] += eq;
+      }
+    });
+    __syncthreads();
+    if (!whole) {
+      // level 3, then each listed member above thr or at it counts in its chunk
       find_threshold(s_h3, 256, krem2, wsum[2], sh[2]);
-      thr = (b1 << 20) | (b2 << 8) | sh[2][0];
+      const uint32_t lo8 = sh[2][0];
+      thr = (hi24 << 8) | lo8;
       krem_eq = sh[2][1];
+      const uint32_t nc2 = s_nc2;
+      if (nc2 <= (uint32_t)kCand) {
+        if (tid < (int)nc2) {
+          if (c_key[tid] > lo8) atomicAdd(&s_gt[c_ch[tid]], 1u);
+          if (c_key[tid] == lo8) atomicAdd(&s_eq[c_ch[tid]], 1u);
+        }
+      } else {
+        // more members in the sub-bin than the list holds (heavy ties): count them again
+        each_block([&](auto& x, auto&, uint32_t nb, int c2, uint32_t) {
+          uint32_t gt = 0, eq = 0;
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            if (g * 64 >= (int)nb) break;
+            const uint32_t key = (uint32_t)x[g];
+            const bool mid = ((uint32_t)(g * 64 + lane) < nb) & ((key >> 8) == hi24);
+            gt += (uint32_t)__popcll(__ballot(mid & (key > thr)));
+            eq += (uint32_t)__popcll(__ballot(mid & (key == thr)));
+          }
+          if (lane == 0) {
+            s_gt[c2] += gt;
+            s_eq[c2] += eq;
+          }
+        });
+      }
+      __syncthreads();
     }
   }
-  // per chunk: members above thr and equal to it
-  // (predicates below are combined with & and |, not && and ||: no branch per entry)
-  each_block([&](auto& x, auto&, uint32_t nb, int c2, uint32_t) {
-    uint32_t gt = 0, eq = 0;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if (g * 64 >= (int)nb) break;   // (the rest of the block lies past its members)
-      const uint32_t key = (uint32_t)x[g];
-      const bool v = (uint32_t)(g * 64 + lane) < nb;
-      gt += (uint32_t)__popcll(__ballot(v & (key > thr)));
-      eq += (uint32_t)__popcll(__ballot(v & (key == thr)));
-    }
-    if (lane == 0) {
-      s_gt[c2] += gt;
-      s_eq[c2] += eq;
-    }
-  });
-  __syncthreads();
   // over the chunks in order: selected members and members at the threshold
   // before each chunk (sg, se), and in the whole row (s_tot)
   auto chunk_offsets = [&](uint32_t* sg, uint32_t* se, uint32_t kr) {
