@@ -588,3 +588,77 @@ def test_fused_indexers_match_separate_calls(case, mode):
         assert torch.equal(i2, i1) and torch.equal(s2, s1)
         assert torch.equal(cand3, cand1)
         assert torch.equal(j3, j1) and torch.equal(t3, t1)
+
+
+def _hier_separate(q, w, k, heads, q_seq, q_len, kc, topk):
+    cand, _ = M.score_topk(q, w, k, heads, q_seq, q_len, kc)
+    idx, sc = M.hier_rerank(q, w, k, cand, q_seq, q_len, topk)
+    return cand, idx, sc
+
+
+@pytest.mark.parametrize("kc,topk,n2,n1", [(4096, 512, 10, 600), (8192, 2048, 20, 3000)])
+def test_fused_hier_heavy_ties(kc, topk, n2, n1):
+    """misa_hier_indexer on keys of three classes: 2, 1 and 0.5 times one positive
+    vector, with positive queries and weights, so that every routed and dense score
+    is tied within its class and the classes keep their order under any routing.
+    The k'-th routed key falls inside class 0.5 and the k-th dense key inside class
+    1: the one-launch selection then meets chunks with more members than its
+    registers hold, a threshold sub-bin and a fine threshold bin of far more than
+    512 keys. The answer is fixed by the tie rule (class, then the lower token
+    index), and the fused call equals the separate calls bit for bit."""
+    x, dev = get("c4x", "grid")
+    c = x.cfg
+    rng = np.random.default_rng(11)
+    cls = np.full((c.nseq, c.L), 0.5, np.float32)
+    for s in range(c.nseq):
+        pos = rng.choice(c.L, size=n2 + n1, replace=False)
+        cls[s, pos[:n2]] = 2.0
+        cls[s, pos[n2:]] = 1.0
+    k = (torch.from_numpy(cls)[:, :, None] * 0.125).expand(c.nseq, c.L, c.d).contiguous().to(torch.bfloat16).cuda()
+    q, w = dev["q"].abs(), dev["w"].abs() + 0.25
+    kbar = M.pool_keys(k, c.B)
+    heads = torch.empty((c.T, c.h), dtype=torch.int32, device="cuda")
+    cand = torch.full((c.T, kc), -7, dtype=torch.int32, device="cuda")
+    idx, sc = M.hier_indexer(q, w, k, kbar, dev["q_seq"], dev["q_len"], c.B, c.h, kc, topk, heads=heads, cand=cand)
+    cand1, idx1, sc1 = _hier_separate(q, w, k, heads, dev["q_seq"], dev["q_len"], kc, topk)
+    torch.cuda.synchronize()
+    assert torch.equal(cand, cand1) and torch.equal(idx, idx1) and torch.equal(sc, sc1)
+    cand, idx, sc = cand.cpu().numpy(), idx.cpu().numpy(), sc.cpu().numpy()
+    for t in range(c.T):
+        s, p = int(x.q_seq[t]), int(min(max(x.q_len[t], 0), c.L))
+        order = np.lexsort((np.arange(p), -cls[s, :p]))   # class descending, then index
+        ec = np.sort(order[:kc])
+        np.testing.assert_array_equal(cand[t][:len(ec)], ec)
+        assert np.all(cand[t][len(ec):] == -1)
+        sub = ec[np.lexsort((ec, -cls[s, ec]))][:topk]
+        np.testing.assert_array_equal(idx[t][:len(sub)], np.sort(sub))
+        # the returned scores are the dense scores of the returned tokens
+        dense = O.routed_scores(np.abs(x.q[t]), np.abs(x.w[t]) + np.float32(0.25), 0.125 * cls[s][:p, None]
+                                * np.ones((1, c.d)), range(c.H), p)
+        np.testing.assert_allclose(sc[t][:len(sub)], dense[np.sort(sub)], rtol=1e-5)
+
+
+def test_fused_hier_short_rows():
+    """misa_hier_indexer on rows shorter than k' (every visible token a candidate,
+    the empty candidate slots taking part in the fine selection as -inf), shorter
+    than k (the output padded with -1 and 0), empty, and full length: equal to the
+    separate calls bit for bit, with the padding in place."""
+    x, dev = get("c4x", "grid")
+    c = x.cfg
+    kc, topk = 4096, 512
+    q_len = dev["q_len"].clone()
+    q_len[0], q_len[1], q_len[2] = 0, 100, 3000
+    kbar = M.pool_keys(dev["k"], c.B)
+    heads = torch.empty((c.T, c.h), dtype=torch.int32, device="cuda")
+    cand = torch.full((c.T, kc), -7, dtype=torch.int32, device="cuda")
+    idx, sc = M.hier_indexer(dev["q"], dev["w"], dev["k"], kbar, dev["q_seq"], q_len, c.B, c.h, kc, topk,
+                             heads=heads, cand=cand)
+    cand1, idx1, sc1 = _hier_separate(dev["q"], dev["w"], dev["k"], heads, dev["q_seq"], q_len, kc, topk)
+    torch.cuda.synchronize()
+    assert torch.equal(cand, cand1) and torch.equal(idx, idx1) and torch.equal(sc, sc1)
+    cand, idx, sc = cand.cpu().numpy(), idx.cpu().numpy(), sc.cpu().numpy()
+    assert np.all(cand[0] == -1) and np.all(idx[0] == -1) and np.all(sc[0] == 0)
+    assert cand[1][:100].tolist() == list(range(100)) and np.all(cand[1][100:] == -1)
+    assert idx[1][:100].tolist() == list(range(100)) and np.all(idx[1][100:] == -1) and np.all(sc[1][100:] == 0)
+    assert cand[2][:3000].tolist() == list(range(3000)) and np.all(cand[2][3000:] == -1)
+    assert np.all(np.diff(idx[2]) > 0) and idx[2][-1] < 3000
