@@ -3,29 +3,34 @@
 //
 // Same selection rule as the per-row kernels (MISA pages: the indexer keeps the
 // top-k tokens of each query; order by score descending, token index
-// ascending; output in ascending token index, -1 padded), computed by launches
-// over (row, chunk) grids:
-//   1. hist     each chunk adds its LDS histogram of the key's top 12 bits into
-//               the row's global histogram (atomics; the decode scoring kernel
-//               usually builds it instead).
-//   2. filter   each chunk reads the finished histogram, finds the threshold
-//               bin b1, counts its keys above b1, appends the keys of bin b1
-//               (key, index) to the row's candidate list and counts their next
-//               12 key bits into the row's level-2 histogram.
-//   3. compact  each chunk resolves the exact threshold key from the level-2
-//               histogram (and, when its threshold bin is not kept whole, the
-//               low 8 bits of that bin's few candidates) and its own output
-//               offset from the candidates' per-chunk counts, then writes its
-//               kept indices in index order from that offset (ballots inside
-//               waves, counts across waves).
-// Each chunk of the compaction works the threshold out for itself (the same
-// result in every chunk), so no chunk waits for another within a launch.
-// The MISA† selection of up to 8192 candidates (hier_select_kernel) takes one
-// launch instead: its chunks hand their members on to the last of them through
+// ascending; output in ascending token index, -1 padded), computed over
+// (row, chunk) grids after a level-1 histogram of each row (the key's top 12
+// bits; the decode scoring kernel usually builds it, else `hist` below):
+//   - up to 256 rows of scores (decode batches): one launch, split_select_kernel.
+//     Each chunk lists its members, the keys in the threshold bin b1 or above it
+//     (a superset of its share of the top-k), and adds their next 12 key bits
+//     to the row's level-2 histogram; the chunk that arrives last on a row
+//     resolves the exact threshold key and writes the row's selection. With RR
+//     (the fused MISA† step, k' <= 8192) every chunk first scores its members
+//     with all heads, and the last chunk also selects the final top-k by those
+//     dense scores.
+//   - more rows, or rows of candidate slots (an index map): two launches.
+//       filter   each chunk finds b1, counts its keys above b1, appends the
+//                keys of b1 (key, index) to the row's candidate list and counts
+//                their next 12 key bits into the row's level-2 histogram;
+//       compact  each chunk resolves the exact threshold key from the level-2
+//                histogram (and, when its threshold sub-bin is not kept whole,
+//                the low 8 bits of that sub-bin's few candidates) and its own
+//                output offset from the candidates' per-chunk counts, then
+//                writes its kept indices in index order from that offset; with
+//                RESCORE (MISA† with k' > 8192) it scores them with all heads.
+//     Every chunk of the compaction works the threshold out for itself, so no
+//     chunk waits for another within a launch.
+// The one-launch form hands the members on to the last chunk through
 // device-coherent stores (sc1: written through to memory, which every XCD's
 // loads with sc1 see) completed before an atomic arrival count; the L2
-// write-back fence that a release would add costs more than the whole selection
-// on gfx950.
+// write-back fence that a release would add costs more than the whole
+// selection on gfx950.
 #include "misa_common.hpp"
 #include "misa_internal.hpp"
 #include "misa_score_dev.hpp"
@@ -39,6 +44,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kBins = kSelBins;
 constexpr int kMaxChunks = 1024;
 constexpr int kCandReg = 8 * kThreads;       // candidates a compaction chunk holds in registers
+constexpr int kOneLaunchRows = 256;          // rows of the one-launch split selection at most
 
 // state[t][*]: the row's level-1 threshold bin, how many of its keys are kept,
 // and how many keys it holds (written by the filter launch's first chunk)
@@ -479,34 +485,37 @@ __global__ __launch_bounds__(kThreads) void split_compact_kernel(TopkArgs a, Spl
   }
 }
 
-// MISA† coarse selection, dense re-scoring and fine selection in one launch
-// (k' <= 8192; one workgroup per (chunk, row), the routed scores' level-1
-// histogram already built by the scoring kernel).
+// The split selection in one launch (one workgroup per (chunk, row), the
+// rows' level-1 histogram already built). Without RR it selects the top-k of
+// the rows (k = a.k) and writes it with its scores. With RR it is the MISA†
+// step: coarse top-k' (k' = a.k <= 8192), dense re-scoring and fine top-k:
 //   - Members of a chunk: for a row of more than k' visible tokens, its keys in
 //     the level-1 threshold bin b1 or above it. That is a superset of the
 //     chunk's share of the exact top-k': all the keys above b1 are in it, and of
 //     the keys of b1 only krem1 are. For a row of at most k' tokens, every
 //     visible token is a member and is kept.
-//   - Each chunk scores its members with all H heads and stores them in index
-//     order as (index, routed key) and dense score in its own region of the
-//     row's member lists; it adds key bits 8..19 of its members in b1 to the
-//     row's level-2 histogram and its members' dense-key range to the row's,
-//     stores its member count and counts its arrival (everything written
-//     through before the count).
+//   - Each chunk (RR: scores its members with all H heads and) stores them in
+//     index order as (index, routed key) (RR: and dense score) in its own region
+//     of the row's member lists; it adds key bits 8..19 of its members in b1 to
+//     the row's level-2 histogram, stores its member count (RR: and dense-key
+//     range) and counts its arrival (everything written through before the
+//     count).
 //   - The chunk that arrives last resolves the exact top-k' among the members
 //     (level 2 from the histogram, level 3 over the members of the threshold
 //     sub-bin): the kept ones are above the threshold key, or equal to it and
-//     among the first krem in index order. It writes their indices as the
+//     among the first krem in index order. Without RR it writes them, with their
+//     scores, as the row's selection. With RR it writes their indices as the
 //     candidate list (ascending, -1 padded to k') and selects the final top-k
 //     among them by dense score out of registers: a histogram of the dense keys
 //     over their range, then the few keys of the threshold bin ranked in LDS.
-// Compared with the filter and compaction launches and a fine-stage select,
-// this saves a launch, the exact threshold's round before the re-scoring and
-// the candidate list's round trip through memory. The price is re-scoring the
-// members of b1 that are not kept, usually a few thousand keys of a 128K row.
-template <int EPT, int D, int RT>
-__global__ __launch_bounds__(kThreads) void hier_select_kernel(TopkArgs a, SplitTopkWs w, RescoreArgs r,
-                                                               float* mscore) {
+// Compared with the filter and compaction launches (and for RR a fine-stage
+// select), this saves a launch, (RR: the exact threshold's round before the
+// re-scoring and the candidate list's round trip through memory). The price is
+// the single workgroup per row that finishes, and with RR re-scoring the members
+// of b1 that are not kept, usually a few thousand keys of a 128K row.
+template <int EPT, int D, int RT, bool RR>
+__global__ __launch_bounds__(kThreads) void split_select_kernel(TopkArgs a, SplitTopkWs w, RescoreArgs r,
+                                                                float* mscore) {
   constexpr int CH = kThreads * EPT;
   constexpr int LDQ = D + 8;    // padded row stride of the staged query rows (bf16)
   constexpr int G = 8, NS = 2;  // last chunk: members per lane and chunk in registers, chunks per wave
@@ -515,20 +524,21 @@ __global__ __launch_bounds__(kThreads) void hier_select_kernel(TopkArgs a, Split
   // and the fine selection's fallback
   __shared__ __attribute__((aligned(16))) RadixScratch<kThreads, 1> rs;
   uint32_t* const lh = rs.hist[0];
-  __shared__ uint32_t lf[kBins];   // the fine level 1
+  __shared__ uint32_t lf[RR ? kBins : 1];   // the fine level 1
   __shared__ uint32_t s_h3[256];
   __shared__ uint32_t sh[3][4];
   __shared__ __attribute__((aligned(16))) uint32_t wsum[4][kWaves];
   __shared__ uint32_t wcnt[kWaves];
-  __shared__ int s_tok[CH];
-  __shared__ __attribute__((aligned(16))) uint16_t s_q[16 * RT * LDQ];
-  __shared__ float s_w[16 * RT];
+  __shared__ int s_tok[RR ? CH : 1];
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[RR ? 16 * RT * LDQ : 8];
+  __shared__ float s_w[RR ? 16 * RT : 1];
   __shared__ uint32_t s_last, s_mm[2];
   // the last chunk, per chunk: members; coarse and fine counts and offsets
-  __shared__ uint32_t s_cnt[kMaxChunks], s_gt[kMaxChunks], s_eq[kMaxChunks], s_fgt[kMaxChunks], s_feq[kMaxChunks];
+  __shared__ uint32_t s_cnt[kMaxChunks], s_gt[kMaxChunks], s_eq[kMaxChunks];
+  __shared__ uint32_t s_fgt[RR ? kMaxChunks : 1], s_feq[RR ? kMaxChunks : 1];
   __shared__ uint32_t s_tot, s_nc, s_nc2, s_fthr, s_fkrem;
   // keys of the coarse threshold sub-bin, then of the fine threshold bin, with their chunks
-  __shared__ uint32_t c_key[kCand], c_w[kCand], c_ch[kCand];
+  __shared__ uint32_t c_key[kCand], c_w[RR ? kCand : 1], c_ch[kCand];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int64_t t = blockIdx.y;
@@ -540,21 +550,25 @@ __global__ __launch_bounds__(kThreads) void hier_select_kernel(TopkArgs a, Split
   const int64_t e0 = (int64_t)c * CH;
   const bool all = n <= a.k;   // every visible token is a candidate
 
-  // ---- every request at once: query rows and weights, the chunk's routed
-  // scores, the row's level-1 histogram
-  const int seq = a.q_seq[t];
-  const uint16_t* kseq = r.k + (int64_t)((seq >= 0 && seq < a.nseq) ? seq : 0) * a.Lmax * D + grp * 8;
+  // ---- every request at once: query rows and weights (RR), the chunk's
+  // routed scores, the row's level-1 histogram
+  const uint16_t* kseq = nullptr;
   constexpr int PIECES = 16 * RT * D / 8;   // 16-byte pieces of the padded row block
   constexpr int QPT = (PIECES + kThreads - 1) / kThreads;
   u32x4 qv[QPT];
+  float wq = 0.f;
+  if constexpr (RR) {
+    const int seq = a.q_seq[t];
+    kseq = r.k + (int64_t)((seq >= 0 && seq < a.nseq) ? seq : 0) * a.Lmax * D + grp * 8;
 #pragma unroll
-  for (int k = 0; k < QPT; ++k) {   // (clamped addresses; rows past H are zeroed when staged)
-    const int i = tid + k * kThreads;
-    const int rr = i / (D / 8), cc = (i % (D / 8)) * 8;
-    const bool ok = i < PIECES && rr < r.H;
-    qv[k] = *reinterpret_cast<const u32x4*>(r.q + (t * r.H + (ok ? rr : 0)) * D + (ok ? cc : 0));
+    for (int k = 0; k < QPT; ++k) {   // (clamped addresses; rows past H are zeroed when staged)
+      const int i = tid + k * kThreads;
+      const int rr = i / (D / 8), cc = (i % (D / 8)) * 8;
+      const bool ok = i < PIECES && rr < r.H;
+      qv[k] = *reinterpret_cast<const u32x4*>(r.q + (t * r.H + (ok ? rr : 0)) * D + (ok ? cc : 0));
+    }
+    wq = r.w[t * r.H + (tid < r.H ? tid : 0)];
   }
-  const float wq = r.w[t * r.H + (tid < r.H ? tid : 0)];
   uint32_t u[EPT];
   bool in[EPT];
   load_chunk<EPT>(a.scores + t * a.stride, e0, n, u, in);
@@ -594,7 +608,7 @@ __global__ __launch_bounds__(kThreads) void hier_select_kernel(TopkArgs a, Split
   }
   const int64_t cap = w.cap;
   uint64_t* const mlist = reinterpret_cast<uint64_t*>(w.cand) + t * cap;
-  float* const mrow = mscore + t * cap;
+  float* const mrow = RR ? mscore + t * cap : nullptr;
   uint32_t* const h2 = w.hist2 + t * kBins;
   const uint64_t lt = (1ull << lane) - 1ull;
   const int64_t base = e0 + (int64_t)wave * 64 * EPT + lane;
@@ -603,49 +617,53 @@ __global__ __launch_bounds__(kThreads) void hier_select_kernel(TopkArgs a, Split
     const uint64_t mk = __ballot(mem[j]);
     const uint32_t pos = run + (uint32_t)__popcll(mk & lt);
     if (mem[j]) {
-      s_tok[pos] = (int)(base + 64 * j);
+      if constexpr (RR) s_tok[pos] = (int)(base + 64 * j);
       store_coherent(mlist + e0 + pos, ((uint64_t)(uint32_t)(base + 64 * j) << 32) | u[j]);
       if (!all && (u[j] >> 20) == b1) (void)atomic_add_coherent(h2 + ((u[j] >> 8) & 0xfffu), 1u);
     }
     run += (uint32_t)__popcll(mk);
   }
+  if constexpr (RR) {
 #pragma unroll
-  for (int k = 0; k < QPT; ++k) {
-    const int i = tid + k * kThreads;
-    const int rr = i / (D / 8), cc = (i % (D / 8)) * 8;
-    if (i < PIECES) *reinterpret_cast<u32x4*>(s_q + rr * LDQ + cc) = rr < r.H ? qv[k] : u32x4{0u, 0u, 0u, 0u};
-  }
-  if (tid < 16 * RT) s_w[tid] = tid < r.H ? wq : 0.f;
-  __syncthreads();
+    for (int k = 0; k < QPT; ++k) {
+      const int i = tid + k * kThreads;
+      const int rr = i / (D / 8), cc = (i % (D / 8)) * 8;
+      if (i < PIECES) *reinterpret_cast<u32x4*>(s_q + rr * LDQ + cc) = rr < r.H ? qv[k] : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (tid < 16 * RT) s_w[tid] = tid < r.H ? wq : 0.f;
+    __syncthreads();
 
-  // ---- dense scores of the members, one 16-key tile per wave, and their key range
-  uint32_t mlo = 0xffffffffu, mhi = 0u;
-  for (int b = wave * 16; b < (int)nsel; b += kWaves * 16) {
-    KeyTiles<D, 1> tile;
-    load_key_tiles<D, 1>(kseq, b, (int)nsel, col, [&](int s) { return s_tok[s]; }, 0, tile);
-    const float v = score_one_tile_lds<D, RT>(s_q, LDQ, s_w, tile, grp, col);
-    if (grp == 0 && b + col < (int)nsel) {
-      store_coherent(mrow + e0 + b + col, v);
-      mlo = min(mlo, score_key(v));
-      mhi = max(mhi, score_key(v));
+    // ---- dense scores of the members, one 16-key tile per wave, and their key range
+    uint32_t mlo = 0xffffffffu, mhi = 0u;
+    for (int b = wave * 16; b < (int)nsel; b += kWaves * 16) {
+      KeyTiles<D, 1> tile;
+      load_key_tiles<D, 1>(kseq, b, (int)nsel, col, [&](int s) { return s_tok[s]; }, 0, tile);
+      const float v = score_one_tile_lds<D, RT>(s_q, LDQ, s_w, tile, grp, col);
+      if (grp == 0 && b + col < (int)nsel) {
+        store_coherent(mrow + e0 + b + col, v);
+        mlo = min(mlo, score_key(v));
+        mhi = max(mhi, score_key(v));
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      mlo = min(mlo, (uint32_t)__shfl_xor((int)mlo, off, kWave));
+      mhi = max(mhi, (uint32_t)__shfl_xor((int)mhi, off, kWave));
+    }
+    if (lane == 0) {
+      atomicMin(&s_mm[0], mlo);
+      atomicMax(&s_mm[1], mhi);
     }
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    mlo = min(mlo, (uint32_t)__shfl_xor((int)mlo, off, kWave));
-    mhi = max(mhi, (uint32_t)__shfl_xor((int)mhi, off, kWave));
-  }
-  if (lane == 0) {
-    atomicMin(&s_mm[0], mlo);
-    atomicMax(&s_mm[1], mhi);
-  }
-  // per chunk: member count, smallest and largest dense key
+  // per chunk: member count (RR: and the smallest and largest dense key)
   uint32_t* const cinfo = w.ndef + (int64_t)a.T * w.nchunk + (t * w.nchunk) * 3;
-  __syncthreads();
+  if constexpr (RR) __syncthreads();
   if (tid == 0) {
     store_coherent(cinfo + 3 * c, nsel);
-    store_coherent(cinfo + 3 * c + 1, s_mm[0]);
-    store_coherent(cinfo + 3 * c + 2, s_mm[1]);
+    if constexpr (RR) {
+      store_coherent(cinfo + 3 * c + 1, s_mm[0]);
+      store_coherent(cinfo + 3 * c + 2, s_mm[1]);
+    }
   }
   // ---- arrival: this chunk's members, count and range are in memory before it counts
   wait_stores();
@@ -665,8 +683,8 @@ __global__ __launch_bounds__(kThreads) void hier_select_kernel(TopkArgs a, Split
   // registers (loaded with the counts, before the counts are known); otherwise
   // every pass loads them again.
   const uint32_t cnt_l = tid < nact ? load_coherent(cinfo + 3 * tid) : 0u;
-  uint32_t klo = tid < nact ? load_coherent(cinfo + 3 * tid + 1) : 0xffffffffu;
-  uint32_t khi = tid < nact ? load_coherent(cinfo + 3 * tid + 2) : 0u;
+  uint32_t klo = RR && tid < nact ? load_coherent(cinfo + 3 * tid + 1) : 0xffffffffu;
+  uint32_t khi = RR && tid < nact ? load_coherent(cinfo + 3 * tid + 2) : 0u;
   uint32_t h2v[HPT];
 #pragma unroll
   for (int k = 0; k < HPT; ++k) h2v[k] = all ? 0u : load_coherent(h2 + tid + k * kThreads);
@@ -682,7 +700,7 @@ __global__ __launch_bounds__(kThreads) void hier_select_kernel(TopkArgs a, Split
       slot = slot < slot_max ? slot : slot_max;
       if (c2 < nact) {
         rx[s2][g] = load_coherent(mlist + slot);
-        rd[s2][g] = load_coherent(mrow + slot);
+        if constexpr (RR) rd[s2][g] = load_coherent(mrow + slot);
       }
     }
   }
@@ -690,27 +708,31 @@ __global__ __launch_bounds__(kThreads) void hier_select_kernel(TopkArgs a, Split
     s_cnt[tid] = cnt_l;
     s_gt[tid] = 0u;
     s_eq[tid] = 0u;
-    s_fgt[tid] = 0u;
-    s_feq[tid] = 0u;
+    if constexpr (RR) {
+      s_fgt[tid] = 0u;
+      s_feq[tid] = 0u;
+    }
   }
 #pragma unroll
   for (int k = 0; k < HPT; ++k) {
     lh[tid + k * kThreads] = h2v[k];
-    lf[tid + k * kThreads] = 0u;
+    if constexpr (RR) lf[tid + k * kThreads] = 0u;
   }
   if (tid < 256) s_h3[tid] = 0u;
   if (tid == 0) {
     s_nc = 0u;
     s_nc2 = 0u;
   }
+  if constexpr (RR) {
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    klo = min(klo, (uint32_t)__shfl_xor((int)klo, off, kWave));
-    khi = max(khi, (uint32_t)__shfl_xor((int)khi, off, kWave));
-  }
-  if (lane == 0 && khi >= klo) {
-    atomicMin(&s_mm[0], klo);
-    atomicMax(&s_mm[1], khi);
+    for (int off = 32; off > 0; off >>= 1) {
+      klo = min(klo, (uint32_t)__shfl_xor((int)klo, off, kWave));
+      khi = max(khi, (uint32_t)__shfl_xor((int)khi, off, kWave));
+    }
+    if (lane == 0 && khi >= klo) {
+      atomicMin(&s_mm[0], klo);
+      atomicMax(&s_mm[1], khi);
+    }
   }
   uint32_t nbig;
   (void)block_excl_scan(cnt_l > 64u * G ? 1u : 0u, wsum[1], nbig);   // (its barrier publishes the above)
@@ -739,7 +761,7 @@ __global__ __launch_bounds__(kThreads) void hier_select_kernel(TopkArgs a, Split
             const uint32_t j = j0 + (uint32_t)(g * 64 + lane);
             const int64_t slot = j < cn ? (int64_t)c2 * CH + j : 0;
             x[g] = load_coherent(mlist + slot);
-            d[g] = load_coherent(mrow + slot);
+            if constexpr (RR) d[g] = load_coherent(mrow + slot);
           }
           body(x, d, cn - j0, c2, j0);
         }
@@ -856,6 +878,50 @@ __global__ __launch_bounds__(kThreads) void hier_select_kernel(TopkArgs a, Split
     }
     return m;
   };
+  if constexpr (!RR) {
+    // ---- the selection: kept members at their output slots (index order) with
+    // their scores, then -1 and 0
+    int32_t* const oi = a.idx + t * (int64_t)a.k;
+    float* const os = a.score ? a.score + t * (int64_t)a.k : nullptr;
+    auto emit = [&](auto& x, uint32_t m, uint32_t nb, uint32_t& sel_run) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        if (g * 64 >= (int)nb) break;
+        const bool sel = (m >> g) & 1u;
+        const uint64_t msel = __ballot(sel);
+        const uint32_t pos = sel_run + lanes_below(msel);
+        if (sel & (pos < (uint32_t)a.k)) {   // (every kept member's slot is below k)
+          oi[pos] = (int32_t)(x[g] >> 32);
+          if (os) os[pos] = key_score((uint32_t)x[g]);
+        }
+        sel_run += (uint32_t)__popcll(msel);
+      }
+    };
+    if (fast) {
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2) {
+        const int c2 = wave + s2 * kWaves;
+        if (c2 < nact) {
+          uint32_t eq_run = s_eq[c2], sel_run = s_gt[c2];
+          emit(rx[s2], coarse_kept(rx[s2], rn[s2], eq_run), rn[s2], sel_run);
+        }
+      }
+    } else {
+      uint32_t eq_run = 0, sel_run = 0;
+      each_block([&](auto& x, auto&, uint32_t nb, int c2, uint32_t j0) {
+        if (j0 == 0) {
+          eq_run = s_eq[c2];
+          sel_run = s_gt[c2];
+        }
+        emit(x, coarse_kept(x, nb, eq_run), nb, sel_run);
+      });
+    }
+    for (int64_t j = (all ? n : (int64_t)a.k) + tid; j < a.k; j += kThreads) {
+      oi[j] = -1;
+      if (os) os[j] = 0.f;
+    }
+    return;
+  }
   // ---- the candidate list: kept members at their slots (index order), -1 after
   // them. The fine selection ranks their dense-score keys less the smallest of
   // the members' (flo); level 1 takes the top 12 of the range's bits. When the
@@ -1127,14 +1193,25 @@ hipError_t launch_topk_split(const TopkArgs& a, const SplitTopkWs& w, bool hist_
   if (a.T == 0) return hipSuccess;
   dim3 grid(w.nchunk, (unsigned)a.T);
   RescoreArgs none{};
+  // rows of scores in place (not of candidate slots), up to kOneLaunchRows of
+  // them: one launch after the histogram, its last workgroup per row selecting
+  const bool one = !a.imap && a.T <= kOneLaunchRows;
   if (w.chunk == kThreads * 4) {
     if (!hist_done) hipLaunchKernelGGL(split_hist_kernel<4>, grid, dim3(kThreads), 0, st, a, w);
-    hipLaunchKernelGGL(split_filter_kernel<4>, grid, dim3(kThreads), 0, st, a, w);
-    hipLaunchKernelGGL((split_compact_kernel<4, 32, 1, false>), grid, dim3(kThreads), 0, st, a, w, none);
+    if (one) {
+      hipLaunchKernelGGL((split_select_kernel<4, 32, 1, false>), grid, dim3(kThreads), 0, st, a, w, none, nullptr);
+    } else {
+      hipLaunchKernelGGL(split_filter_kernel<4>, grid, dim3(kThreads), 0, st, a, w);
+      hipLaunchKernelGGL((split_compact_kernel<4, 32, 1, false>), grid, dim3(kThreads), 0, st, a, w, none);
+    }
   } else {
     if (!hist_done) hipLaunchKernelGGL(split_hist_kernel<1>, grid, dim3(kThreads), 0, st, a, w);
-    hipLaunchKernelGGL(split_filter_kernel<1>, grid, dim3(kThreads), 0, st, a, w);
-    hipLaunchKernelGGL((split_compact_kernel<1, 32, 1, false>), grid, dim3(kThreads), 0, st, a, w, none);
+    if (one) {
+      hipLaunchKernelGGL((split_select_kernel<1, 32, 1, false>), grid, dim3(kThreads), 0, st, a, w, none, nullptr);
+    } else {
+      hipLaunchKernelGGL(split_filter_kernel<1>, grid, dim3(kThreads), 0, st, a, w);
+      hipLaunchKernelGGL((split_compact_kernel<1, 32, 1, false>), grid, dim3(kThreads), 0, st, a, w, none);
+    }
   }
   return hipGetLastError();
 }
@@ -1174,10 +1251,10 @@ template <int EPT, int D>
 void launch_hier_d(const TopkArgs& a, const SplitTopkWs& w, const RescoreArgs& r, float* mscore, hipStream_t st) {
   dim3 grid(w.nchunk, (unsigned)a.T);
   switch ((r.H + 15) / 16) {
-    case 1: hipLaunchKernelGGL((hier_select_kernel<EPT, D, 1>), grid, dim3(kThreads), 0, st, a, w, r, mscore); break;
-    case 2: hipLaunchKernelGGL((hier_select_kernel<EPT, D, 2>), grid, dim3(kThreads), 0, st, a, w, r, mscore); break;
-    case 3: hipLaunchKernelGGL((hier_select_kernel<EPT, D, 3>), grid, dim3(kThreads), 0, st, a, w, r, mscore); break;
-    default: hipLaunchKernelGGL((hier_select_kernel<EPT, D, 4>), grid, dim3(kThreads), 0, st, a, w, r, mscore); break;
+    case 1: hipLaunchKernelGGL((split_select_kernel<EPT, D, 1, true>), grid, dim3(kThreads), 0, st, a, w, r, mscore); break;
+    case 2: hipLaunchKernelGGL((split_select_kernel<EPT, D, 2, true>), grid, dim3(kThreads), 0, st, a, w, r, mscore); break;
+    case 3: hipLaunchKernelGGL((split_select_kernel<EPT, D, 3, true>), grid, dim3(kThreads), 0, st, a, w, r, mscore); break;
+    default: hipLaunchKernelGGL((split_select_kernel<EPT, D, 4, true>), grid, dim3(kThreads), 0, st, a, w, r, mscore); break;
   }
 }
 template <int EPT>
