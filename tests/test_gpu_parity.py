@@ -662,3 +662,30 @@ def test_fused_hier_short_rows():
     assert idx[1][:100].tolist() == list(range(100)) and np.all(idx[1][100:] == -1) and np.all(sc[1][100:] == 0)
     assert cand[2][:3000].tolist() == list(range(3000)) and np.all(cand[2][3000:] == -1)
     assert np.all(np.diff(idx[2]) > 0) and idx[2][-1] < 3000
+
+
+@pytest.mark.parametrize("topk", [1, 1000, 40001])
+def test_split_forms_agree(topk):
+    """Rows above 32K scores take the one-launch split selection in batches of at
+    most 256 rows and the filter and compaction launches beyond: the same queries
+    selected in one batch of 300 rows and in two of 150 give the same indices and
+    scores bit for bit (MISA and dense)."""
+    x = make_inputs("c1m", mode="grid", L=40001, T=300, topk=1000)
+    dev = upload(x)
+    c = x.cfg
+    kbar = M.pool_keys(dev["k"], c.B)
+    hd = M.route(dev["q"], dev["w"], dev["k"], kbar, dev["q_seq"], dev["q_len"], c.B, c.h)
+    halves = [slice(0, 150), slice(150, 300)]
+    i_all, s_all = M.score_topk(dev["q"], dev["w"], dev["k"], hd, dev["q_seq"], dev["q_len"], topk)
+    d_all, e_all = M.dsa_index_dense(dev["q"], dev["w"], dev["k"], dev["q_seq"], dev["q_len"], topk)
+    for sl in halves:
+        args = [t[sl].contiguous() for t in (dev["q"], dev["w"])]
+        qs, ql = dev["q_seq"][sl].contiguous(), dev["q_len"][sl].contiguous()
+        i_h, s_h = M.score_topk(args[0], args[1], dev["k"], hd[sl].contiguous(), qs, ql, topk)
+        d_h, e_h = M.dsa_index_dense(args[0], args[1], dev["k"], qs, ql, topk)
+        torch.cuda.synchronize()
+        assert torch.equal(i_h, i_all[sl]) and torch.equal(s_h, s_all[sl])
+        assert torch.equal(d_h, d_all[sl]) and torch.equal(e_h, e_all[sl])
+    # and one row against the oracle
+    oi, _ = O.score_topk(x.q, x.w, x.k, hd.cpu().numpy()[:1], x.q_seq, x.q_len, topk, queries=[0])
+    np.testing.assert_array_equal(i_all.cpu().numpy()[0], oi[0])
