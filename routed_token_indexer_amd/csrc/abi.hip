@@ -83,7 +83,7 @@ size_t pivot_head_bytes(int64_t ng, int32_t H, int32_t kc) {
 // rows, then (for few long rows) the split top-k's state.
 size_t select_ws_bytes(int64_t T, int64_t max_len) {
   size_t b = round_up((size_t)T * (size_t)max_len * sizeof(float));
-  if (misa::use_split_topk(T, max_len)) b += round_up(misa::split_topk_ws_bytes(T, max_len));
+  if (misa::use_split_topk(T, max_len, true)) b += round_up(misa::split_topk_ws_bytes(T, max_len));
   return b;
 }
 
@@ -398,7 +398,7 @@ int32_t score_and_select(const char* fn, const void* q, const float* w, const vo
   const int64_t max_len = gather ? kc : Lmax;
   const bool wide = !gather && wide_tiles(T, nseq);
   const bool few = !gather && few_tiles(T, nseq);
-  const bool split = idx && misa::use_split_topk(T, max_len);
+  const bool split = idx && misa::use_split_topk(T, max_len, !gather && !wide && !few);
   misa::SplitTopkWs sw{};
   hipError_t e = hipSuccess;
   if (split) {
@@ -541,7 +541,7 @@ int32_t run_indexer(const char* fn, bool hier, const void* q, const float* w, co
   FusedLayout f = fused_layout(T, H, Lmax, B, hier ? kc : 0, ws);
   // coarse selection: split over chunks for long rows (MISA† always: its
   // compaction also re-scores the kept tokens); one workgroup per row otherwise
-  const bool coarse_split = hier || misa::use_split_topk(T, Lmax);
+  const bool coarse_split = hier || misa::use_split_topk(T, Lmax, true);
   const bool fine_split = hier && kc > misa::topk_row_reg_max();
   // 1. router partials (+ partial-block dots), clearing the top-k state of the later launches
   misa::RouteArgs ra{};

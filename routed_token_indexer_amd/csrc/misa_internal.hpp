@@ -123,7 +123,8 @@ SplitTopkWs split_topk_carve(void* base, int64_t T, int64_t max_len);
 // Words at the start of the carved region that must be zero before the launch.
 int64_t split_topk_zero_words(int64_t T);
 hipError_t launch_zero(uint32_t* p, int64_t words, hipStream_t st);
-bool use_split_topk(int64_t T, int64_t max_len);
+// hist_in_scoring: the scoring kernel builds the rows' level-1 histogram.
+bool use_split_topk(int64_t T, int64_t max_len, bool hist_in_scoring);
 // hist_done: the level-1 histogram was already accumulated by the scoring kernel.
 hipError_t launch_topk_split(const TopkArgs& a, const SplitTopkWs& w, bool hist_done, hipStream_t st);
 // rows of this length can always take the split path (whatever T)

@@ -45,6 +45,7 @@ constexpr int kBins = kSelBins;
 constexpr int kMaxChunks = 1024;
 constexpr int kCandReg = 8 * kThreads;       // candidates a compaction chunk holds in registers
 constexpr int kOneLaunchRows = 256;          // rows of the one-launch split selection at most
+constexpr int kSplitShortRows = 64;          // rows at most for the split selection of rows <= 32K
 
 // state[t][*]: the row's level-1 threshold bin, how many of its keys are kept,
 // and how many keys it holds (written by the filter launch's first chunk)
@@ -1154,9 +1155,13 @@ inline size_t al(size_t x) { return (x + 255) / 256 * 256; }
 
 }  // namespace
 
-bool use_split_topk(int64_t T, int64_t max_len) {
-  // shorter rows are selected by one workgroup each, out of registers
-  return T <= 4096 && max_len > topk_row_reg_max() && max_len <= (int64_t)kMaxChunks * kThreads * 4;
+bool use_split_topk(int64_t T, int64_t max_len, bool hist_in_scoring) {
+  if (T > 4096 || max_len > (int64_t)kMaxChunks * kThreads * 4) return false;
+  if (max_len > topk_row_reg_max()) return true;
+  // rows of 16K..32K scores in a small batch whose histogram the scoring kernel
+  // builds: the one-launch selection over chunks beats a workgroup per row;
+  // shorter rows, or rows needing a histogram launch, take one workgroup each
+  return hist_in_scoring && T <= kSplitShortRows && max_len > 16384;
 }
 
 int64_t split_topk_zero_words(int64_t T) { return (int64_t)(al((size_t)T * (2 * kBins + 4) * 4) / 4); }
@@ -1198,20 +1203,20 @@ hipError_t launch_topk_split(const TopkArgs& a, const SplitTopkWs& w, bool hist_
   const bool one = !a.imap && a.T <= kOneLaunchRows;
   if (w.chunk == kThreads * 4) {
     if (!hist_done) hipLaunchKernelGGL(split_hist_kernel<4>, grid, dim3(kThreads), 0, st, a, w);
-    if (one) {
-      hipLaunchKernelGGL((split_select_kernel<4, 32, 1, false>), grid, dim3(kThreads), 0, st, a, w, none, nullptr);
-    } else {
-      hipLaunchKernelGGL(split_filter_kernel<4>, grid, dim3(kThreads), 0, st, a, w);
-      hipLaunchKernelGGL((split_compact_kernel<4, 32, 1, false>), grid, dim3(kThreads), 0, st, a, w, none);
-    }
   } else {
     if (!hist_done) hipLaunchKernelGGL(split_hist_kernel<1>, grid, dim3(kThreads), 0, st, a, w);
-    if (one) {
-      hipLaunchKernelGGL((split_select_kernel<1, 32, 1, false>), grid, dim3(kThreads), 0, st, a, w, none, nullptr);
-    } else {
-      hipLaunchKernelGGL(split_filter_kernel<1>, grid, dim3(kThreads), 0, st, a, w);
-      hipLaunchKernelGGL((split_compact_kernel<1, 32, 1, false>), grid, dim3(kThreads), 0, st, a, w, none);
-    }
+  }
+  if (one) {
+    // chunks of 4096 scores whatever the histogram's chunking: fewer members
+    // for the last workgroup to gather (chunk indices stay below w.nchunk)
+    dim3 g4((unsigned)((w.nchunk * (int64_t)w.chunk + kThreads * 4 - 1) / (kThreads * 4)), (unsigned)a.T);
+    hipLaunchKernelGGL((split_select_kernel<4, 32, 1, false>), g4, dim3(kThreads), 0, st, a, w, none, nullptr);
+  } else if (w.chunk == kThreads * 4) {
+    hipLaunchKernelGGL(split_filter_kernel<4>, grid, dim3(kThreads), 0, st, a, w);
+    hipLaunchKernelGGL((split_compact_kernel<4, 32, 1, false>), grid, dim3(kThreads), 0, st, a, w, none);
+  } else {
+    hipLaunchKernelGGL(split_filter_kernel<1>, grid, dim3(kThreads), 0, st, a, w);
+    hipLaunchKernelGGL((split_compact_kernel<1, 32, 1, false>), grid, dim3(kThreads), 0, st, a, w, none);
   }
   return hipGetLastError();
 }
