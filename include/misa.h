@@ -244,7 +244,7 @@ MISA_API int32_t misa_hier_indexer(const void* q, const float* w, const void* k,
  *  - Sizes whose workspace (misa_workspace_bytes(MISA_OP_HIER_INDEXER, ...))
  *    exceeds MISA_SCRATCH_BYTES are refused with MISA_ERR_WORKSPACE before
  *    anything is enqueued (decode batches fit: 4 x 128K tokens need about
- *    7 MiB; a long causal prefill does not).
+ *    9 MiB; a long causal prefill does not).
  *  - The scratch belongs to the GPU of `stream` (NULL: the current device). Its
  *    address is looked up once per device, on the first call there. Every call
  *    on a GPU shares that GPU's array and leaves its contents behind; each call
