@@ -109,7 +109,7 @@ struct SplitTopkWs {
   uint32_t* hist;      // [T][4096] level-1 histogram (zero on entry; bin b at word hist_word(b))
   uint32_t* hist2;     // [T][4096] key bits 8..19 of the level-1 threshold bin's keys (zero on entry)
   uint32_t* state;     // [T][8] level-1 threshold bin, how many of its keys are kept, how many it holds
-  uint32_t* counter;   // [T][4] candidate-list cursor, arrivals of the MISA† fine stage (zero on entry)
+  uint32_t* counter;   // [T][4] candidate-list cursor, arrivals of the one-launch selection (zero on entry)
   uint32_t* ndef;      // [T][nchunk] keys above the level-1 threshold bin in each chunk; then
                        // [T][nchunk][3] the MISA† selection's member count and dense-key range
   uint32_t* cand;      // [T][cap][2] (key, index) of the level-1 threshold bin
@@ -137,8 +137,8 @@ struct RescoreArgs {
   const uint16_t* k;
   int H;
   int d;
-  float* scores;            // [T][kc] dense score of each candidate slot
-  uint32_t* hist;           // [T][4096] level-1 histogram of those scores (zero on entry)
+  float* scores;            // [T][kc] dense score of each candidate slot (compaction only)
+  uint32_t* hist;           // [T][4096] level-1 histogram of those scores (zero on entry; compaction only)
   // the final top-k, selected in the same launch (launch_hier_select only)
   int32_t* fidx;            // [T][ftopk]
   float* fscore;            // [T][ftopk] or null

@@ -50,9 +50,9 @@ constexpr int kSplitShortRows = 64;          // rows at most for the split selec
 // state[t][*]: the row's level-1 threshold bin, how many of its keys are kept,
 // and how many keys it holds (written by the filter launch's first chunk)
 enum { ST_B1 = 0, ST_KREM1 = 1, ST_M = 2 };
-// counter[t][*] (zero on entry): candidate-list cursor, arrivals of the MISA†
-// selection
-enum { CT_CAND = 0, CT_FINE = 2 };
+// counter[t][*] (zero on entry): candidate-list cursor (two-launch form),
+// arrivals of the one-launch selection
+enum { CT_CAND = 0, CT_ARRIVE = 2 };
 
 __device__ __forceinline__ int64_t row_len_of(const TopkArgs& a, int64_t t, int& p) {
   p = query_prefix_len(a.q_seq, a.q_len, a.nseq, a.Lmax, t);
@@ -669,7 +669,7 @@ __global__ __launch_bounds__(kThreads) void split_select_kernel(TopkArgs a, Spli
   // ---- arrival: this chunk's members, count and range are in memory before it counts
   wait_stores();
   __syncthreads();
-  if (tid == 0) s_last = atomic_add_coherent(w.counter + t * 4 + CT_FINE, 1u) == (uint32_t)nact - 1 ? 1u : 0u;
+  if (tid == 0) s_last = atomic_add_coherent(w.counter + t * 4 + CT_ARRIVE, 1u) == (uint32_t)nact - 1 ? 1u : 0u;
   if (tid == 0) {   // for the last chunk's reduction of the ranges
     s_mm[0] = 0xffffffffu;
     s_mm[1] = 0u;
