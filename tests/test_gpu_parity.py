@@ -689,3 +689,55 @@ def test_split_forms_agree(topk):
     # and one row against the oracle
     oi, _ = O.score_topk(x.q, x.w, x.k, hd.cpu().numpy()[:1], x.q_seq, x.q_len, topk, queries=[0])
     np.testing.assert_array_equal(i_all.cpu().numpy()[0], oi[0])
+
+
+# shapes of the fused MISA† selection: (L, kc, topk, mode, short rows); the rows
+# of 70001 keys take chunks of 4096 scores, the shorter ones chunks of 1024
+_HIER_SWEEP = [
+    (40000, 512, 1, "grid", False), (40000, 2048, 2048, "gauss", True), (40000, 8192, 100, "grid", True),
+    (70001, 1024, 1000, "gauss", False), (70001, 8192, 8192, "grid", False), (70001, 4096, 7, "gauss", True),
+    (70001, 6000, 3000, "grid", True), (131072, 8192, 2048, "grid", True),
+]
+
+
+@pytest.mark.parametrize("L,kc,topk,mode,short", _HIER_SWEEP)
+def test_fused_hier_sweep(L, kc, topk, mode, short):
+    """misa_hier_indexer over a sweep of row lengths, k' and k (k = 1 and k = k'
+    included), both value modes, full rows and rows cut short (an empty row, rows
+    shorter than k and than k', and rows ending inside a chunk): bit for bit the
+    separate calls, which the rest of the suite checks against the oracle."""
+    x = make_inputs("c4", mode=mode, L=L, T=4, nseq=4, kc=kc, topk=topk)
+    dev = upload(x)
+    c = x.cfg
+    q_len = dev["q_len"].clone()
+    if short:
+        q_len[0], q_len[1], q_len[2] = 0, max(1, topk // 2), min(L - 1, kc + 4097)
+    kbar = M.pool_keys(dev["k"], c.B)
+    heads = torch.empty((c.T, c.h), dtype=torch.int32, device="cuda")
+    cand = torch.full((c.T, kc), -7, dtype=torch.int32, device="cuda")
+    idx, sc = M.hier_indexer(dev["q"], dev["w"], dev["k"], kbar, dev["q_seq"], q_len, c.B, c.h, kc, topk,
+                             heads=heads, cand=cand)
+    cand1, idx1, sc1 = _hier_separate(dev["q"], dev["w"], dev["k"], heads, dev["q_seq"], q_len, kc, topk)
+    torch.cuda.synchronize()
+    assert torch.equal(cand, cand1) and torch.equal(idx, idx1) and torch.equal(sc, sc1)
+
+
+@pytest.mark.parametrize("L", [16385, 20001, 32768])
+def test_split_and_register_selects_agree(L):
+    """Rows of 16K..32K scores: a decode batch of 4 rows takes the one-launch split
+    selection, a batch of more than 64 rows the register row select; the same
+    queries give the same indices and scores bit for bit in both (grid mode, k
+    inside a tie-heavy row)."""
+    x = make_inputs("c1m", mode="grid", L=L, T=68, topk=1000)
+    dev = upload(x)
+    c = x.cfg
+    kbar = M.pool_keys(dev["k"], c.B)
+    hd = M.route(dev["q"], dev["w"], dev["k"], kbar, dev["q_seq"], dev["q_len"], c.B, c.h)
+    # one query per sequence (decode layout, split selection) against the 68-row batch
+    rows = [0, 17, 34, 51]
+    sub = lambda t: t[rows].contiguous()
+    i_all, s_all = M.score_topk(dev["q"], dev["w"], dev["k"], hd, dev["q_seq"], dev["q_len"], c.topk)
+    i_4, s_4 = M.score_topk(sub(dev["q"]), sub(dev["w"]), dev["k"], sub(hd), sub(dev["q_seq"]), sub(dev["q_len"]),
+                            c.topk)
+    torch.cuda.synchronize()
+    assert torch.equal(i_4, i_all[rows]) and torch.equal(s_4, s_all[rows])
