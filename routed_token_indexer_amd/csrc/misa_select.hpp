@@ -111,6 +111,30 @@ __device__ __forceinline__ void find_threshold(const uint32_t* hist, int nb, uin
   __syncthreads();
 }
 
+// find_threshold by the calling wave alone, for nb <= 256 bins (four per
+// lane; no barrier inside: the caller puts one before out[] is read).
+__device__ __forceinline__ void find_threshold_wave(const uint32_t* hist, int nb, uint32_t krem, uint32_t* out) {
+  constexpr int PER = 4;
+  const int lane = threadIdx.x & 63;
+  uint32_t c[PER], mine = 0;
+#pragma unroll
+  for (int jj = 0; jj < PER; ++jj) {
+    const int b = PER * lane + jj;
+    c[jj] = b < nb ? hist[nb - 1 - b] : 0u;
+    mine += c[jj];
+  }
+  uint32_t above = wave_incl_scan(mine) - mine;
+#pragma unroll
+  for (int jj = 0; jj < PER; ++jj) {
+    if (above < krem && above + c[jj] >= krem) {
+      out[0] = (uint32_t)(nb - 1 - (PER * lane + jj));
+      out[1] = krem - above;
+      out[2] = (krem - above == c[jj]) ? 1u : 0u;
+    }
+    above += c[jj];
+  }
+}
+
 // Scratch of radix_select for NT threads: NH histograms (one per level, or a
 // single one cleared between levels), a scan and a result slot per level.
 template <int NT = kSelThreads, int NH = 3>

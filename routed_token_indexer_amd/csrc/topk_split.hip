@@ -539,7 +539,8 @@ __global__ __launch_bounds__(kThreads) void split_select_kernel(TopkArgs a, Spli
   __shared__ uint32_t s_fgt[RR ? kMaxChunks : 1], s_feq[RR ? kMaxChunks : 1];
   __shared__ uint32_t s_tot, s_nc, s_nc2, s_fthr, s_fkrem;
   // keys of the coarse threshold sub-bin, then of the fine threshold bin, with their chunks
-  __shared__ uint32_t c_key[kCand], c_w[RR ? kCand : 1], c_ch[kCand];
+  __shared__ uint32_t c_key[kCand], c_ch[kCand];
+  __shared__ uint64_t c_kw[RR ? kCand : 1];   // the fine bin's keys: key | weight << 32
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int64_t t = blockIdx.y;
@@ -816,7 +817,8 @@ __global__ __launch_bounds__(kThreads) void split_select_kernel(TopkArgs a, Spli
     __syncthreads();
     if (!whole) {
       // level 3, then each listed member above thr or at it counts in its chunk
-      find_threshold(s_h3, 256, krem2, wsum[2], sh[2]);
+      if (wave == 0) find_threshold_wave(s_h3, 256, krem2, sh[2]);
+      __syncthreads();
       const uint32_t lo8 = sh[2][0];
       thr = (hi24 << 8) | lo8;
       krem_eq = sh[2][1];
@@ -849,10 +851,21 @@ __global__ __launch_bounds__(kThreads) void split_select_kernel(TopkArgs a, Spli
   }
   // over the chunks in order: selected members and members at the threshold
   // before each chunk (sg, se), and in the whole row (s_tot)
+  // (up to 64 chunks: wave 0 alone, one chunk per lane)
   auto chunk_offsets = [&](uint32_t* sg, uint32_t* se, uint32_t kr) {
-    const uint32_t gt = tid < nact ? sg[tid] : 0u, eq = tid < nact ? se[tid] : 0u;
-    uint32_t eq_before;
-    const uint32_t gt_before = block_excl_scan2(gt, eq, &wsum[2][0], eq_before);
+    uint32_t gt = 0, eq = 0, gt_before = 0, eq_before = 0;
+    if (nact <= 64) {
+      if (wave == 0) {
+        gt = lane < nact ? sg[lane] : 0u;
+        eq = lane < nact ? se[lane] : 0u;
+        gt_before = wave_incl_scan(gt) - gt;
+        eq_before = wave_incl_scan(eq) - eq;
+      }
+    } else {
+      gt = tid < nact ? sg[tid] : 0u;
+      eq = tid < nact ? se[tid] : 0u;
+      gt_before = block_excl_scan2(gt, eq, &wsum[2][0], eq_before);
+    }
     if (tid < nact) {
       sg[tid] = gt_before + (eq_before < kr ? eq_before : kr);
       se[tid] = eq_before;
@@ -1023,8 +1036,7 @@ __global__ __launch_bounds__(kThreads) void split_select_kernel(TopkArgs a, Spli
       if (inb & !by_bin) {
         const uint32_t s = atomicAdd(&s_nc, 1u);
         if (s < (uint32_t)kCand) {
-          c_key[s] = fk[g];
-          c_w[s] = 1u;
+          c_kw[s] = (1ull << 32) | fk[g];
           c_ch[s] = (uint32_t)c2;
         }
       }
@@ -1037,8 +1049,7 @@ __global__ __launch_bounds__(kThreads) void split_select_kernel(TopkArgs a, Spli
   if (!by_bin && tid == 0 && npad && ((kpad - flo) >> fsh) == d0) {
     const uint32_t s = atomicAdd(&s_nc, 1u);
     if (s < (uint32_t)kCand) {
-      c_key[s] = kpad;
-      c_w[s] = npad;
+      c_kw[s] = ((uint64_t)npad << 32) | kpad;
       c_ch[s] = 0xffffffffu;   // the empty slots: after every chunk
     }
   }
@@ -1048,32 +1059,37 @@ __global__ __launch_bounds__(kThreads) void split_select_kernel(TopkArgs a, Spli
     if (nc <= (uint32_t)kCand) {
       // the key K with fewer than krem keys of the bin above it and at least
       // krem at or above it; krem - (keys above K) of those equal to K are kept
+      // (a key with fewer than krem keys at or above it lies above K; each listed
+      // key above K or at it counts in its chunk)
       const uint32_t kr = fkrem;
       if (tid < (int)nc) {
-        const uint32_t ki = c_key[tid];
+        const uint32_t ki = (uint32_t)c_kw[tid];
         uint32_t gt = 0, eq = 0;
-        for (uint32_t j = 0; j < nc; ++j) {
-          const uint32_t kj = c_key[j], wj = c_w[j];
-          gt += kj > ki ? wj : 0u;
-          eq += kj == ki ? wj : 0u;
+        for (uint32_t j = 0; j < nc; j += 4) {   // four list reads in flight (weight 0 past the list)
+          uint64_t e[4];
+#pragma unroll
+          for (int u2 = 0; u2 < 4; ++u2) e[u2] = j + u2 < nc ? c_kw[j + u2] : 0ull;
+#pragma unroll
+          for (int u2 = 0; u2 < 4; ++u2) {
+            const uint32_t kj = (uint32_t)e[u2], wj = (uint32_t)(e[u2] >> 32);
+            gt += kj > ki ? wj : 0u;
+            eq += kj == ki ? wj : 0u;
+          }
         }
-        if ((gt < kr) & (kr <= gt + eq)) {
+        const bool at = (gt < kr) & (kr <= gt + eq);
+        if (at) {
           s_fthr = ki;
           s_fkrem = kr - gt;
         }
+        if (c_ch[tid] != 0xffffffffu) {
+          if (gt + eq < kr) atomicAdd(&s_fgt[c_ch[tid]], 1u);
+          if (at) atomicAdd(&s_feq[c_ch[tid]], 1u);
+        }
       }
       __syncthreads();
-      const uint32_t fthr = s_fthr;
-      fpre = fthr - flo;
+      fpre = s_fthr - flo;
       fmask = 0xffffffffu;
       fkrem = s_fkrem;
-      // each listed key above K or at it counts in its chunk
-      if (tid < (int)nc && c_ch[tid] != 0xffffffffu) {
-        const uint32_t ki = c_key[tid];
-        if (ki > fthr) atomicAdd(&s_fgt[c_ch[tid]], 1u);
-        if (ki == fthr) atomicAdd(&s_feq[c_ch[tid]], 1u);
-      }
-      __syncthreads();
     } else {
       // more keys in the bin than the list holds (heavy ties): radix select over
       // all of the kept members, then their counts per chunk again
