@@ -289,13 +289,18 @@ def test_prefill_row_equals_decode_call():
 
 
 # ------------------------------------------------------------------ edge cases
-def test_empty_and_invalid_queries():
-    x, dev = get("c1r", "grid")
+@pytest.mark.parametrize("case", ["c1r", "c1s", "c1x"])
+def test_empty_and_invalid_queries(case):
+    """Empty, invalid, over-long and short prefixes in one batch, through the
+    register row select (c1r), the one-launch split selection of 16K-32K rows
+    (c1s) and of longer rows (c1x)."""
+    x, dev = get(case, "grid")
     q_len = dev["q_len"].clone()
     q_seq = dev["q_seq"].clone()
     q_len[0] = 0          # empty prefix
     q_seq[1] = 99         # sequence out of range: treated as empty
     q_len[2] = 10 ** 9    # clamped to Lmax
+    q_len[3] = 50         # shorter than k: every token, then -1 / 0
     kbar = M.pool_keys(dev["k"], x.cfg.B)
     heads = M.route(dev["q"], dev["w"], dev["k"], kbar, q_seq, q_len, x.cfg.B, x.cfg.h)
     idx, sc = M.score_topk(dev["q"], dev["w"], dev["k"], heads, q_seq, q_len, x.cfg.topk)
@@ -308,6 +313,10 @@ def test_empty_and_invalid_queries():
     hi = h[2:3]
     oi, _ = O.score_topk(x.q, x.w, x.k, hi, x.q_seq, x.q_len, x.cfg.topk, queries=[2])
     np.testing.assert_array_equal(idx.cpu().numpy()[2], oi[0])
+    for out, scr in ((idx, sc), (di, None)):
+        o = out.cpu().numpy()
+        assert o[3][:50].tolist() == list(range(50)) and np.all(o[3][50:] == -1)
+    assert np.all(sc.cpu().numpy()[3][50:] == 0)
 
 
 def test_short_prefix_takes_all():
