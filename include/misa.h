@@ -98,6 +98,10 @@ MISA_API const char* misa_last_error(void);
  * Arguments that an op does not use are ignored (kc matters for the MISA†
  * ops, and stands for m, the blocks kept, in the block ops; B for the ops that
  * route or pool). Returns 0 if none is needed.
+ * The scoring ops hold fp32 score rows for at most 1 GiB of queries at a time
+ * (min(T, 2^28 / Lmax) rows): a larger batch, such as a long causal prefill, is
+ * scored and selected in consecutive slabs of queries on the stream, so the
+ * workspace does not grow with T * Lmax beyond that bound.
  */
 MISA_API size_t misa_workspace_bytes(int32_t op, int64_t T, int32_t H, int64_t Lmax, int32_t B, int32_t topk,
                             int32_t kc);

@@ -79,11 +79,28 @@ size_t pivot_head_bytes(int64_t ng, int32_t H, int32_t kc) {
          round_up((size_t)ng * (size_t)kc * 4);
 }
 
+// Scoring + selection keeps the fp32 score rows of at most this many bytes of
+// queries at a time: a larger batch (a long causal prefill) is scored and
+// selected in consecutive slabs of queries that reuse one slab of rows, so that
+// the workspace grows with the row length, not with the batch times the row length.
+#ifndef MISA_SCORE_SLAB_BYTES
+#define MISA_SCORE_SLAB_BYTES (1ull << 30)
+#endif
+constexpr size_t kScoreSlabBytes = MISA_SCORE_SLAB_BYTES;
+
+// Queries per slab for rows of max_len scores (the whole batch when it fits).
+int64_t slab_rows(int64_t T, int64_t max_len) {
+  const int64_t per = max_len > 0 ? (int64_t)(kScoreSlabBytes / ((size_t)max_len * sizeof(float))) : T;
+  const int64_t r = per < 1 ? 1 : per;
+  return T < r ? T : r;
+}
+
 // Workspace of scoring + selection over rows of at most max_len: the fp32 score
-// rows, then (for few long rows) the split top-k's state.
+// rows of one slab of queries, then (for few long rows) the split top-k's state.
 size_t select_ws_bytes(int64_t T, int64_t max_len) {
-  size_t b = round_up((size_t)T * (size_t)max_len * sizeof(float));
-  if (misa::use_split_topk(T, max_len, true)) b += round_up(misa::split_topk_ws_bytes(T, max_len));
+  const int64_t S = slab_rows(T, max_len);
+  size_t b = round_up((size_t)S * (size_t)max_len * sizeof(float));
+  if (misa::use_split_topk(S, max_len, true)) b += round_up(misa::split_topk_ws_bytes(S, max_len));
   return b;
 }
 
@@ -376,6 +393,21 @@ int32_t score_and_select(const char* fn, const void* q, const float* w, const vo
                          int32_t hh, const int32_t* cand, int32_t kc, const int32_t* q_seq, const int32_t* q_len,
                          int64_t T, int32_t H, int32_t d, int64_t nseq, int64_t Lmax, int32_t topk, int32_t* idx,
                          float* score, float* scores, int64_t stride, hipStream_t st) {
+  const int64_t S = slab_rows(T, stride);
+  if (idx && S < T) {   // (without a selection the rows themselves are the output: no slabs)
+    // consecutive slabs of queries, each scored into the same rows and selected
+    // before the next one overwrites them (stream order); every pointer that is
+    // indexed by the query moves with the slab
+    for (int64_t t0 = 0; t0 < T; t0 += S) {
+      const int64_t n = T - t0 < S ? T - t0 : S;
+      const int32_t rc = score_and_select(
+          fn, static_cast<const uint16_t*>(q) + t0 * H * d, w + t0 * H, k, heads ? heads + t0 * hh : nullptr, hh,
+          cand ? cand + t0 * kc : nullptr, kc, q_seq + t0, q_len + t0, n, H, d, nseq, Lmax, topk,
+          idx ? idx + t0 * topk : nullptr, score ? score + t0 * topk : nullptr, scores, stride, st);
+      if (rc) return rc;
+    }
+    return ok();
+  }
   misa::ScoreArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.w = w;

@@ -65,6 +65,19 @@ def test_workspace_sizes(L):
     # the router splits long prefixes over chunks for few queries, one chunk for many
     assert B.workspace_bytes(B.OP_ROUTE, 4, 64, 131072, 128) > 0
     assert B.workspace_bytes(B.OP_ROUTE, 16384, 64, 16384, 64) == 0
+    # a long causal prefill keeps score rows for at most 1 GiB of queries at a
+    # time (slabs of 2^28 / Lmax queries): 16K x 16K fits in one slab; 128K x
+    # 128K takes slabs of 2048 queries, whose rows of 128K scores also carry the
+    # split top-k's state: about 3 GiB instead of 64 GiB
+    assert B.workspace_bytes(B.OP_SCORE_TOPK, 16384, 64, 16384, 0, 2048) == 1 << 30
+    assert B.workspace_bytes(B.OP_SCORE_TOPK, 16385, 64, 16384, 0, 2048) == 1 << 30
+    for op in (B.OP_SCORE_TOPK, B.OP_DSA_DENSE):
+        big = B.workspace_bytes(op, 131072, 64, 131072, 0, 2048)
+        assert big == B.workspace_bytes(op, 2048, 64, 131072, 0, 2048)
+        assert (1 << 30) < big < 4 << 30
+    # rows longer than a slab hold one query at a time
+    assert B.workspace_bytes(B.OP_SCORE_TOPK, 8, 64, (1 << 28) + 64, 0, 2048) >= ((1 << 28) + 64) * 4
+    assert B.workspace_bytes(B.OP_SCORE_TOPK, 8, 64, (1 << 28) + 64, 0, 2048) < 2 * ((1 << 28) + 64) * 4
 
 
 FAKE = ctypes.c_void_p(1 << 20)      # aligned, never dereferenced: validation fails first

@@ -468,6 +468,35 @@ def test_prefill_shapes(d, H, h):
     np.testing.assert_array_equal(dv.cpu().numpy(), odv.astype(np.float32))
 
 
+def test_prefill_query_slabs():
+    """A prefill batch whose score rows exceed the library's 1 GiB slab: 2100
+    causal queries over a key cache of Lmax = 131072 positions (rows of 512 KiB)
+    are scored and selected in slabs of 2048 queries and one of 52. Every row
+    equals the same call over a cache of 2100 positions (one slab), bit for bit,
+    for the routed and the dense indexer, and the routed rows at the slab
+    boundary equal the oracle's (grid mode)."""
+    x = make_inputs("c2", mode="grid", L=2100, T=2100, topk=256)
+    c = x.cfg
+    dev = upload(x)
+    big = torch.zeros((1, 131072, c.d), dtype=torch.bfloat16, device="cuda")
+    big[:, : c.L] = dev["k"]
+    # the workspace is one slab's (2048 queries)
+    assert (M.workspace_bytes(M.OP_SCORE_TOPK, c.T, c.H, 131072, 0, c.topk) ==
+            M.workspace_bytes(M.OP_SCORE_TOPK, 2048, c.H, 131072, 0, c.topk))
+    ho, _ = O.route(x.q, x.w, x.k, x.q_seq, x.q_len, c.B, c.h)
+    hd = torch.from_numpy(ho).cuda()
+    ri, rs = M.score_topk(dev["q"], dev["w"], dev["k"], hd, dev["q_seq"], dev["q_len"], c.topk)
+    si, ss = M.score_topk(dev["q"], dev["w"], big, hd, dev["q_seq"], dev["q_len"], c.topk)
+    assert torch.equal(si, ri) and torch.equal(ss, rs)
+    di, ds = M.dsa_index_dense(dev["q"], dev["w"], dev["k"], dev["q_seq"], dev["q_len"], c.topk)
+    bi, bs = M.dsa_index_dense(dev["q"], dev["w"], big, dev["q_seq"], dev["q_len"], c.topk)
+    assert torch.equal(bi, di) and torch.equal(bs, ds)
+    qs = [0, 255, 256, 2047, 2048, 2049, 2099]
+    oi, ov = O.score_topk(x.q, x.w, x.k, ho[qs], x.q_seq, x.q_len, c.topk, queries=qs)
+    np.testing.assert_array_equal(si.cpu().numpy()[qs], oi)
+    np.testing.assert_array_equal(ss.cpu().numpy()[qs], ov.astype(np.float32))
+
+
 def test_prefill_mixed_sequences():
     """A prefill batch over three sequences with the queries in shuffled order: query
     tiles straddle sequences (one key pass per distinct sequence in a tile), and the
