@@ -497,6 +497,54 @@ def test_prefill_query_slabs():
     np.testing.assert_array_equal(ss.cpu().numpy()[qs], ov.astype(np.float32))
 
 
+def test_rerank_query_slabs():
+    """The gathered re-rank over more queries than one 1 GiB slab of candidate
+    score rows holds (k' = 8192: 32768 queries per slab): 33000 queries on grid
+    inputs with candidate rows that are ascending, partly past the query's
+    prefix and partly -1 padded. Rows on both sides of the slab boundary and a
+    spread of others equal the oracle's, bit for bit, and each equals the same
+    query re-ranked alone."""
+    from routed_token_indexer_amd.workloads import bf16_bits
+    rng = np.random.default_rng(5)
+    T, H, d, L, kc, topk = 33000, 8, 32, 9000, 8192, 64
+    k = (rng.integers(-2, 3, size=(1, L, d)).astype(np.float32) / 16).astype(np.float32)
+    q = (rng.integers(-2, 3, size=(T, H, d)).astype(np.float32) / 16).astype(np.float32)
+    w = (rng.integers(1, 5, size=(T, H)).astype(np.float32) / 4).astype(np.float32)
+    q_seq = np.zeros(T, np.int32)
+    q_len = rng.integers(1, L + 1, size=T).astype(np.int32)
+    # kc distinct ids per row: an arithmetic progression mod L with a step prime to L
+    step = rng.choice([7, 11, 13, 17, 19, 23, 29, 31], size=T)
+    start = rng.integers(0, L, size=T)
+    cand = ((start[:, None] + np.arange(kc)[None, :] * step[:, None]) % L).astype(np.int32)
+    cand.sort(axis=1)
+    npad = rng.integers(0, 64, size=T)
+    cand[np.arange(kc)[None, :] >= (kc - npad)[:, None]] = -1   # the largest ids give way to padding
+
+    def dev_bf16(x):
+        return torch.from_numpy(bf16_bits(x).view(np.int16)).cuda().view(torch.bfloat16).contiguous()
+
+    dq, dk = dev_bf16(q), dev_bf16(k)
+    dw, ds, dl = torch.from_numpy(w).cuda(), torch.from_numpy(q_seq).cuda(), torch.from_numpy(q_len).cuda()
+    dc = torch.from_numpy(cand).cuda()
+    assert (M.workspace_bytes(M.OP_HIER_RERANK, T, H, L, 0, topk, kc) ==
+            M.workspace_bytes(M.OP_HIER_RERANK, 32768, H, L, 0, topk, kc))
+    idx, sc = M.hier_rerank(dq, dw, dk, dc, ds, dl, topk)
+    qs = [0, 1, 4097, 20000, 32766, 32767, 32768, 32769, T - 1]
+    # the oracle takes the candidates inside the prefix (the library skips the others)
+    inside = np.full((len(qs), kc), -1, np.int32)
+    for i, t in enumerate(qs):
+        v = cand[t][(cand[t] >= 0) & (cand[t] < q_len[t])]
+        inside[i, : len(v)] = v
+    oi, ov = O.hier_rerank(q, w, k, inside, q_seq, q_len, topk, queries=qs)
+    np.testing.assert_array_equal(idx.cpu().numpy()[qs], oi)
+    np.testing.assert_array_equal(sc.cpu().numpy()[qs], ov.astype(np.float32))
+    for t in qs:
+        sl = slice(t, t + 1)
+        ai, asc = M.hier_rerank(dq[sl].contiguous(), dw[sl].contiguous(), dk, dc[sl].contiguous(),
+                                ds[sl].contiguous(), dl[sl].contiguous(), topk)
+        assert torch.equal(ai[0], idx[t]) and torch.equal(asc[0], sc[t]), t
+
+
 def test_prefill_mixed_sequences():
     """A prefill batch over three sequences with the queries in shuffled order: query
     tiles straddle sequences (one key pass per distinct sequence in a tile), and the
