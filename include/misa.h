@@ -101,7 +101,10 @@ MISA_API const char* misa_last_error(void);
  * The scoring ops hold fp32 score rows for at most 1 GiB of queries at a time
  * (min(T, 2^28 / Lmax) rows): a larger batch, such as a long causal prefill, is
  * scored and selected in consecutive slabs of queries on the stream, so the
- * workspace does not grow with T * Lmax beyond that bound.
+ * workspace does not grow with T * Lmax beyond that bound. misa_indexer and
+ * misa_hier_indexer run their fused decode pipeline (score rows for the whole
+ * batch) only for batches of at most 4096 queries; larger batches take the
+ * separate calls and their bound.
  */
 MISA_API size_t misa_workspace_bytes(int32_t op, int64_t T, int32_t H, int64_t Lmax, int32_t B, int32_t topk,
                             int32_t kc);

@@ -104,6 +104,11 @@ size_t select_ws_bytes(int64_t T, int64_t max_len) {
   return b;
 }
 
+// Decode batches of at most this many queries take the fused pipeline below
+// (larger ones, and every prefill or multi-token batch, take the separate
+// calls, whose score rows are bounded by the query slabs).
+constexpr int64_t kFusedMaxRows = 4096;
+
 // Workspace of the fused decode pipeline (misa_indexer / misa_hier_indexer):
 // router partials and partial-block dots, the coarse score rows and their split
 // top-k state, and for MISA† the candidate list, its dense scores and their
@@ -300,12 +305,14 @@ size_t misa_workspace_bytes(int32_t op, int64_t T, int32_t H, int64_t Lmax, int3
     case MISA_OP_HIER_INDEXER: {
       if (B < 1 || H < 1) return 0;
       const bool hier = op == MISA_OP_HIER_INDEXER;
-      const FusedLayout f = fused_layout(T, H, Lmax, B, hier ? kc : 0, nullptr);
+      // the fused layout holds score rows for the whole batch: only batches that
+      // may take the fused pipeline (at most kFusedMaxRows queries) size it
+      const size_t fb = T <= kFusedMaxRows ? fused_layout(T, H, Lmax, B, hier ? kc : 0, nullptr).bytes : 0;
       size_t sep = misa_workspace_bytes(MISA_OP_ROUTE, T, H, Lmax, B, 0, 0) + round_up((size_t)T * H * 4);
       size_t sc = misa_workspace_bytes(MISA_OP_SCORE_TOPK, T, H, Lmax, B, hier ? kc : topk, 0);
       if (hier) sc += round_up((size_t)T * (size_t)kc * 4) + misa_workspace_bytes(MISA_OP_HIER_RERANK, T, H, Lmax, B, topk, kc);
       sep += sc;
-      return f.bytes > sep ? f.bytes : sep;
+      return fb > sep ? fb : sep;
     }
   }
   return 0;
@@ -549,8 +556,8 @@ int32_t run_indexer(const char* fn, bool hier, const void* q, const float* w, co
   rc = check_ws(fn, ws, ws_bytes, misa_workspace_bytes(op, T, H, Lmax, B, topk, hier ? kc : 0));
   if (rc) return rc;
 
-  const bool fused = !wide_tiles(T, nseq) && !few_tiles(T, nseq) && misa::split_topk_always_ok(Lmax) &&
-                     (!hier || misa::split_topk_always_ok(kc));
+  const bool fused = T <= kFusedMaxRows && !wide_tiles(T, nseq) && !few_tiles(T, nseq) &&
+                     misa::split_topk_always_ok(Lmax) && (!hier || misa::split_topk_always_ok(kc));
   if (!fused) {
     char* p = static_cast<char*>(ws);
     const size_t rws = misa_workspace_bytes(MISA_OP_ROUTE, T, H, Lmax, B, 0, 0);

@@ -75,6 +75,10 @@ def test_workspace_sizes(L):
         big = B.workspace_bytes(op, 131072, 64, 131072, 0, 2048)
         assert big == B.workspace_bytes(op, 2048, 64, 131072, 0, 2048)
         assert (1 << 30) < big < 4 << 30
+    # the whole indexers on a long prefill take the separate calls: the same bound
+    # (MISA-dagger adds the candidate rows, T x k' ids, when the caller passes none)
+    assert B.workspace_bytes(B.OP_INDEXER, 131072, 64, 131072, 64, 2048) < 4 << 30
+    assert B.workspace_bytes(B.OP_HIER_INDEXER, 131072, 64, 131072, 64, 2048, 8192) < 131072 * 8192 * 4 + (5 << 30)
     # rows longer than a slab hold one query at a time
     assert B.workspace_bytes(B.OP_SCORE_TOPK, 8, 64, (1 << 28) + 64, 0, 2048) >= ((1 << 28) + 64) * 4
     assert B.workspace_bytes(B.OP_SCORE_TOPK, 8, 64, (1 << 28) + 64, 0, 2048) < 2 * ((1 << 28) + 64) * 4
