@@ -1173,7 +1173,12 @@ inline size_t al(size_t x) { return (x + 255) / 256 * 256; }
 
 bool use_split_topk(int64_t T, int64_t max_len, bool hist_in_scoring) {
   if (T > 4096 || max_len > (int64_t)kMaxChunks * kThreads * 4) return false;
-  if (max_len > topk_row_reg_max()) return true;
+  // rows too long for the register select: split over chunks for a few rows,
+  // or when the scoring kernel has built their histograms; a larger batch
+  // without them (a slab of a long prefill) keeps the chip busy with one
+  // workgroup per row, whose streaming select reads each row a few times
+  // instead of building histograms with device-wide atomics
+  if (max_len > topk_row_reg_max()) return T <= 256 || hist_in_scoring;
   // rows of 16K..32K scores in a small batch whose histogram the scoring kernel
   // builds: the one-launch selection over chunks beats a workgroup per row;
   // shorter rows, or rows needing a histogram launch, take one workgroup each

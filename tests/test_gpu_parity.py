@@ -545,6 +545,37 @@ def test_rerank_query_slabs():
         assert torch.equal(ai[0], idx[t]) and torch.equal(asc[0], sc[t]), t
 
 
+def test_many_long_rows_streaming_select():
+    """A prefill-like batch of 300 queries whose rows hold 40001..40300 scores:
+    longer than the register select takes, more than 256 rows, and no level-1
+    histogram from the scoring kernel, so one workgroup per row streams its row
+    from memory (a slab of a long prefill selects this way). Grid mode: every
+    routed row, and a sample of dense rows, equal the oracle's bit for bit."""
+    from routed_token_indexer_amd.workloads import bf16_bits
+    base = make_inputs("c1", mode="grid", L=40300, T=1, nseq=1, H=8, d=32, h=2, B=32, topk=500)
+    rng = np.random.default_rng(17)
+    T, H, d = 300, base.cfg.H, base.cfg.d
+    q = (rng.integers(-2, 3, size=(T, H, d)).astype(np.float32) / 16).astype(np.float32)
+    w = (rng.integers(1, 5, size=(T, H)).astype(np.float32) / 4).astype(np.float32)
+    q_seq = np.zeros(T, np.int32)
+    q_len = np.arange(40001, 40001 + T, dtype=np.int32)
+    dev = upload(base)
+    dev["q"] = torch.from_numpy(bf16_bits(q).view(np.int16)).cuda().view(torch.bfloat16).contiguous()
+    dev["w"] = torch.from_numpy(w).cuda()
+    dev["q_seq"] = torch.from_numpy(q_seq).cuda()
+    dev["q_len"] = torch.from_numpy(q_len).cuda()
+    ho = np.tile(np.array([1, 6], np.int32), (T, 1))   # given heads: the selection is under test
+    idx, sc = M.score_topk(dev["q"], dev["w"], dev["k"], torch.from_numpy(ho).cuda(), dev["q_seq"], dev["q_len"], 500)
+    oi, ov = O.score_topk(q, w, base.k, ho, q_seq, q_len, 500)
+    np.testing.assert_array_equal(idx.cpu().numpy(), oi)
+    np.testing.assert_array_equal(sc.cpu().numpy(), ov.astype(np.float32))
+    di, dv = M.dsa_index_dense(dev["q"], dev["w"], dev["k"], dev["q_seq"], dev["q_len"], 500)
+    qs = [0, 1, 150, 255, 256, 299]
+    odi, odv = O.dsa_index_dense(q, w, base.k, q_seq, q_len, 500, queries=qs)
+    np.testing.assert_array_equal(di.cpu().numpy()[qs], odi)
+    np.testing.assert_array_equal(dv.cpu().numpy()[qs], odv.astype(np.float32))
+
+
 def test_prefill_mixed_sequences():
     """A prefill batch over three sequences with the queries in shuffled order: query
     tiles straddle sequences (one key pass per distinct sequence in a tile), and the
