@@ -362,6 +362,14 @@ def main():
                   f"step {subs[name]['step_frac']:.3f} of roofline", file=sys.stderr, flush=True)
             del del_wl
             torch.cuda.empty_cache()
+        # a causal prefill at 128K context (score rows in query slabs)
+        try:
+            subs["c2_128k"] = prefill_128k(M, dev)
+            print(f"[bench] c2_128k: {subs['c2_128k']['us_per_step'] / 1e3:.1f} ms/step, kernel "
+                  f"{subs['c2_128k']['kernel_frac']:.3f} step {subs['c2_128k']['step_frac']:.3f} of roofline",
+                  file=sys.stderr, flush=True)
+        except Exception as e:   # a timing record only: never lose the headline line for it
+            subs["c2_128k"] = {"error": f"{type(e).__name__}: {e}"[:300]}
         out["configs"] = subs
 
     # ---- the CPU oracle on the host cores, on a bounded sample of the same workload
@@ -369,6 +377,58 @@ def main():
         out["cpu_baseline"] = cpu_baseline(x, c, wl.hier, wl.prefill)
 
     print(json.dumps(out), flush=True)
+
+
+def prefill_128k(M, dev, steps=2, warmup=1):
+    """A causal prefill at 128K context (every position a query): pooling, routing,
+    routed scoring and the row top-k, the c2 step at 8x the length. The score rows
+    take consecutive slabs of 2048 queries. Inputs are drawn on the GPU with
+    torch's seeded generator: q and k ~ N(0, 1/d) i.i.d., w = softmax of N(0, 1)
+    (the workload generator's AR(1) keys would take minutes on the host at this
+    size); this is a timing record, not a parity case."""
+    import torch
+    L = T = 131072
+    H, d, B, h, k = 64, 128, 64, 8, 2048
+    g = torch.Generator(device=dev)
+    g.manual_seed(1302)
+    q = (torch.randn(T, H, d, device=dev, generator=g) / d ** 0.5).to(torch.bfloat16)
+    keys = (torch.randn(1, L, d, device=dev, generator=g) / d ** 0.5).to(torch.bfloat16)
+    w = torch.softmax(torch.randn(T, H, device=dev, generator=g), dim=1).float().contiguous()
+    q_seq = torch.zeros(T, dtype=torch.int32, device=dev)
+    q_len = torch.arange(1, T + 1, dtype=torch.int32, device=dev)
+    kbar = torch.empty((1, L // B, d), dtype=torch.float32, device=dev)
+    heads = torch.empty((T, h), dtype=torch.int32, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    sc = torch.empty((T, k), dtype=torch.float32, device=dev)
+    wsb = M.workspace_bytes(M.OP_INDEXER, T, H, L, B, k)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    def step(_):
+        M.pool_keys(keys, B, kbar=kbar)
+        M.indexer(q, w, keys, kbar, q_seq, q_len, B, h, k, heads=heads, idx=idx, score=sc, ws=ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    M.timing_begin(M.KERNEL_SCORE, capacity=128 * steps + 16)
+    ms = timed(step, steps, 0)
+    k_ms, k_n = M.timing_end()
+    n = (idx >= 0).sum(dim=1)
+    valid = bool(n.eq(torch.clamp(q_len, max=k)).all().item())
+    p = np.arange(1, T + 1, dtype=np.float64)
+    routed = 2.0 * h * d * p.sum()
+    router = 2.0 * H * d * np.ceil(p / B).sum()
+    tokens = int(p.sum())
+    del q, keys, w, ws, idx, sc
+    torch.cuda.empty_cache()
+    return {"workload": "causal prefill at 128K context: L=131072, every position a query, H=64, d=128, B=64, h=8, "
+                        "k=2048 (inputs drawn on the GPU)",
+            "us_per_step": round(ms * 1e3, 1), "gtokens_per_s": round(tokens / ms / 1e6, 3),
+            "tokens_per_step": tokens, "workspace_bytes": wsb, "score_row_slabs": -(-T // 2048),
+            "step_frac": round((routed + router) / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "kernel_frac": round(routed / (k_ms * 1e-3 / max(steps, 1)) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "kernel_us": round(k_ms * 1e3 / max(steps, 1), 1), "kernel_launches_per_step": k_n / max(steps, 1),
+            "roofline_unit": "TFLOP/s", "rows_valid": valid, "timing": "eager launches"}
 
 
 def rows_and_recall(wl, args):
