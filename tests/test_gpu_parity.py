@@ -576,6 +576,25 @@ def test_many_long_rows_streaming_select():
     np.testing.assert_array_equal(dv.cpu().numpy()[qs], odv.astype(np.float32))
 
 
+def test_many_long_rows_all_ties():
+    """The same 300 rows of 40001..40300 scores with every score equal (zero
+    queries): the threshold bin holds the whole row, more than the streaming
+    select lists in LDS, so it takes its radix levels over the row; the kept
+    tokens are the lowest indices."""
+    base = make_inputs("c1", mode="grid", L=40300, T=1, nseq=1, H=8, d=32, h=2, B=32, topk=500)
+    T = 300
+    dev = upload(base)
+    dev["q"] = torch.zeros((T, base.cfg.H, base.cfg.d), dtype=torch.bfloat16, device="cuda")
+    dev["w"] = torch.ones((T, base.cfg.H), dtype=torch.float32, device="cuda")
+    dev["q_seq"] = torch.zeros(T, dtype=torch.int32, device="cuda")
+    dev["q_len"] = torch.arange(40001, 40001 + T, dtype=torch.int32, device="cuda")
+    hd = torch.tensor([[1, 6]] * T, dtype=torch.int32, device="cuda")
+    idx, sc = M.score_topk(dev["q"], dev["w"], dev["k"], hd, dev["q_seq"], dev["q_len"], 500)
+    expect = torch.arange(500, dtype=torch.int32, device="cuda").expand(T, 500)
+    assert torch.equal(idx, expect)
+    assert torch.all(sc == 0)
+
+
 def test_prefill_mixed_sequences():
     """A prefill batch over three sequences with the queries in shuffled order: query
     tiles straddle sequences (one key pass per distinct sequence in a tile), and the
