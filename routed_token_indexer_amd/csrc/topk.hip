@@ -74,7 +74,7 @@ __device__ __forceinline__ void topk_row_general(const TopkArgs& a, int64_t t) {
   __shared__ uint32_t rowk[kRowCap];
   __shared__ uint32_t wsum[kTopkWaves];
   __shared__ uint32_t wgt[kTopkWaves], weq[kTopkWaves];
-  __shared__ uint32_t sh_digit, sh_krem;
+  __shared__ uint32_t sh_digit, sh_krem, s_m;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int64_t n;
   int p;
@@ -120,20 +120,19 @@ __device__ __forceinline__ void topk_row_general(const TopkArgs& a, int64_t t) {
   }
   auto key_at = [&](int64_t e) -> uint32_t { return inlds ? rowk[e] : score_key(row[e]); };
 
-  // ---- radix select of the k-th largest key
+  // ---- radix select of the k-th largest key: levels of 12, 12 and 8 key bits,
+  // each a histogram of the keys that match the digits found so far
   uint32_t prefix = 0, pmask = 0;
   uint32_t krem = (uint32_t)k;
   const int shifts[3] = {20, 8, 0};
   const int nbins[3] = {4096, 4096, 256};
-#pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
+  auto level = [&](int pass, auto&& feed) {   // feed(add) calls add(key) for every key counted
     const int shift = shifts[pass], nb = nbins[pass];
     for (int i = tid; i < nb; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
-    for (int64_t e = tid; e < n; e += kTopkThreads) {
-      const uint32_t u = key_at(e);
+    feed([&](uint32_t u) {
       if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
-    }
+    });
     __syncthreads();
     // thread i owns bins [nb - 4(i+1), nb - 4i), scanned from the top
     const int ngrp = nb / 4;
@@ -159,25 +158,105 @@ __device__ __forceinline__ void topk_row_general(const TopkArgs& a, int64_t t) {
     pmask |= (uint32_t)(nb - 1) << shift;
     krem = sh_krem;
     __syncthreads();
+  };
+  auto row_keys = [&](auto&& add) {
+    for (int64_t e = tid; e < n; e += kTopkThreads) add(key_at(e));
+  };
+  // index-ordered output: wave w owns a contiguous segment and needs the counts of
+  // keys above the k-th key (wgt) and equal to it (weq) in every segment
+  const int64_t seg = ((n + kTopkWaves - 1) / kTopkWaves + 63) / 64 * 64;
+  const int64_t s0 = wave * seg, s1 = min(s0 + seg, n);
+  bool counted = false;
+  level(0, row_keys);
+  if (!inlds) {
+    // A row in memory: a second pass (in the same strided order as the first)
+    // lists the keys of the threshold bin with their indices in LDS, each wave
+    // in a region of its own (no atomics), and counts every segment's keys in
+    // higher bins; the last two levels then run over the lists, and the
+    // segments' counts come from them: the row is read three times instead of
+    // five. A wave with more keys in the bin than its region holds sends the row
+    // through the levels over the row.
+    constexpr int kPerWave = kRowCap / 2 / kTopkWaves;
+    uint32_t* const lkey = rowk + wave * 2 * kPerWave;
+    uint32_t* const lidx = lkey + kPerWave;
+    const uint32_t b1 = prefix >> 20;
+    if (tid < kTopkWaves) {
+      wgt[tid] = 0u;
+      weq[tid] = 0u;
+    }
+    if (tid == 0) s_m = 0u;
+    __syncthreads();
+    uint32_t nl = 0;   // keys this wave has listed so far (lane 0's copy is the wave's)
+    // the segment of element e, followed along the stride (no division per element)
+    int sg = 0;
+    int64_t sg_end = seg;
+    for (int64_t e = tid; e < n; e += kTopkThreads) {
+      while (e >= sg_end) {
+        ++sg;
+        sg_end += seg;
+      }
+      const uint32_t u = key_at(e);
+      if ((u >> 20) > b1) atomicAdd(&wgt[sg], 1u);
+      const bool inb = (u >> 20) == b1;
+      const uint64_t mb = __ballot(inb);
+      const uint32_t pos = nl + lanes_below(mb);
+      if (inb && pos < (uint32_t)kPerWave) {
+        lkey[pos] = u;
+        lidx[pos] = (uint32_t)e;
+      }
+      nl += (uint32_t)__popcll(mb);
+    }
+    nl = (uint32_t)__builtin_amdgcn_readfirstlane((int)nl);
+    __shared__ uint32_t s_nl[kTopkWaves];
+    if (lane == 0) {
+      s_nl[wave] = nl;
+      if (nl > (uint32_t)kPerWave) s_m = 1u;
+    }
+    __syncthreads();
+    if (s_m == 0u) {
+      // entry j of wave w's list: key at rowk[2 w kPerWave + j], index kPerWave further
+      auto list_keys = [&](auto&& add) {
+        for (int i = tid; i < kTopkWaves * kPerWave; i += kTopkThreads) {
+          const int w = i / kPerWave, j = i % kPerWave;
+          if ((uint32_t)j < s_nl[w]) add(rowk[2 * w * kPerWave + j]);
+        }
+      };
+      level(1, list_keys);
+      level(2, list_keys);
+      const uint32_t us = prefix;
+      for (int i = tid; i < kTopkWaves * kPerWave; i += kTopkThreads) {
+        const int w = i / kPerWave, j = i % kPerWave;
+        if ((uint32_t)j >= s_nl[w]) continue;
+        const uint32_t u = rowk[2 * w * kPerWave + j];
+        const int ls = (int)(rowk[2 * w * kPerWave + kPerWave + j] / (uint32_t)seg);   // the entry's segment
+        if (u > us) atomicAdd(&wgt[ls], 1u);
+        else if (u == us) atomicAdd(&weq[ls], 1u);
+      }
+      __syncthreads();
+      counted = true;
+    }
+  }
+  if (!counted) {
+    level(1, row_keys);
+    level(2, row_keys);
   }
   const uint32_t ustar = prefix;   // the k-th key; krem keys equal to it are kept
 
-  // ---- index-ordered compaction: wave w owns a contiguous segment
-  const int64_t seg = ((n + kTopkWaves - 1) / kTopkWaves + 63) / 64 * 64;
-  const int64_t s0 = wave * seg, s1 = min(s0 + seg, n);
-  uint32_t cgt = 0, ceq = 0;
-  for (int64_t e = s0 + lane; e < s1; e += 64) {
-    const uint32_t u = key_at(e);
-    cgt += u > ustar ? 1u : 0u;
-    ceq += u == ustar ? 1u : 0u;
+  if (!counted) {
+    uint32_t cgt = 0, ceq = 0;
+    for (int64_t e = s0 + lane; e < s1; e += 64) {
+      const uint32_t u = key_at(e);
+      cgt += u > ustar ? 1u : 0u;
+      ceq += u == ustar ? 1u : 0u;
+    }
+    cgt = wave_sum(cgt);
+    ceq = wave_sum(ceq);
+    if (lane == 0) {
+      wgt[wave] = cgt;
+      weq[wave] = ceq;
+    }
+    __syncthreads();
   }
-  cgt = wave_sum(cgt);
-  ceq = wave_sum(ceq);
-  if (lane == 0) {
-    wgt[wave] = cgt;
-    weq[wave] = ceq;
-  }
-  __syncthreads();
   uint32_t eq_run = 0, sel_run = 0;
   for (int w = 0; w < wave; ++w) {
     const uint32_t take = eq_run >= krem ? 0u : min(weq[w], krem - eq_run);
