@@ -184,6 +184,46 @@ def test_full_c2_prefill_sampled(mode):
 
 
 @pytest.mark.parametrize("mode", ["gauss", "grid"])
+def test_full_c2_dense_and_hier_sampled(mode):
+    """The causal prefill at 16384 through the dense indexer and through
+    misa_hier_indexer (k' = 2k; a prefill batch takes the separate calls: route,
+    routed top-k', dense re-rank), on a sample of rows: the dense sets and scores
+    against the oracle's dense rows, and MISA-dagger's candidates and final sets
+    against the oracle on the GPU's (checked) head sets."""
+    x, dev = get("c2", mode)
+    c = x.cfg
+    exact = mode == "grid"
+    kc = 2 * c.topk
+    rng = np.random.default_rng(12)
+    qs = sorted(set(rng.choice(c.T, size=10, replace=False).tolist()) | {0, 2047, 2048, 4095, 4096, 16383})
+    di, ds = M.dsa_index_dense(dev["q"], dev["w"], dev["k"], dev["q_seq"], dev["q_len"], c.topk)
+    kbar = M.pool_keys(dev["k"], c.B)
+    heads = torch.empty((c.T, c.h), dtype=torch.int32, device="cuda")
+    cand = torch.empty((c.T, kc), dtype=torch.int32, device="cuda")
+    idx = torch.empty((c.T, c.topk), dtype=torch.int32, device="cuda")
+    sc = torch.empty((c.T, c.topk), dtype=torch.float32, device="cuda")
+    M.hier_indexer(dev["q"], dev["w"], dev["k"], kbar, dev["q_seq"], dev["q_len"], c.B, c.h, kc, c.topk,
+                   heads=heads, cand=cand, idx=idx, score=sc)
+    torch.cuda.synchronize()
+    di, ds = di.cpu().numpy(), ds.cpu().numpy()
+    dense_rows = oracle_rows(x, np.tile(np.arange(c.H), (len(qs), 1)), qs)
+    odi, _ = O.dsa_index_dense(x.q, x.w, x.k, x.q_seq, x.q_len, c.topk, queries=qs)
+    tally = OverlapTally()
+    for i, t in enumerate(qs):
+        tally.add(di[t], odi[i], dense_rows[i], c.topk, exact, label=f"c2/{mode} dense t={t}")
+        selected_scores_ok(di[t], ds[t], dense_rows[i], c.topk, exact, label=f"c2/{mode} dense t={t}")
+    tally.check()
+    use = check_router(x, heads.cpu().numpy()[qs], qs, c.h, exact)
+    routed_rows = oracle_rows(x, use, qs)
+    co, _ = O.score_topk(x.q, x.w, x.k, use, x.q_seq, x.q_len, kc, queries=qs)
+    cand, idx, sc = cand.cpu().numpy(), idx.cpu().numpy(), sc.cpu().numpy()
+    io, _ = O.hier_rerank(x.q, x.w, x.k, co, x.q_seq, x.q_len, c.topk, queries=qs)
+    check_hier_end_to_end(x, qs, cand[qs], idx[qs], co, io, routed_rows, kc, c.topk, exact, label=f"c2/{mode}")
+    for i, t in enumerate(qs):
+        selected_scores_ok(idx[t], sc[t], dense_rows[i], c.topk, exact, label=f"c2/{mode} hier t={t}")
+
+
+@pytest.mark.parametrize("mode", ["gauss", "grid"])
 @pytest.mark.parametrize("name", ["c1", "c4"])
 def test_full_block_indexer(name, mode):
     """The block filter composed with routing at full size, in the launch
